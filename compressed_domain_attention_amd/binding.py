@@ -1,0 +1,250 @@
+"""ctypes binding of libcdattn.so (argument marshalling only).
+
+Every step of the path runs in the library's HIP kernels; this module turns
+torch tensors into pointers and strides, keeps the two host-side counters of
+each stream, and grows archives by capacity doubling (start at 16 blocks,
+double when full), the policy of cache.py ``_CodecStream._grow``.  PyTorch
+is used only to allocate device memory and to name the current HIP stream.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+FMT_F32, FMT_BF16, FMT_I8 = 0, 1, 2
+_FMT_NAMES = {"f32": FMT_F32, "bf16": FMT_BF16, "i8": FMT_I8}
+_TORCH_DTYPE = {FMT_F32: torch.float32, FMT_BF16: torch.bfloat16, FMT_I8: torch.int8}
+_ELEM_BYTES = {FMT_F32: 4, FMT_BF16: 2, FMT_I8: 1}
+INITIAL_BLOCKS = 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path():
+    return os.path.join(_HERE, "libcdattn.so")
+
+
+class CodecError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        msg = _lib().codec_status_string(status).decode() if _LIB is not None else str(status)
+        super().__init__(f"{what}: {msg} (status {status})")
+
+
+class _Stream(ctypes.Structure):
+    _fields_ = [
+        ("block", ctypes.c_int32), ("keep", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("fmt", ctypes.c_int32), ("raw_dtype", ctypes.c_int32), ("n_tail", ctypes.c_int32),
+        ("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("capacity", ctypes.c_int64),
+        ("n_blocks", ctypes.c_int64),
+        ("rows", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("tail", ctypes.c_void_p),
+    ]
+
+
+_I64_2 = ctypes.c_int64 * 2
+_I64_3 = ctypes.c_int64 * 3
+
+
+def _lib():
+    """Load libcdattn.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build the HIP library first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(path)
+        P = ctypes.POINTER(_Stream)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        lib.codec_basis.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_float)]
+        lib.codec_encode_blocks.argtypes = [P, vp, _I64_3, i64, vp]
+        lib.codec_append_step.argtypes = [P, P, vp, _I64_2, vp, _I64_2, vp]
+        lib.codec_decode_workspace_bytes.argtypes = [P, P, i64, ctypes.POINTER(ctypes.c_size_t)]
+        lib.codec_decode_attention.argtypes = [vp, _I64_2, i64, P, P, f32, vp, _I64_2, i32,
+                                               vp, ctypes.c_size_t, vp]
+        lib.codec_status_string.argtypes = [ctypes.c_int]
+        lib.codec_status_string.restype = ctypes.c_char_p
+        for name in ("codec_basis", "codec_encode_blocks", "codec_append_step",
+                     "codec_decode_workspace_bytes", "codec_decode_attention"):
+            getattr(lib, name).restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def library():
+    """The loaded ctypes library (loads it on first use)."""
+    return _lib()
+
+
+def _check(status, what):
+    if status != 0:
+        raise CodecError(status, what)
+
+
+def _fmt(f):
+    if isinstance(f, str):
+        return _FMT_NAMES[f]
+    return int(f)
+
+
+def _hip_stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def basis(R, S):
+    """A (R x S) fp32 synthesis matrix as a CPU tensor (A[i, j] = M[j, i])."""
+    A = (ctypes.c_float * (R * S))()
+    _check(_lib().codec_basis(R, S, A), "codec_basis")
+    return torch.tensor(list(A), dtype=torch.float32).reshape(R, S)
+
+
+class CodecStream:
+    """A compressed key or value stream in device memory.
+
+    Holds rows (B, H, capacity, S, D), scales (B, H, capacity, S) for int8,
+    and the raw tail (B, H, R, D).  ``n_blocks`` / ``n_tail`` mirror the
+    library's counters.
+    """
+
+    def __init__(self, B, H, D, R, S, fmt="i8", raw_dtype="bf16", device="cuda", capacity=0):
+        self.B, self.H, self.D, self.R, self.S = int(B), int(H), int(D), int(R), int(S)
+        self.fmt, self.raw_dtype = _fmt(fmt), _fmt(raw_dtype)
+        self.device = torch.device(device)
+        self.n_blocks, self.n_tail = 0, 0
+        self.capacity = 0
+        self.rows = self.scales = None
+        self.tail = torch.zeros((self.B, self.H, self.R, self.D), dtype=_TORCH_DTYPE[self.raw_dtype],
+                                device=self.device)
+        self._grow(max(int(capacity), INITIAL_BLOCKS))
+
+    # cache.py ``_CodecStream._grow``: start at 16 blocks and double until the
+    # request fits; archived blocks are copied over verbatim.
+    def _grow(self, need):
+        if need <= self.capacity:
+            return
+        cap = max(INITIAL_BLOCKS, self.capacity)
+        while cap < need:
+            cap *= 2
+        rows = torch.empty((self.B, self.H, cap, self.S, self.D), dtype=_TORCH_DTYPE[self.fmt],
+                           device=self.device)
+        scales = (torch.empty((self.B, self.H, cap, self.S), dtype=torch.float32, device=self.device)
+                  if self.fmt == FMT_I8 else None)
+        if self.n_blocks:
+            rows[:, :, :self.n_blocks].copy_(self.rows[:, :, :self.n_blocks])
+            if scales is not None:
+                scales[:, :, :self.n_blocks].copy_(self.scales[:, :, :self.n_blocks])
+        self.rows, self.scales, self.capacity = rows, scales, cap
+
+    def _desc(self):
+        d = _Stream()
+        d.block, d.keep, d.head_dim = self.R, self.S, self.D
+        d.fmt, d.raw_dtype, d.n_tail = self.fmt, self.raw_dtype, self.n_tail
+        d.batch, d.heads, d.capacity, d.n_blocks = self.B, self.H, self.capacity, self.n_blocks
+        d.rows = self.rows.data_ptr()
+        d.scales = self.scales.data_ptr() if self.scales is not None else None
+        d.tail = self.tail.data_ptr()
+        return d
+
+    def _sync(self, d):
+        self.n_blocks, self.n_tail = int(d.n_blocks), int(d.n_tail)
+
+    @property
+    def seq_len(self):
+        return self.n_blocks * self.R + self.n_tail
+
+    def storage_bytes(self):
+        """Logical bytes: valid archive region (+ scales) and the raw tail
+        (cache.py ``storage_bytes``; spare capacity is not counted)."""
+        per_block = self.S * self.D * _ELEM_BYTES[self.fmt] + (4 * self.S if self.fmt == FMT_I8 else 0)
+        return self.B * self.H * (self.n_blocks * per_block + self.n_tail * self.D * _ELEM_BYTES[self.raw_dtype])
+
+    def encode(self, x, stream=None):
+        """Archive a (B, H, T, D) run of raw tokens; the tail must be empty."""
+        return encode_blocks(self, x, stream)
+
+
+def encode_blocks(s, x, stream=None):
+    if x.dtype != _TORCH_DTYPE[s.raw_dtype] or x.dim() != 4 or x.stride(3) != 1:
+        raise ValueError("x must be (B, H, T, D) of the stream's raw dtype with unit d stride")
+    T = x.shape[2]
+    s._grow(s.n_blocks + T // s.R)
+    d = s._desc()
+    st = _hip_stream(s.device) if stream is None else ctypes.c_void_p(stream)
+    _check(_lib().codec_encode_blocks(ctypes.byref(d), ctypes.c_void_p(x.data_ptr()),
+                                      _I64_3(x.stride(0), x.stride(1), x.stride(2)), T, st),
+           "codec_encode_blocks")
+    s._sync(d)
+
+
+def append_step(k, v, k_new, v_new, stream=None):
+    """Append one token (B, H, 1, D) to both streams (archives at block ends)."""
+    for s, t in ((k, k_new), (v, v_new)):
+        if t.dtype != _TORCH_DTYPE[s.raw_dtype] or t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError("new token must be (B, H, 1, D) of the raw dtype with unit d stride")
+    if k.n_tail + 1 == k.R:
+        k._grow(k.n_blocks + 1)
+        v._grow(v.n_blocks + 1)
+    dk, dv = k._desc(), v._desc()
+    st = _hip_stream(k.device) if stream is None else ctypes.c_void_p(stream)
+    _check(_lib().codec_append_step(ctypes.byref(dk), ctypes.byref(dv),
+                                    ctypes.c_void_p(k_new.data_ptr()), _I64_2(k_new.stride(0), k_new.stride(1)),
+                                    ctypes.c_void_p(v_new.data_ptr()), _I64_2(v_new.stride(0), v_new.stride(1)),
+                                    st), "codec_append_step")
+    k._sync(dk)
+    v._sync(dv)
+
+
+def decode_workspace_bytes(k, v, Hq):
+    n = ctypes.c_size_t(0)
+    _check(_lib().codec_decode_workspace_bytes(ctypes.byref(k._desc()), ctypes.byref(v._desc()),
+                                               int(Hq), ctypes.byref(n)), "codec_decode_workspace_bytes")
+    return int(n.value)
+
+
+_WS_CACHE = {}
+
+
+def _workspace(nbytes, device):
+    """A zero-filled workspace per device, grown on demand and then reused
+    (the kernels leave its counters at zero after every call)."""
+    key = (device.type, device.index)
+    ws = _WS_CACHE.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WS_CACHE[key] = ws
+    return ws
+
+
+def decode_attention(q, k, v, scale=None, out=None, out_dtype=torch.float32, workspace=None, stream=None):
+    """Decode attention of q (B, Hq, 1, D) bf16 over streams k, v.
+
+    Default scale D ** -0.5 (the Triton wrapper's default).  Returns out
+    (B, Hq, 1, D) in out_dtype (float32 or bfloat16).
+    """
+    if q.dtype != torch.bfloat16 or q.dim() != 4 or q.shape[2] != 1 or q.stride(3) != 1:
+        raise ValueError("q must be (B, Hq, 1, D) bf16 with unit d stride")
+    B, Hq, _, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, 1, D), dtype=out_dtype, device=q.device)
+    odt = {torch.float32: FMT_F32, torch.bfloat16: FMT_BF16}[out.dtype]
+    dk, dv = k._desc(), v._desc()
+    need = decode_workspace_bytes(k, v, Hq)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    st = _hip_stream(q.device) if stream is None else ctypes.c_void_p(stream)
+    _check(_lib().codec_decode_attention(
+        ctypes.c_void_p(q.data_ptr()), _I64_2(q.stride(0), q.stride(1)), Hq,
+        ctypes.byref(dk), ctypes.byref(dv), ctypes.c_float(float(scale)),
+        ctypes.c_void_p(out.data_ptr()), _I64_2(out.stride(0), out.stride(1)), odt,
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), st),
+        "codec_decode_attention")
+    return out
+
+
+def default_scale(D):
+    return 1.0 / math.sqrt(D)

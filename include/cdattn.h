@@ -1,0 +1,195 @@
+/*
+ * cdattn.h -- C ABI of the compressed-domain decode attention library
+ * (libcdattn.so, HIP kernels for AMD Instinct MI355X / gfx950).
+ *
+ * The method (flashcodec-kv 1.0.0; README sections "Math", "Causal-safety
+ * design" and "Materialization-free decode attention"; cache.py
+ * ``_CodecStream``; triton_attention.py):
+ *   - the sequence axis of a (batch, heads, seq, head_dim) key or value
+ *     tensor is cut into blocks of R tokens;
+ *   - every complete block X (R x D) is stored as the S lowest-frequency
+ *     rows of its orthonormal DCT-II, C = M X (S x D), either as floats or as
+ *     int8 codes with one fp32 scale per (block, frequency) row;
+ *   - the incomplete last block stays raw (the "tail");
+ *   - one decode query attends to the archive without reconstructing it:
+ *     s = rows . q, logits = A s (A = M^T, R x S), online softmax,
+ *     w = p A, acc += w . rows, split over block chunks and merged with a
+ *     (max, sum, acc) combine.
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers unless stated otherwise.
+ *   - Strides are in elements.  The head_dim axis is always contiguous.
+ *   - Every call validates all arguments synchronously BEFORE any HIP call;
+ *     on error it returns a non-zero status, enqueues nothing and changes
+ *     nothing (stream counters included).
+ *   - Work is enqueued on the caller's `stream` and the call returns without
+ *     waiting.  The library allocates no memory and keeps no pointer past
+ *     the call.  The caller owns every buffer.
+ *   - Calls that share a stream descriptor or a workspace must not run
+ *     concurrently on different HIP streams.
+ */
+#ifndef CDATTN_H
+#define CDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+enum {
+  CODEC_OK = 0,
+  CODEC_ERR_NULL = 1,        /* a required pointer is NULL                            */
+  CODEC_ERR_SHAPE = 2,       /* a size is out of range or two shapes disagree         */
+  CODEC_ERR_FORMAT = 3,      /* unknown or unsupported row / raw / query / out format */
+  CODEC_ERR_CAPACITY = 4,    /* archive capacity too small for the blocks to write    */
+  CODEC_ERR_STATE = 5,       /* stream counters forbid the call (e.g. tail not empty) */
+  CODEC_ERR_WORKSPACE = 6,   /* decode workspace missing, too small or misaligned     */
+  CODEC_ERR_UNSUPPORTED = 7, /* valid arguments but no kernel compiled for them       */
+  CODEC_ERR_HIP = 8,         /* a HIP runtime call or kernel launch failed            */
+  CODEC_ERR_SCALE = 9        /* softmax scale not finite or not positive              */
+};
+
+/* ------------------------------------------------------------- formats  */
+enum {
+  CODEC_F32 = 0,   /* IEEE binary32                                            */
+  CODEC_BF16 = 1,  /* bfloat16 (upper half of binary32), round-to-nearest-even */
+  CODEC_I8 = 2     /* int8 codes in [-127, 127] + fp32 scale per (block, row)  */
+};
+
+/* Limits of this build. */
+#define CODEC_MAX_BLOCK 32   /* R: tokens per block                            */
+#define CODEC_MAX_KEEP 16    /* S: kept frequencies (S <= R)                   */
+/* head_dim D must be 64, 128 or 256.  GQA group G = Hq / H must be >= 1.     */
+
+/*
+ * One compressed key or value stream: the archive of complete blocks and the
+ * raw tail of one (B, H, seq, D) tensor (cache.py ``_CodecStream``: raw tail
+ * plus capacity-grown archive of coefficient rows; README "Causal-safety
+ * design": only complete blocks are archived and never rewritten).
+ *
+ * Memory layouts (dense, row-major, owned by the caller):
+ *   rows   [B][H][capacity][S][D]  elements of `fmt`
+ *          block n of (b, h) holds the S coefficient rows of tokens
+ *          n*R .. n*R+R-1 (frequency j = 0 .. S-1, lowest first)
+ *   scales [B][H][capacity][S]     fp32, only when fmt == CODEC_I8
+ *          (stored value = code * scale)
+ *   tail   [B][H][R][D]            elements of `raw_dtype`; slots
+ *          0 .. n_tail-1 hold the newest tokens, in order
+ * The sequence length is n_blocks * R + n_tail.  The library advances
+ * n_blocks / n_tail itself on success of encode and append calls; the caller
+ * grows `capacity` (and re-points `rows` / `scales`) when a call returns
+ * CODEC_ERR_CAPACITY.
+ */
+typedef struct codec_stream {
+  int32_t block;      /* R, 1 .. CODEC_MAX_BLOCK                          */
+  int32_t keep;       /* S, 1 .. min(R, CODEC_MAX_KEEP)                    */
+  int32_t head_dim;   /* D, 64 | 128 | 256                                 */
+  int32_t fmt;        /* CODEC_F32 | CODEC_BF16 | CODEC_I8 (rows)          */
+  int32_t raw_dtype;  /* CODEC_BF16 | CODEC_F32 (raw tokens and tail)      */
+  int32_t n_tail;     /* raw tokens in the tail, 0 .. R-1                  */
+  int64_t batch;      /* B >= 1                                            */
+  int64_t heads;      /* H >= 1 (kv heads)                                 */
+  int64_t capacity;   /* blocks allocated per (b, h), >= n_blocks          */
+  int64_t n_blocks;   /* archived blocks per (b, h)                        */
+  void *rows;         /* device, see layout above                          */
+  float *scales;      /* device, fmt == CODEC_I8 only (else ignored)       */
+  void *tail;         /* device, see layout above                          */
+} codec_stream;
+
+/*
+ * codec_basis -- synthesis matrix A = M^T of the kept DCT-II rows, on the host.
+ * README "Math", JPEG item: M[j, i] = c_j cos(pi (2i + 1) j / (2R)),
+ * c_0 = sqrt(1/R), c_j = sqrt(2/R) (the normalisation that makes the rows
+ * orthonormal).  Evaluated in double precision and rounded to fp32; this is
+ * exactly the basis the kernels encode and decode with.
+ *   A_host: caller-owned host array of R*S floats, A[i*S + j] = fp32(M[j][i]).
+ * Errors: CODEC_ERR_NULL, CODEC_ERR_SHAPE (R or S out of range).
+ */
+int codec_basis(int32_t R, int32_t S, float *A_host);
+
+/*
+ * codec_encode_blocks -- archive a run of raw tokens (prefill).
+ * cache.py ``_CodecStream.append`` / ``_archive``: the floor(T/R) complete
+ * blocks are projected onto the kept DCT-II rows and written at archive
+ * slots n_blocks .. n_blocks + floor(T/R) - 1 in one launch; the last T mod R
+ * tokens are copied verbatim into tail slots 0 .. T mod R - 1.
+ * Arithmetic (bit-exact contract): c = sum_{i<R} fp64(A[i][j]) * fp64(x_i)
+ * accumulated left to right from +0.0 in fp64; fp32 rows = fp32(c); bf16
+ * rows = bf16(fp32(c)) (both round-to-nearest-even); int8 rows:
+ * a = max_d |c|, scale = fp32(a / 127), code = clamp(rint(c / scale), +-127)
+ * with ties to even, scale 0 -> codes 0.
+ *   s        stream; requires s->n_tail == 0; on success n_blocks grows by
+ *            floor(T/R) and n_tail = T mod R.
+ *   x        device, (B, H, T, D) elements of s->raw_dtype.
+ *   x_stride element strides of the b, h and t axes (d stride is 1).
+ *   T        tokens, >= 0 (T == 0 is a no-op).
+ * Errors: NULL, SHAPE, FORMAT, STATE (tail not empty), CAPACITY, HIP.
+ */
+int codec_encode_blocks(codec_stream *s, const void *x, const int64_t x_stride[3],
+                        int64_t T, hipStream_t stream);
+
+/*
+ * codec_append_step -- append one decode token to a key and a value stream.
+ * cache.py ``_CodecStream.append`` with one token: the token goes into tail
+ * slot n_tail; when that completes a block (n_tail + 1 == R) the same launch
+ * encodes the R tail tokens into archive slot n_blocks with the arithmetic of
+ * codec_encode_blocks (bit-identical), and the tail becomes empty.  Archived
+ * blocks are never touched (README "Causal-safety design").
+ *   k, v          the two streams (same B, H, R, D; formats may differ).
+ *   k_new, v_new  device, (B, H, 1, D) of the stream's raw_dtype.
+ *   kn_stride, vn_stride  element strides of the b and h axes.
+ * Errors: NULL, SHAPE, FORMAT, CAPACITY (a block completes and capacity ==
+ * n_blocks), HIP.  Counters of both streams change only on success.
+ */
+int codec_append_step(codec_stream *k, codec_stream *v,
+                      const void *k_new, const int64_t kn_stride[2],
+                      const void *v_new, const int64_t vn_stride[2],
+                      hipStream_t stream);
+
+/*
+ * codec_decode_workspace_bytes -- workspace needed by codec_decode_attention
+ * for these streams and Hq query heads (a pure function of the shapes).
+ * The workspace holds the per-split (max, sum, acc) partials and one
+ * arrival counter per (b, kv head, query group).  It must be zero-filled
+ * once before its first use; every completed decode call leaves the
+ * counters at zero again, so it can be reused without clearing.
+ * Errors: NULL, SHAPE, FORMAT, UNSUPPORTED.
+ */
+int codec_decode_workspace_bytes(const codec_stream *k, const codec_stream *v,
+                                 int64_t Hq, size_t *bytes);
+
+/*
+ * codec_decode_attention -- one decode query per head against the
+ * compressed archive and the raw tail, without reconstructing K or V.
+ * README "Materialization-free decode attention" (q . K[p] = (q . S^T) A[p],
+ * out = (p A) S) and triton_attention.py (split over block chunks, partial
+ * (max, sum, acc) per split, flash-decoding combine).  Query head hq uses kv
+ * head hq / (Hq / H).  Result = softmax(scale * q . K_t) weighted sum of V_t
+ * over all n_blocks * R + n_tail tokens, K_t / V_t being the decoded rows.
+ *   q            device, (B, Hq, 1, D) bf16; q_stride = strides of b and h.
+ *   Hq           query heads, a multiple of k->heads.
+ *   k, v         streams with equal B, H, R, S, D, n_blocks, n_tail.
+ *   scale        softmax scale (> 0, finite); the usual choice is D^-1/2.
+ *   out          device, (B, Hq, 1, D) of out_dtype (CODEC_F32 | CODEC_BF16);
+ *                out_stride = strides of b and h.
+ *   workspace    device, >= codec_decode_workspace_bytes, 256-byte aligned,
+ *                zero-filled before its first use (see above).
+ * Errors: NULL, SHAPE (includes an empty sequence), FORMAT, SCALE,
+ * WORKSPACE, UNSUPPORTED, HIP.
+ */
+int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
+                           const codec_stream *k, const codec_stream *v, float scale,
+                           void *out, const int64_t out_stride[2], int32_t out_dtype,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* codec_status_string -- static text for a status code (never NULL). */
+const char *codec_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CDATTN_H */

@@ -1,0 +1,7 @@
+"""fp64 CPU oracle (test infrastructure only; never used by the product path)."""
+from .codec_oracle import *  # noqa: F401,F403
+from .codec_oracle import (F32, BF16, I8, FORMATS, dct_basis_f64, dct_basis_f32,  # noqa: F401
+                           f32_to_bf16_bits, bf16_bits_to_f64, project_blocks,
+                           quantize_rows, encode_rows, encode, dequantize,
+                           reconstruct, materialise, attention, decode_attention,
+                           decode_attention_heads, Stream, storage_bytes)

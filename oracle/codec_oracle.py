@@ -1,0 +1,338 @@
+"""fp64 CPU oracle for compressed-domain decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test suite, the smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code, tables or constants
+with the HIP library; the two meet only through the seeded synthetic inputs.
+
+What it computes, and where the pages fix it
+--------------------------------------------
+Citations name the page and the section on it.  "README" is the project
+description shipped in the flashcodec-kv 1.0.0 wheel (page "flashcodec-kv
+1.0.0 .whl, page 4"); "cache.py" is the stream manager source on page
+"flashcodec-kv 1.0.0 .whl, page 2"; "triton_attention.py" is the kernel
+source on page 4.
+
+* Block DCT-II basis, lowest S of R frequencies kept, orthonormal rows
+  (README, section "Math", JPEG item).
+* Encode: every complete block of R tokens along the sequence axis becomes
+  S coefficient rows C = M X (README "Math"; cache.py ``_CodecStream._archive``).
+* int8 variant: codes plus one fp32 scale per (block, frequency)
+  (README, paragraph on ``quant_bits=8``; cache.py ``_archive_spec``).
+* Only complete blocks are archived; the rest stays raw at full fidelity
+  (README "Causal-safety design"; cache.py ``append``).
+* Decode attention is, up to rounding, ordinary softmax attention over the
+  reconstructed keys/values X_hat = M^T C followed by the raw tail
+  (README "Materialization-free decode attention": the coefficient-domain
+  form equals the materialised one).  The oracle therefore materialises.
+* GQA: query head hq reads kv head hq // G (triton_attention.py, program
+  id decomposition in the split kernel).
+
+Readings where the pages are silent (each also listed in the design notes)
+---------------------------------------------------------------------------
+1. c_0 = sqrt(1/R), c_j = sqrt(2/R) for j >= 1: the only constants that make
+   the rows orthonormal.
+2. The basis used by the codec is M32 = fp32(M64) (round to nearest even).
+3. Projection: fp64, products M32[j,i]*x exact, summed left to right over
+   i = 0..R-1 starting from +0.0.
+4. Float rows are fp32(C); bf16 rows are bf16(fp32(C)), both RNE.
+5. int8: a = max_d |C|, scale = fp32(a / 127) (fp64 division, then RNE),
+   code = clamp(rint_half_even(C / fp64(scale)), -127, 127); a zero scale
+   gives zero codes.
+6. Dequantised row = code * scale (exact in fp64).
+7. Softmax uses the natural exponential, max-subtracted; default
+   scale = D ** -0.5 (triton_attention.py host wrapper).
+8. n = 0 complete blocks is allowed (tail-only attention); T = 0 is an error.
+"""
+
+import math
+
+import numpy as np
+
+F32 = "f32"
+BF16 = "bf16"
+I8 = "i8"
+FORMATS = (F32, BF16, I8)
+
+
+# ---------------------------------------------------------------------------
+# basis
+# ---------------------------------------------------------------------------
+def dct_basis_f64(R, S):
+    """Analysis matrix M64 (S x R): M[j, i] = c_j cos(pi (2i + 1) j / (2R)).
+
+    README "Math", JPEG item: M[j, n] = c_j cos(pi/r (n + 1/2) j) with
+    orthonormal rows; the lowest S frequencies are kept.  Reading 1 fixes
+    c_j.  Evaluated element by element with the C library's cos.
+    """
+    if not (1 <= S <= R):
+        raise ValueError("need 1 <= S <= R")
+    M = np.empty((S, R), dtype=np.float64)
+    for j in range(S):
+        cj = math.sqrt(1.0 / R) if j == 0 else math.sqrt(2.0 / R)
+        for i in range(R):
+            M[j, i] = cj * math.cos(math.pi * (2 * i + 1) * j / (2 * R))
+    return M
+
+
+def dct_basis_f32(R, S):
+    """The codec's basis: M64 rounded to fp32 (reading 2)."""
+    return dct_basis_f64(R, S).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# rounding helpers (bit-level, so results can be compared byte for byte)
+# ---------------------------------------------------------------------------
+def f32_to_bf16_bits(v):
+    """Round fp32 values to bf16, nearest-even; returns the uint16 patterns."""
+    u = np.ascontiguousarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits):
+    """Exact value of bf16 bit patterns as fp64."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# encode
+# ---------------------------------------------------------------------------
+def project_blocks(x, R, S):
+    """fp64 coefficients of every complete block.
+
+    x: (..., T, D) real values (bf16 or fp32 values held in any float dtype).
+    Returns C: (..., n, S, D) with n = T // R and
+        C[..., n, j, :] = sum_{i<R} M32[j, i] * x[..., n*R + i, :]
+    summed left to right from +0.0 (reading 3).  README "Math": C = M X
+    block by block along the sequence axis.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T, D = x.shape[-2], x.shape[-1]
+    lead = x.shape[:-2]
+    n = T // R
+    xb = x[..., : n * R, :].reshape(*lead, n, R, D)
+    M = dct_basis_f32(R, S).astype(np.float64)
+    C = np.empty((*lead, n, S, D), dtype=np.float64)
+    for j in range(S):
+        acc = np.zeros((*lead, n, D), dtype=np.float64)
+        for i in range(R):
+            acc = acc + M[j, i] * xb[..., i, :]
+        C[..., j, :] = acc
+    return C
+
+
+def quantize_rows(C):
+    """int8 codes and fp32 scales, one scale per (block, frequency) row.
+
+    README paragraph on ``quant_bits=8`` (int8 coefficients with a
+    per-(block, frequency) scale); the scale rule and rounding are
+    reading 5.  Returns (codes int8 (..., S, D), scales float32 (..., S)).
+    """
+    C = np.asarray(C, dtype=np.float64)
+    a = np.max(np.abs(C), axis=-1)
+    s32 = (a / 127.0).astype(np.float32)
+    s64 = s32.astype(np.float64)[..., None]
+    codes = np.zeros(C.shape, dtype=np.int8)
+    nz = np.broadcast_to(s64 != 0.0, C.shape)
+    y = np.divide(C, s64, out=np.zeros_like(C), where=nz)
+    codes[nz] = np.clip(np.rint(y[nz]), -127, 127).astype(np.int8)
+    return codes, s32
+
+
+def encode_rows(C, fmt):
+    """Store fp64 coefficients in format `fmt` (reading 4 / 5).
+
+    Returns (rows, scales): rows float32 for F32, uint16 bf16 patterns for
+    BF16, int8 codes for I8; scales float32 for I8 else None.
+    """
+    if fmt == F32:
+        return np.asarray(C, dtype=np.float64).astype(np.float32), None
+    if fmt == BF16:
+        return f32_to_bf16_bits(np.asarray(C, dtype=np.float64).astype(np.float32)), None
+    if fmt == I8:
+        return quantize_rows(C)
+    raise ValueError(f"unknown format {fmt!r}")
+
+
+def encode(x, R, S, fmt):
+    """Archive a (…, T, D) sequence: complete blocks encoded, tail kept raw.
+
+    cache.py ``append``/``_archive``: the first (T // R) * R tokens are
+    compressed block by block; the last T mod R tokens stay verbatim.
+    Returns dict(rows, scales, tail, n_blocks) with tail the raw values as
+    fp64 (..., T mod R, D).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[-2]
+    n = T // R
+    rows, scales = encode_rows(project_blocks(x, R, S), fmt)
+    return dict(fmt=fmt, R=R, S=S, rows=rows, scales=scales,
+                tail=x[..., n * R:, :].copy(), n_blocks=n)
+
+
+# ---------------------------------------------------------------------------
+# decode (materialise) and attention
+# ---------------------------------------------------------------------------
+def dequantize(rows, scales, fmt):
+    """fp64 coefficient rows from their stored form (reading 6)."""
+    if fmt == F32:
+        return np.asarray(rows, dtype=np.float32).astype(np.float64)
+    if fmt == BF16:
+        return bf16_bits_to_f64(rows)
+    if fmt == I8:
+        return np.asarray(rows, dtype=np.int8).astype(np.float64) * \
+            np.asarray(scales, dtype=np.float32).astype(np.float64)[..., None]
+    raise ValueError(f"unknown format {fmt!r}")
+
+
+def reconstruct(C, R):
+    """Synthesis X_hat = M32^T C per block (README "Math": X_hat = M^T C).
+
+    C: (..., n, S, D) fp64 -> (..., n * R, D) fp64, with
+    X_hat[..., n*R + i, :] = sum_j M32[j, i] * C[..., n, j, :].
+    """
+    C = np.asarray(C, dtype=np.float64)
+    *lead, n, S, D = C.shape
+    M = dct_basis_f32(R, S).astype(np.float64)
+    X = np.zeros((*lead, n, R, D), dtype=np.float64)
+    for i in range(R):
+        for j in range(S):
+            X[..., i, :] += M[j, i] * C[..., j, :]
+    return X.reshape(*lead, n * R, D)
+
+
+def materialise(archive):
+    """Full (..., n*R + t, D) fp64 view: reconstructed blocks then raw tail."""
+    C = dequantize(archive["rows"], archive["scales"], archive["fmt"])
+    X = reconstruct(C, archive["R"])
+    return np.concatenate([X, np.asarray(archive["tail"], dtype=np.float64)], axis=-2)
+
+
+def attention(q, K, V, scale):
+    """Single-query softmax attention, fp64, GQA by hq // G.
+
+    q: (B, Hq, D); K, V: (B, Hkv, T, D).  Returns (B, Hq, D).
+    z_t = scale * q . K_t ;  p = exp(z - max z) / sum ;  out = sum_t p_t V_t.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv, T = K.shape[1], K.shape[2]
+    if T == 0:
+        raise ValueError("nothing to attend: T = 0")
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // G
+            z = scale * (K[b, h] @ q[b, hq])
+            p = np.exp(z - z.max())
+            out[b, hq] = (p @ V[b, h]) / p.sum()
+    return out
+
+
+def decode_attention(q, k_archive, v_archive, scale=None):
+    """Decode attention over a compressed K/V archive (materialised).
+
+    q: (B, Hq, D) (a (B, Hq, 1, D) query is accepted too).  Default scale is
+    D ** -0.5, as in the Triton host wrapper.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    if q.ndim == 4:
+        q = q[:, :, 0, :]
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    return attention(q, materialise(k_archive), materialise(v_archive), scale)
+
+
+def decode_attention_heads(q, k_archive, v_archive, scale, pairs):
+    """Same as ``decode_attention`` but only for the listed (b, hq) pairs.
+
+    Materialises one kv head at a time so full-size archives can be sampled
+    without building every head.  Returns {(b, hq): out (D,)}.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    if q.ndim == 4:
+        q = q[:, :, 0, :]
+    Hq = q.shape[1]
+    Hkv = k_archive["rows"].shape[1]
+    G = Hq // Hkv
+    res = {}
+    cache = {}
+    for (b, hq) in pairs:
+        h = hq // G
+        if (b, h) not in cache:
+            cache.clear()
+            cache[(b, h)] = tuple(materialise(_head(a, b, h)) for a in (k_archive, v_archive))
+        K, V = cache[(b, h)]
+        res[(b, hq)] = attention(q[b:b + 1, hq:hq + 1], K[None, None], V[None, None], scale)[0, 0]
+    return res
+
+
+def _head(archive, b, h):
+    out = dict(archive)
+    out["rows"] = archive["rows"][b, h]
+    out["scales"] = None if archive["scales"] is None else archive["scales"][b, h]
+    out["tail"] = archive["tail"][b, h]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# streaming (append with automatic archiving at block boundaries)
+# ---------------------------------------------------------------------------
+class Stream:
+    """One K or V stream: a growing archive of complete blocks + a raw tail.
+
+    cache.py ``_CodecStream.append``: new tokens are concatenated onto the
+    raw tail, every complete block is archived, the remainder stays raw.
+    Archived entries are never rewritten (README "Causal-safety design").
+    """
+
+    def __init__(self, R, S, fmt):
+        self.R, self.S, self.fmt = R, S, fmt
+        self.rows = []      # list of (..., S, D) per archived block
+        self.scales = []
+        self.tail = None    # (..., t, D) fp64
+
+    def append(self, tokens):
+        tokens = np.asarray(tokens, dtype=np.float64)
+        buf = tokens if self.tail is None else np.concatenate([self.tail, tokens], axis=-2)
+        n_full = buf.shape[-2] // self.R
+        if n_full:
+            rows, scales = encode_rows(project_blocks(buf[..., : n_full * self.R, :], self.R, self.S), self.fmt)
+            for k in range(n_full):
+                self.rows.append(rows[..., k, :, :])
+                self.scales.append(None if scales is None else scales[..., k, :])
+        self.tail = buf[..., n_full * self.R:, :]
+
+    @property
+    def n_blocks(self):
+        return len(self.rows)
+
+    def archive(self):
+        """Snapshot in the same dict form as ``encode``."""
+        lead = self.tail.shape[:-2]
+        D = self.tail.shape[-1]
+        if self.rows:
+            rows = np.stack(self.rows, axis=-3)
+            scales = np.stack(self.scales, axis=-2) if self.fmt == I8 else None
+        else:
+            dt = {F32: np.float32, BF16: np.uint16, I8: np.int8}[self.fmt]
+            rows = np.zeros((*lead, 0, self.S, D), dtype=dt)
+            scales = np.zeros((*lead, 0, self.S), dtype=np.float32) if self.fmt == I8 else None
+        return dict(fmt=self.fmt, R=self.R, S=self.S, rows=rows, scales=scales,
+                    tail=self.tail.copy(), n_blocks=len(self.rows))
+
+
+def storage_bytes(n_blocks, S, D, fmt, tail_tokens, tail_elem_bytes):
+    """Logical bytes of one (b, h) stream: archived rows (+ scales) + tail.
+
+    cache.py ``storage_bytes``: valid archive region plus the raw tail.
+    """
+    row_b = {F32: 4, BF16: 2, I8: 1}[fmt]
+    return n_blocks * S * (D * row_b + (4 if fmt == I8 else 0)) + tail_tokens * D * tail_elem_bytes

@@ -1,0 +1,311 @@
+"""Pins for the fp64 oracle, against facts the pages and mathematics fix.
+
+None of these re-type the oracle's own formula: each compares it with a
+closed form, a library routine, a hand-worked value, an invariant, or a
+figure printed on the pages (tests/golden/).
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.fft
+import torch
+
+import oracle as O
+from compressed_domain_attention_amd import synthetic as syn
+
+
+# ---------------------------------------------------------------- basis ----
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 12, 16, 32])
+def test_basis_rows_orthonormal(R):
+    # README "Math": the analysis rows are orthonormal.
+    M = O.dct_basis_f64(R, R)
+    assert np.abs(M @ M.T - np.eye(R)).max() <= 1e-14
+    M32 = O.dct_basis_f32(R, R).astype(np.float64)
+    assert np.abs(M32 @ M32.T - np.eye(R)).max() <= 4 * R * 2.0 ** -24
+
+
+def test_basis_closed_forms():
+    # R = 1: the transform is the identity.
+    assert O.dct_basis_f64(1, 1).tolist() == [[1.0]]
+    # R = 2: the normalised Haar pair (sum and difference over sqrt 2).
+    h = 0.7071067811865476          # 1/sqrt(2), correctly rounded
+    M2 = O.dct_basis_f64(2, 2)
+    np.testing.assert_allclose(M2, [[h, h], [h, -h]], rtol=0, atol=2e-16)
+    # R = 4, frequency 1: sqrt(1/2) cos(k pi/8) for k = 1, 3, 5, 7;
+    # cos(pi/8) = sqrt(2 + sqrt 2) / 2 = 0.92387953251128674,
+    # cos(3 pi/8) = sqrt(2 - sqrt 2) / 2 = 0.38268343236508978.
+    c1, c3 = 0.92387953251128674 * h, 0.38268343236508978 * h
+    np.testing.assert_allclose(O.dct_basis_f64(4, 2)[1], [c1, c3, -c3, -c1], rtol=0, atol=4e-16)
+    # the constant row has all entries 1/sqrt(R)
+    for R in (3, 8, 16):
+        np.testing.assert_allclose(O.dct_basis_f64(R, 1)[0], np.full(R, 1 / math.sqrt(R)), rtol=0, atol=2.3e-16)
+
+
+@pytest.mark.parametrize("R,S", [(2, 1), (3, 2), (8, 2), (8, 8), (12, 5), (16, 4)])
+def test_projection_equals_scipy_dct(R, S):
+    # The lowest S outputs of the orthonormal DCT-II of each block.
+    rng = np.random.default_rng(R * 100 + S)
+    x = rng.standard_normal((3, 5 * R, 7))
+    ref = scipy.fft.dct(x.reshape(3, 5, R, 7), type=2, norm="ortho", axis=2)[:, :, :S, :]
+    M = O.dct_basis_f64(R, S)
+    got = np.einsum("ji,bnid->bnjd", M, x.reshape(3, 5, R, 7))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-13)
+    # and the codec's fp32-basis projection is within the basis rounding
+    C = O.project_blocks(x, R, S)
+    bound = R * 2.0 ** -24 * np.abs(x).max() * 1.01
+    assert np.abs(C - ref).max() <= bound
+
+
+# ---------------------------------------------------------------- encode ---
+def test_projection_by_hand_r2():
+    # R = 2, D = 1, block [1, 3]: c0 = 4 * fp32(1/sqrt 2), c1 = -2 * fp32(1/sqrt 2);
+    # fp32(1/sqrt 2) = 0.707106769084930419921875, so the fp32 rows are
+    # 2.8284270763397216796875 and -1.4142135381698608398437500.
+    arc = O.encode(np.array([[1.0], [3.0]]), 2, 2, O.F32)
+    assert arc["rows"].shape == (1, 2, 1)
+    assert arc["rows"][0, 0, 0] == np.float32(2.8284270763397216796875)
+    assert arc["rows"][0, 1, 0] == np.float32(-1.41421353816986083984375)
+    # one kept frequency: just the block mean times sqrt 2
+    arc1 = O.encode(np.array([[1.0], [3.0], [5.0]]), 2, 1, O.F32)
+    assert arc1["n_blocks"] == 1 and arc1["tail"].tolist() == [[5.0]]
+
+
+def test_all_frequencies_is_lossless():
+    # README "Math": keeping all R rows is lossless per block (up to the fp32
+    # rounding of the basis entries).
+    rng = np.random.default_rng(1)
+    for R in (2, 8, 16):
+        x = rng.standard_normal((2, 3, 4 * R, 16))
+        xh = O.reconstruct(O.project_blocks(x, R, R), R)
+        assert np.abs(xh - x).max() <= 4 * R * 2.0 ** -24 * np.abs(x).max()
+
+
+def test_parseval_when_all_kept():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((6 * 8, 32))
+    C = O.project_blocks(x, 8, 8)
+    e_x = (x.reshape(6, 8, 32) ** 2).sum(axis=(1, 2))
+    e_c = (C ** 2).sum(axis=(1, 2))
+    np.testing.assert_allclose(e_c, e_x, rtol=1e-6)
+
+
+def test_quality_monotone_in_kept_frequencies():
+    # The reconstruction error can only shrink as more frequencies are kept.
+    k, _, _ = syn.small_case(1, 1, 1, 32, 8 * 64, rho=0.95, seed=3)
+    x = syn.bf16_to_numpy(k)[0, 0]
+    errs = []
+    for S in range(1, 9):
+        xh = O.reconstruct(O.project_blocks(x, 8, S), 8)
+        errs.append(np.linalg.norm(xh - x))
+    assert all(errs[i + 1] <= errs[i] + 1e-9 for i in range(7))
+    assert errs[-1] <= 1e-5 * np.linalg.norm(x)
+
+
+def test_k2_cosine_on_correlated_signal():
+    # README test list: k = 2 keeps cosine similarity above 0.99 on a
+    # smooth autocorrelated signal (parity unpinned beyond this bound).
+    k, _, _ = syn.small_case(2, 2, 2, 64, 2048, rho=0.99, seed=4)
+    x = syn.bf16_to_numpy(k)
+    xh = O.reconstruct(O.project_blocks(x, 8, 2), 8)
+    cos = (xh * x).sum() / np.linalg.norm(xh) / np.linalg.norm(x)
+    assert cos > 0.99
+
+
+def test_quantiser_by_hand():
+    # scale = fp32(1.27 / 127) = fp32(0.01) = 0.00999999977648258209228515625
+    # 0.5 / s = 50.0000011..., -1.27 / s = -127.0000028..., 1.27 / s likewise.
+    codes, s = O.quantize_rows(np.array([[0.5, -1.27, 0.0, 1.27]]))
+    assert s.tolist() == [np.float32(0.00999999977648258209228515625)]
+    assert codes.tolist() == [[50, -127, 0, 127]]
+    # ties go to even: scale exactly 1.0 (absmax 127)
+    codes, s = O.quantize_rows(np.array([[127.0, 2.5, -3.5, 0.5, -0.5, 1.5, -126.5]]))
+    assert s.tolist() == [1.0]
+    assert codes.tolist() == [[127, 2, -4, 0, 0, 2, -126]]
+    # an all-zero row: scale 0, codes 0
+    codes, s = O.quantize_rows(np.zeros((1, 5)))
+    assert s.tolist() == [0.0] and codes.tolist() == [[0] * 5]
+
+
+def test_quantiser_invariants():
+    rng = np.random.default_rng(5)
+    C = rng.standard_normal((40, 3, 64)) * rng.uniform(1e-3, 1e3, size=(40, 3, 1))
+    C[0, 1] = 0.0
+    codes, s = O.quantize_rows(C)
+    assert codes.dtype == np.int8 and s.dtype == np.float32
+    assert np.abs(codes.astype(int)).max() <= 127
+    nz = s > 0
+    assert (np.abs(codes.astype(int)).max(axis=-1)[nz] == 127).all()
+    err = np.abs(C - codes.astype(np.float64) * s.astype(np.float64)[..., None])
+    assert (err <= s.astype(np.float64)[..., None] / 2 * (1 + 2.0 ** -40)).all()
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(6)
+    v = (rng.standard_normal(10000) * 10.0 ** rng.uniform(-30, 30, 10000)).astype(np.float32)
+    # exact ties and near-ties on both sides
+    v[:4] = np.array([1.00390625, 1.01171875, -1.00390625, 1.0039063], dtype=np.float32)
+    ours = O.f32_to_bf16_bits(v)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (ours == ref).all()
+
+
+@pytest.mark.parametrize("fmt", [O.F32, O.BF16, O.I8])
+def test_causal_invariant_stream_equals_batch(fmt):
+    # README "Causal-safety design" and cache.py ``append``: only complete
+    # blocks are archived, never rewritten; token-by-token appends give the
+    # same bytes as encoding the whole prefix at once.
+    R, S = 8, 3
+    k, _, _ = syn.small_case(2, 2, 2, 16, 5 * R + 3, seed=8)
+    x = syn.bf16_to_numpy(k)
+    st = O.Stream(R, S, fmt)
+    seen = []
+    for t in range(x.shape[-2]):
+        st.append(x[..., t:t + 1, :])
+        a = st.archive()
+        for i, old in enumerate(seen):
+            assert np.array_equal(a["rows"][..., i, :, :], old)
+        if a["n_blocks"] > len(seen):
+            seen.append(a["rows"][..., len(seen), :, :].copy())
+    full = O.encode(x, R, S, fmt)
+    a = st.archive()
+    assert np.array_equal(a["rows"], full["rows"])
+    if fmt == O.I8:
+        assert np.array_equal(a["scales"], full["scales"])
+    assert np.array_equal(a["tail"], full["tail"]) and a["tail"].shape[-2] == 3
+
+
+# ------------------------------------------------------------- attention ---
+def _sdpa_ref(q, K, V, scale):
+    """torch fp64 CPU scaled_dot_product_attention with kv heads repeated."""
+    G = q.shape[1] // K.shape[1]
+    Kt = torch.from_numpy(np.repeat(K, G, axis=1))
+    Vt = torch.from_numpy(np.repeat(V, G, axis=1))
+    qt = torch.from_numpy(q[:, :, None, :])
+    out = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, scale=scale)
+    return out[:, :, 0, :].numpy()
+
+
+def test_attention_matches_torch_sdpa():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((2, 6, 24))
+    K = rng.standard_normal((2, 3, 77, 24)) * 3
+    V = rng.standard_normal((2, 3, 77, 24))
+    np.testing.assert_allclose(O.attention(q, K, V, 0.3), _sdpa_ref(q, K, V, 0.3), rtol=0, atol=1e-12)
+
+
+def test_attention_by_hand():
+    # T = 3 tokens, D = 2, scale 1: logits 0, 1, 2.
+    q = np.array([[[1.0, 0.0]]])
+    K = np.array([[[[0.0, 0.0], [1.0, 0.0], [2.0, 0.0]]]])
+    V = np.array([[[[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]]]])
+    e = math.e
+    den = 1 + e + e * e
+    want = [(1 + e * e) / den, (e + e * e) / den]
+    np.testing.assert_allclose(O.attention(q, K, V, 1.0)[0, 0], want, rtol=0, atol=1e-15)
+
+
+def test_coefficient_domain_identity():
+    # README "Materialization-free decode attention": with K_block = A S,
+    # q . K[p] = (q . S^T) A[p] and out = (p A) S.  Computed here directly in
+    # the coefficient domain and compared with the oracle's materialised path.
+    R, S, D, G = 8, 3, 16, 2
+    k, v, q = syn.small_case(1, 2 * G, 2, D, 9 * R + 5, seed=10)
+    ka = O.encode(syn.bf16_to_numpy(k), R, S, O.I8)
+    va = O.encode(syn.bf16_to_numpy(v), R, S, O.BF16)
+    qn = syn.bf16_to_numpy(q)[:, :, 0, :]
+    scale = D ** -0.5
+    A = O.dct_basis_f32(R, S).astype(np.float64).T       # R x S synthesis
+    Kc = ka["rows"].astype(np.float64) * ka["scales"].astype(np.float64)[..., None]
+    Vc = O.bf16_bits_to_f64(va["rows"])
+    out = np.empty_like(qn)
+    for hq in range(2 * G):
+        h = hq // G
+        sj = Kc[0, h] @ qn[0, hq]                         # (n, S)
+        z = np.concatenate([(sj @ A.T).reshape(-1), ka["tail"][0, h] @ qn[0, hq]]) * scale
+        p = np.exp(z - z.max())
+        nb = Kc.shape[2]
+        w = p[: nb * R].reshape(nb, R) @ A                # (n, S)
+        acc = np.einsum("ns,nsd->d", w, Vc[0, h]) + p[nb * R:] @ va["tail"][0, h]
+        out[0, hq] = acc / p.sum()
+    got = O.decode_attention(qn, ka, va, scale)
+    np.testing.assert_allclose(got, out, rtol=0, atol=1e-12)
+
+
+def test_identity_codec_equals_plain_attention():
+    # R = 1, S = 1, fp32 rows: the basis is [1] and bf16 values are exact in
+    # fp32, so the archive holds the keys/values themselves.
+    k, v, q = syn.small_case(2, 4, 2, 32, 50, seed=11)
+    K, V, qn = (syn.bf16_to_numpy(t) for t in (k, v, q))
+    got = O.decode_attention(qn, O.encode(K, 1, 1, O.F32), O.encode(V, 1, 1, O.F32), 0.2)
+    np.testing.assert_allclose(got, _sdpa_ref(qn[:, :, 0], K, V, 0.2), rtol=0, atol=1e-12)
+
+
+def test_tail_only_is_plain_attention():
+    k, v, q = syn.small_case(1, 2, 1, 16, 5, seed=12)
+    K, V, qn = (syn.bf16_to_numpy(t) for t in (k, v, q))
+    ka, va = O.encode(K, 8, 2, O.I8), O.encode(V, 8, 2, O.I8)
+    assert ka["n_blocks"] == 0
+    np.testing.assert_allclose(O.decode_attention(qn, ka, va), _sdpa_ref(qn[:, :, 0], K, V, 16 ** -0.5),
+                               rtol=0, atol=1e-12)
+
+
+def test_all_frequencies_attention_close_to_raw():
+    k, v, q = syn.small_case(1, 4, 2, 32, 8 * 20 + 3, seed=13)
+    K, V, qn = (syn.bf16_to_numpy(t) for t in (k, v, q))
+    got = O.decode_attention(qn, O.encode(K, 8, 8, O.F32), O.encode(V, 8, 8, O.F32))
+    ref = _sdpa_ref(qn[:, :, 0], K, V, 32 ** -0.5)
+    assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def test_gqa_equals_repeated_heads():
+    R, S = 8, 2
+    k, v, q = syn.small_case(1, 6, 2, 16, 8 * 7, seed=14)
+    K, V, qn = (syn.bf16_to_numpy(t) for t in (k, v, q))
+    got = O.decode_attention(qn, O.encode(K, R, S, O.I8), O.encode(V, R, S, O.I8))
+    Kr, Vr = np.repeat(K, 3, axis=1), np.repeat(V, 3, axis=1)
+    ref = O.decode_attention(qn, O.encode(Kr, R, S, O.I8), O.encode(Vr, R, S, O.I8))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-13)
+
+
+def test_sampled_heads_match_full():
+    R, S = 8, 3
+    k, v, q = syn.small_case(2, 8, 2, 16, 8 * 5 + 2, seed=15)
+    K, V, qn = (syn.bf16_to_numpy(t) for t in (k, v, q))
+    ka, va = O.encode(K, R, S, O.I8), O.encode(V, R, S, O.BF16)
+    full = O.decode_attention(qn, ka, va, 0.25)
+    part = O.decode_attention_heads(qn, ka, va, 0.25, [(0, 0), (1, 7), (1, 3)])
+    for (b, hq), o in part.items():
+        np.testing.assert_allclose(o, full[b, hq], rtol=0, atol=1e-14)
+
+
+# --------------------------------------------------------------- storage ---
+def _read_table(path):
+    rows = []
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if line:
+            rows.append(line.split())
+    return rows
+
+
+def test_storage_matches_printed_tables(golden_dir):
+    for row in _read_table(os.path.join(golden_dir, "storage_tables.txt")):
+        kind, fmt = row[0], row[1]
+        S, D = int(row[2]), int(row[3])
+        R = 8
+        if kind == "ratio":
+            raw_b, pct, dec = int(row[4]), float(row[5]), int(row[6])
+            n = 1000
+            comp = O.storage_bytes(n, S, D, fmt, 0, raw_b)
+            raw = n * R * D * raw_b
+            assert abs(100.0 * comp / raw - pct) <= 0.5 * 10.0 ** -dec + 1e-9, row
+        else:
+            BH, seq, mb, ratio = int(row[4]), int(row[5]), float(row[6]), float(row[7])
+            n, t = seq // R, seq % R
+            comp = 2 * BH * O.storage_bytes(n, S, D, fmt, t, 4)
+            raw = 2 * BH * seq * D * 4
+            assert abs(comp / 2 ** 20 - mb) <= 0.05 + 1e-9, row
+            assert abs(comp / raw - ratio) <= 0.005 + 1e-9, row
