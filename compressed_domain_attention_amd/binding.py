@@ -60,10 +60,11 @@ def _lib():
         P = ctypes.POINTER(_Stream)
         vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         lib.codec_basis.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_float)]
-        lib.codec_encode_blocks.argtypes = [P, vp, _I64_3, i64, vp]
-        lib.codec_append_step.argtypes = [P, P, vp, _I64_2, vp, _I64_2, vp]
+        LP = ctypes.POINTER(ctypes.c_int64)
+        lib.codec_encode_blocks.argtypes = [P, vp, LP, i64, vp]
+        lib.codec_append_step.argtypes = [P, P, vp, LP, vp, LP, vp]
         lib.codec_decode_workspace_bytes.argtypes = [P, P, i64, ctypes.POINTER(ctypes.c_size_t)]
-        lib.codec_decode_attention.argtypes = [vp, _I64_2, i64, P, P, f32, vp, _I64_2, i32,
+        lib.codec_decode_attention.argtypes = [vp, LP, i64, P, P, f32, vp, LP, i32,
                                                vp, ctypes.c_size_t, vp]
         lib.codec_status_string.argtypes = [ctypes.c_int]
         lib.codec_status_string.restype = ctypes.c_char_p

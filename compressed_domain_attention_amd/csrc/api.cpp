@@ -1,0 +1,335 @@
+// Host side of the C ABI declared in include/cdattn.h: argument validation
+// (always before any HIP call), the DCT basis, the split plan of the decode,
+// and kernel launches.  No allocation, no synchronisation, no state.
+
+#include <math.h>
+#include <string.h>
+
+#include "cdattn.h"
+#include "internal.h"
+
+using namespace cdattn;
+
+namespace {
+
+bool fmt_ok(int f) { return f == CODEC_F32 || f == CODEC_BF16 || f == CODEC_I8; }
+bool raw_ok(int f) { return f == CODEC_F32 || f == CODEC_BF16; }
+int elem_bytes(int f) { return f == CODEC_F32 ? 4 : (f == CODEC_BF16 ? 2 : 1); }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Analysis basis in double, rounded to fp32 (flashcodec-kv README "Math":
+// M[j, i] = c_j cos(pi (2i + 1) j / (2R)), c_0 = sqrt(1/R), c_j = sqrt(2/R)).
+double basis_entry(int R, int j, int i) {
+  const double cj = j == 0 ? sqrt(1.0 / R) : sqrt(2.0 / R);
+  return cj * cos(M_PI * (2 * i + 1) * j / (2.0 * R));
+}
+
+int check_stream(const codec_stream *s) {
+  if (!s) return CODEC_ERR_NULL;
+  if (s->block < 1 || s->block > CODEC_MAX_BLOCK) return CODEC_ERR_SHAPE;
+  if (s->keep < 1 || s->keep > s->block || s->keep > CODEC_MAX_KEEP) return CODEC_ERR_SHAPE;
+  if (s->head_dim < 1) return CODEC_ERR_SHAPE;
+  if (s->batch < 1 || s->heads < 1) return CODEC_ERR_SHAPE;
+  if (s->batch * s->heads > (int64_t)1 << 31) return CODEC_ERR_SHAPE;
+  if (!fmt_ok(s->fmt) || !raw_ok(s->raw_dtype)) return CODEC_ERR_FORMAT;
+  if (s->n_tail < 0 || s->n_tail >= s->block) return CODEC_ERR_STATE;
+  if (s->n_blocks < 0) return CODEC_ERR_STATE;
+  if (s->capacity < s->n_blocks) return CODEC_ERR_CAPACITY;
+  if (!s->tail) return CODEC_ERR_NULL;
+  if (s->capacity > 0 && !s->rows) return CODEC_ERR_NULL;
+  if (s->capacity > 0 && s->fmt == CODEC_I8 && !s->scales) return CODEC_ERR_NULL;
+  if (!aligned16(s->tail) || (s->rows && !aligned16(s->rows)) ||
+      (s->fmt == CODEC_I8 && s->scales && !aligned16(s->scales)))
+    return CODEC_ERR_SHAPE;
+  if (s->head_dim != 64 && s->head_dim != 128 && s->head_dim != 256) return CODEC_ERR_UNSUPPORTED;
+  return CODEC_OK;
+}
+
+bool same_geometry(const codec_stream *a, const codec_stream *b) {
+  return a->block == b->block && a->keep == b->keep && a->head_dim == b->head_dim && a->batch == b->batch &&
+         a->heads == b->heads && a->n_blocks == b->n_blocks && a->n_tail == b->n_tail;
+}
+
+void fill_M(int R, int S, float *M) {
+  for (int j = 0; j < S; ++j)
+    for (int i = 0; i < R; ++i) M[j * R + i] = (float)basis_entry(R, j, i);
+}
+
+EncodeArgs stream_encode_args(const codec_stream *s) {
+  EncodeArgs e;
+  memset(&e, 0, sizeof(e));
+  e.raw = s->raw_dtype;
+  e.fmt = s->fmt;
+  e.R = s->block;
+  e.S = s->keep;
+  e.H = s->heads;
+  e.n0 = s->n_blocks;
+  e.cap = s->capacity;
+  e.rows = s->rows;
+  e.scales = s->scales;
+  e.tail = s->tail;
+  return e;
+}
+
+// Split plan of the decode: splits per (b, kv head, query group), blocks per
+// split, workgroups.  A pure function of the shapes.
+struct Plan {
+  int GS, NQG, SP, ns;
+  int64_t pairs, chunk, n_wg;
+  size_t off_ml, off_acc, bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workgroups that fill MI355X once: 256 CUs x 2 resident 8-wave workgroups.
+constexpr int64_t kTargetWorkgroups = 512;
+
+Plan make_plan(const codec_stream *k, int64_t Hq) {
+  Plan p;
+  const int64_t G = Hq / k->heads;
+  p.GS = decode_group_size((int)G);
+  p.NQG = (int)(G / p.GS);
+  p.SP = decode_pad_keep(k->keep);
+  p.pairs = k->batch * k->heads * p.NQG;
+  const int64_t n = k->n_blocks;
+  const int64_t NB = decode_tile_rows(k->head_dim) / k->keep;   // blocks per tile
+  if (n == 0) {
+    p.ns = 1;
+    p.chunk = 0;
+  } else {
+    const int64_t tiles = (n + NB - 1) / NB;
+    const int64_t min_tiles = kDecodeWaves / 2;                   // tiles per split, at least
+    int64_t ns = (kTargetWorkgroups + p.pairs - 1) / p.pairs;
+    int64_t ns_max = (tiles + min_tiles - 1) / min_tiles;
+    if (ns > ns_max) ns = ns_max;
+    if (ns < 1) ns = 1;
+    if (ns > 1024) ns = 1024;
+    int64_t chunk_tiles = (tiles + ns - 1) / ns;
+    p.chunk = chunk_tiles * NB;
+    p.ns = (int)((n + p.chunk - 1) / p.chunk);
+  }
+  p.n_wg = p.pairs * p.ns;
+  const size_t counters = align256((size_t)p.pairs * 4);
+  const size_t ml = align256((size_t)p.pairs * p.ns * p.GS * 2 * 4);
+  const size_t acc = (size_t)p.pairs * p.ns * p.GS * k->head_dim * 4;
+  p.off_ml = counters;
+  p.off_acc = counters + ml;
+  p.bytes = counters + ml + acc;
+  return p;
+}
+
+int check_decode(const codec_stream *k, const codec_stream *v, int64_t Hq) {
+  int rc = check_stream(k);
+  if (rc) return rc;
+  rc = check_stream(v);
+  if (rc) return rc;
+  if (!same_geometry(k, v)) return CODEC_ERR_SHAPE;
+  if (Hq < 1 || Hq % k->heads != 0) return CODEC_ERR_SHAPE;
+  if (k->n_blocks * k->block + k->n_tail == 0) return CODEC_ERR_SHAPE;
+  return CODEC_OK;
+}
+
+}  // namespace
+
+namespace cdattn {
+int decode_group_size(int G) {
+  if (G % 8 == 0) return 8;
+  if (G % 4 == 0) return 4;
+  if (G % 2 == 0) return 2;
+  return 1;
+}
+int decode_pad_keep(int S) {
+  int sp = 2;
+  while (sp < S) sp *= 2;
+  return sp;
+}
+int launch_decode(int D, int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_decode_d64(GS, SP, a, n_wg, stream);
+    case 128: return launch_decode_d128(GS, SP, a, n_wg, stream);
+    case 256: return launch_decode_d256(GS, SP, a, n_wg, stream);
+    default: return -1;
+  }
+}
+}  // namespace cdattn
+
+extern "C" {
+
+const char *codec_status_string(int status) {
+  switch (status) {
+    case CODEC_OK: return "ok";
+    case CODEC_ERR_NULL: return "a required pointer is NULL";
+    case CODEC_ERR_SHAPE: return "size out of range, shapes disagree, or misaligned buffer";
+    case CODEC_ERR_FORMAT: return "unknown or unsupported format";
+    case CODEC_ERR_CAPACITY: return "archive capacity too small";
+    case CODEC_ERR_STATE: return "stream counters forbid this call";
+    case CODEC_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case CODEC_ERR_UNSUPPORTED: return "no kernel for this configuration";
+    case CODEC_ERR_HIP: return "HIP runtime or kernel launch error";
+    case CODEC_ERR_SCALE: return "scale must be finite and positive";
+    default: return "unknown status";
+  }
+}
+
+int codec_basis(int32_t R, int32_t S, float *A_host) {
+  if (!A_host) return CODEC_ERR_NULL;
+  if (R < 1 || R > CODEC_MAX_BLOCK || S < 1 || S > R || S > CODEC_MAX_KEEP) return CODEC_ERR_SHAPE;
+  for (int i = 0; i < R; ++i)
+    for (int j = 0; j < S; ++j) A_host[i * S + j] = (float)basis_entry(R, j, i);
+  return CODEC_OK;
+}
+
+int codec_encode_blocks(codec_stream *s, const void *x, const int64_t x_stride[3], int64_t T,
+                        hipStream_t stream) {
+  int rc = check_stream(s);
+  if (rc) return rc;
+  if (!x_stride) return CODEC_ERR_NULL;
+  if (T < 0) return CODEC_ERR_SHAPE;
+  if (T > 0 && !x) return CODEC_ERR_NULL;
+  if (s->n_tail != 0) return CODEC_ERR_STATE;
+  const int64_t R = s->block;
+  const int64_t n_new = T / R;
+  const int32_t t = (int32_t)(T % R);
+  if (n_new > 0 && s->n_blocks + n_new > s->capacity) return CODEC_ERR_CAPACITY;
+  if (T > 0) {
+    if (!aligned16(x)) return CODEC_ERR_SHAPE;
+    for (int i = 0; i < 3; ++i)
+      if (x_stride[i] < 0 || x_stride[i] % 8 != 0) return CODEC_ERR_SHAPE;
+  }
+  if (T == 0) return CODEC_OK;
+  EncodeLaunch L;
+  memset(&L, 0, sizeof(L));
+  L.e = stream_encode_args(s);
+  L.e.src0 = x;
+  L.e.s0_b = x_stride[0];
+  L.e.s0_h = x_stride[1];
+  L.e.s0_t = x_stride[2];
+  L.e.src1 = x;
+  L.e.split_i = (int32_t)R;
+  L.e.n_new = n_new;
+  L.e.n_copy = t;
+  fill_M((int)R, s->keep, L.M);
+  (void)hipGetLastError();
+  if (launch_encode(s->head_dim, L, s->batch * s->heads, stream) != 0) return CODEC_ERR_HIP;
+  s->n_blocks += n_new;
+  s->n_tail = t;
+  return CODEC_OK;
+}
+
+int codec_append_step(codec_stream *k, codec_stream *v, const void *k_new, const int64_t kn_stride[2],
+                      const void *v_new, const int64_t vn_stride[2], hipStream_t stream) {
+  int rc = check_stream(k);
+  if (rc) return rc;
+  rc = check_stream(v);
+  if (rc) return rc;
+  if (!same_geometry(k, v)) return CODEC_ERR_SHAPE;
+  if (!k_new || !v_new || !kn_stride || !vn_stride) return CODEC_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return CODEC_ERR_SHAPE;
+  for (int i = 0; i < 2; ++i)
+    if (kn_stride[i] < 0 || kn_stride[i] % 8 != 0 || vn_stride[i] < 0 || vn_stride[i] % 8 != 0)
+      return CODEC_ERR_SHAPE;
+  const int complete = (k->n_tail + 1 == k->block) ? 1 : 0;
+  if (complete && (k->n_blocks + 1 > k->capacity || v->n_blocks + 1 > v->capacity)) return CODEC_ERR_CAPACITY;
+  AppendArgs A;
+  memset(&A, 0, sizeof(A));
+  const codec_stream *ss[2] = {k, v};
+  const void *nw[2] = {k_new, v_new};
+  const int64_t *ns[2] = {kn_stride, vn_stride};
+  for (int i = 0; i < 2; ++i) {
+    EncodeArgs &e = A.e[i];
+    e = stream_encode_args(ss[i]);
+    const int64_t R = ss[i]->block, D = ss[i]->head_dim;
+    e.src0 = ss[i]->tail;
+    e.s0_b = ss[i]->heads * R * D;
+    e.s0_h = R * D;
+    e.s0_t = D;
+    e.src1 = nw[i];
+    e.s1_b = ns[i][0];
+    e.s1_h = ns[i][1];
+    e.split_i = (int32_t)(R - 1);
+    e.n_new = 1;
+  }
+  A.t = k->n_tail;
+  A.complete = complete;
+  fill_M(k->block, k->keep, A.M);
+  (void)hipGetLastError();
+  if (launch_append(k->head_dim, A, k->batch * k->heads, stream) != 0) return CODEC_ERR_HIP;
+  for (codec_stream *s : {k, v}) {
+    if (complete) {
+      s->n_blocks += 1;
+      s->n_tail = 0;
+    } else {
+      s->n_tail += 1;
+    }
+  }
+  return CODEC_OK;
+}
+
+int codec_decode_workspace_bytes(const codec_stream *k, const codec_stream *v, int64_t Hq, size_t *bytes) {
+  if (!bytes) return CODEC_ERR_NULL;
+  const int rc = check_decode(k, v, Hq);
+  if (rc) return rc;
+  *bytes = make_plan(k, Hq).bytes;
+  return CODEC_OK;
+}
+
+int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
+                           const codec_stream *v, float scale, void *out, const int64_t out_stride[2],
+                           int32_t out_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !q_stride || !out || !out_stride) return CODEC_ERR_NULL;
+  int rc = check_decode(k, v, Hq);
+  if (rc) return rc;
+  if (out_dtype != CODEC_F32 && out_dtype != CODEC_BF16) return CODEC_ERR_FORMAT;
+  if (!(scale > 0.0f) || !isfinite(scale)) return CODEC_ERR_SCALE;
+  if (!aligned16(q) || q_stride[0] < 0 || q_stride[1] < 0 || q_stride[0] % 8 || q_stride[1] % 8)
+    return CODEC_ERR_SHAPE;
+  if (out_stride[0] < 0 || out_stride[1] < 0) return CODEC_ERR_SHAPE;
+  const Plan p = make_plan(k, Hq);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < p.bytes)
+    return CODEC_ERR_WORKSPACE;
+
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t *>(q);
+  a.q_sb = q_stride[0];
+  a.q_sh = q_stride[1];
+  a.krows = k->rows;
+  a.kscales = k->scales;
+  a.ktail = k->tail;
+  a.vrows = v->rows;
+  a.vscales = v->scales;
+  a.vtail = v->tail;
+  a.k_bh_rows = k->capacity * k->keep;
+  a.v_bh_rows = v->capacity * v->keep;
+  a.kf = k->fmt;
+  a.vf = v->fmt;
+  a.kraw = k->raw_dtype;
+  a.vraw = v->raw_dtype;
+  a.H = (int32_t)k->heads;
+  a.G = (int32_t)(Hq / k->heads);
+  a.NQG = p.NQG;
+  a.R = k->block;
+  a.S = k->keep;
+  a.n_blocks = k->n_blocks;
+  a.n_tail = k->n_tail;
+  a.ns = p.ns;
+  a.chunk = p.chunk;
+  a.qk_scale = (float)((double)scale * 1.4426950408889634);   // log2(e)
+  a.out = out;
+  a.o_sb = out_stride[0];
+  a.o_sh = out_stride[1];
+  a.out_f32 = out_dtype == CODEC_F32 ? 1 : 0;
+  char *ws = static_cast<char *>(workspace);
+  a.counters = reinterpret_cast<uint32_t *>(ws);
+  a.part_ml = reinterpret_cast<float *>(ws + p.off_ml);
+  a.part_acc = reinterpret_cast<float *>(ws + p.off_acc);
+  for (int r = 0; r < k->block; ++r)
+    for (int j = 0; j < p.SP; ++j) a.A[r * p.SP + j] = j < k->keep ? (float)basis_entry(k->block, j, r) : 0.0f;
+  (void)hipGetLastError();
+  const int lr = launch_decode(k->head_dim, p.GS, p.SP, a, p.n_wg, stream);
+  if (lr < 0) return CODEC_ERR_UNSUPPORTED;
+  if (lr > 0) return CODEC_ERR_HIP;
+  return CODEC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,8 @@
+// Decode-attention kernels for head_dim 64 (instantiations of decode_impl.h).
+#include "decode_impl.h"
+
+namespace cdattn {
+int launch_decode_d64(int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
+  return dec::launch_d<64>(GS, SP, a, n_wg, stream);
+}
+}  // namespace cdattn

@@ -1,0 +1,243 @@
+// Block DCT-II encode of raw key/value tokens into the compressed archive,
+// and the single-token append that archives a block when it completes.
+//
+// Method: flashcodec-kv 1.0.0 README, section "Math" (JPEG item): every
+// complete block X of R tokens (R x D) is stored as the S lowest rows of
+// C = M X, M the orthonormal DCT-II; README paragraph on 8-bit
+// quantisation and cache.py ``_archive_spec``: optional int8 codes with one
+// fp32 scale per (block, frequency) row; cache.py ``append``: complete
+// blocks are archived, the remainder stays raw in the tail.
+//
+// Arithmetic contract (bit-exact, shared with the CPU reference by
+// specification only):
+//   c[j][d] = sum over i = 0..R-1, in that order, starting from +0.0, of
+//             fp64(M[j][i]) * fp64(x[i][d])      (products exact in fp64)
+//   fp32 rows: fp32(c) (RNE);  bf16 rows: bf16(fp32(c)) (RNE, RNE)
+//   int8 rows: a = max_d |c|, scale = fp32(a / 127) (fp64 divide, RNE),
+//              code = clamp(rint_even(c / fp64(scale)), -127, 127),
+//              scale == 0 -> all codes 0.
+// The quotient c / scale is evaluated as c * (1 / scale); within 1e-9 of a
+// half-integer it is recomputed with an IEEE fp64 division.  The product
+// differs from the correctly rounded quotient by < 6e-14 for |c/scale| <=
+// 128, so both round to the same integer everywhere outside that band.
+//
+// The encode is streaming work (S fp64 FMAs per input element): plain fp64
+// VALU, one wave per block, lanes along head_dim.  MFMA is not used because
+// the contract fixes the order of the R additions.
+
+#include "internal.h"
+
+namespace cdattn {
+namespace {
+
+__device__ inline uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Load EPL consecutive raw elements (bf16 or fp32) as floats.
+template <int EPL>
+__device__ inline void load_raw(const void *base, int64_t elem_off, int raw, float (&x)[EPL]) {
+  if (raw == BF16) {
+    const uint16_t *p = static_cast<const uint16_t *>(base) + elem_off;
+    if constexpr (EPL == 1) {
+      x[0] = __uint_as_float((uint32_t)p[0] << 16);
+    } else if constexpr (EPL == 2) {
+      uint32_t w = *reinterpret_cast<const uint32_t *>(p);
+      x[0] = __uint_as_float(w << 16);
+      x[1] = __uint_as_float(w & 0xFFFF0000u);
+    } else {
+      uint2 w = *reinterpret_cast<const uint2 *>(p);
+      x[0] = __uint_as_float(w.x << 16);
+      x[1] = __uint_as_float(w.x & 0xFFFF0000u);
+      x[2] = __uint_as_float(w.y << 16);
+      x[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    }
+  } else {
+    const float *p = static_cast<const float *>(base) + elem_off;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = p[e];
+  }
+}
+
+template <int EPL>
+__device__ inline void store_raw(void *base, int64_t elem_off, int raw, const float (&x)[EPL]) {
+  if (raw == BF16) {
+    uint16_t *p = static_cast<uint16_t *>(base) + elem_off;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) p[e] = (uint16_t)(__float_as_uint(x[e]) >> 16);  // exact: x holds bf16 values
+  } else {
+    float *p = static_cast<float *>(base) + elem_off;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) p[e] = x[e];
+  }
+}
+
+__device__ inline double wave_max_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ inline int8_t quantise(double c, float s32, double inv) {
+  if (s32 == 0.0f) return 0;
+  double y = c * inv;
+  double r = rint(y);
+  if (fabs(y - floor(y) - 0.5) < 1e-9) r = rint(c / (double)s32);
+  r = fmin(fmax(r, -127.0), 127.0);
+  return (int8_t)(int)r;
+}
+
+// Encode block `n` (call-relative) of stream row (b, h) into archive slot
+// a.n0 + n.  One wave; lane owns head_dim elements [lane*EPL, lane*EPL+EPL).
+template <int EPL, int SP>
+__device__ void encode_block(const EncodeArgs &a, const float *__restrict__ M, int64_t b, int64_t h,
+                             int64_t n, int lane) {
+  constexpr int D = EPL * 64;
+  const int d0 = lane * EPL;
+  const int R = a.R, S = a.S;
+  double c[SP][EPL];
+#pragma unroll
+  for (int j = 0; j < SP; ++j)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) c[j][e] = 0.0;  // +0.0
+
+  for (int i = 0; i < R; ++i) {
+    float x[EPL];
+    if (i < a.split_i)
+      load_raw<EPL>(a.src0, b * a.s0_b + h * a.s0_h + (n * R + i) * a.s0_t + d0, a.raw, x);
+    else
+      load_raw<EPL>(a.src1, b * a.s1_b + h * a.s1_h + d0, a.raw, x);
+#pragma unroll
+    for (int j = 0; j < SP; ++j) {
+      if (j < S) {
+        const double m = (double)M[j * R + i];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) c[j][e] = fma(m, (double)x[e], c[j][e]);
+      }
+    }
+  }
+
+  const int64_t slot = (b * a.H + h) * a.cap + a.n0 + n;
+#pragma unroll
+  for (int j = 0; j < SP; ++j) {
+    if (j >= S) break;
+    const int64_t row = (slot * S + j) * D + d0;
+    if (a.fmt == F32) {
+      float *p = static_cast<float *>(a.rows) + row;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) p[e] = (float)c[j][e];
+    } else if (a.fmt == BF16) {
+      uint16_t *p = static_cast<uint16_t *>(a.rows) + row;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) p[e] = bf16_rne((float)c[j][e]);
+    } else {
+      double amax = 0.0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) amax = fmax(amax, fabs(c[j][e]));
+      amax = wave_max_f64(amax);
+      const float s32 = (float)(amax / 127.0);
+      const double inv = s32 != 0.0f ? 1.0 / (double)s32 : 0.0;
+      int8_t *p = static_cast<int8_t *>(a.rows) + row;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) p[e] = quantise(c[j][e], s32, inv);
+      if (lane == 0) a.scales[slot * S + j] = s32;
+    }
+  }
+}
+
+// Grid: x = (b, h) * per_bh + wave-group; each wave one block (or the tail copy).
+template <int EPL, int SP>
+__global__ __launch_bounds__(64 * kEncodeWaves) void encode_kernel(EncodeLaunch L, int64_t per_bh) {
+  const EncodeArgs &a = L.e;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t bh = blockIdx.x / per_bh;
+  const int64_t n = (blockIdx.x % per_bh) * kEncodeWaves + wave;
+  const int64_t b = bh / a.H, h = bh % a.H;
+  if (n < a.n_new) {
+    encode_block<EPL, SP>(a, L.M, b, h, n, lane);
+  } else if (n == a.n_new && a.n_copy > 0) {
+    // raw remainder -> tail slots 0 .. n_copy-1, verbatim
+    const int d0 = lane * EPL;
+    for (int i = 0; i < a.n_copy; ++i) {
+      float x[EPL];
+      load_raw<EPL>(a.src0, b * a.s0_b + h * a.s0_h + (a.n_new * a.R + i) * a.s0_t + d0, a.raw, x);
+      store_raw<EPL>(a.tail, ((bh * a.R) + i) * (EPL * 64) + d0, a.raw, x);
+    }
+  }
+}
+
+// Grid: x = (b, h), y = stream (0 keys, 1 values); one wave each.
+template <int EPL, int SP>
+__global__ __launch_bounds__(64) void append_kernel(AppendArgs A) {
+  const EncodeArgs &a = A.e[blockIdx.y];
+  const int lane = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / a.H, h = bh % a.H;
+  if (A.complete) {
+    // tail slots 0..R-2 plus the new token form the block; slot R-1 of the
+    // tail is not written since the tail empties.
+    encode_block<EPL, SP>(a, A.M, b, h, 0, lane);
+  } else {
+    const int d0 = lane * EPL;
+    float x[EPL];
+    load_raw<EPL>(a.src1, b * a.s1_b + h * a.s1_h + d0, a.raw, x);
+    store_raw<EPL>(a.tail, ((bh * a.R) + A.t) * (EPL * 64) + d0, a.raw, x);
+  }
+}
+
+template <int EPL>
+int launch_encode_epl(int SP, const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
+  const int64_t units = L.e.n_new + (L.e.n_copy > 0 ? 1 : 0);
+  if (units == 0) return 0;
+  const int64_t per_bh = (units + kEncodeWaves - 1) / kEncodeWaves;
+  const dim3 grid((unsigned)(per_bh * BH)), block(64 * kEncodeWaves);
+  switch (SP) {
+    case 2: hipLaunchKernelGGL((encode_kernel<EPL, 2>), grid, block, 0, stream, L, per_bh); break;
+    case 4: hipLaunchKernelGGL((encode_kernel<EPL, 4>), grid, block, 0, stream, L, per_bh); break;
+    case 8: hipLaunchKernelGGL((encode_kernel<EPL, 8>), grid, block, 0, stream, L, per_bh); break;
+    case 16: hipLaunchKernelGGL((encode_kernel<EPL, 16>), grid, block, 0, stream, L, per_bh); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+template <int EPL>
+int launch_append_epl(int SP, const AppendArgs &A, int64_t BH, hipStream_t stream) {
+  const dim3 grid((unsigned)BH, 2), block(64);
+  switch (SP) {
+    case 2: hipLaunchKernelGGL((append_kernel<EPL, 2>), grid, block, 0, stream, A); break;
+    case 4: hipLaunchKernelGGL((append_kernel<EPL, 4>), grid, block, 0, stream, A); break;
+    case 8: hipLaunchKernelGGL((append_kernel<EPL, 8>), grid, block, 0, stream, A); break;
+    case 16: hipLaunchKernelGGL((append_kernel<EPL, 16>), grid, block, 0, stream, A); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+}  // namespace
+
+// Returns 0 on success, 1 on a HIP launch error, -1 if no kernel exists.
+int launch_encode(int D, const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
+  const int SP = decode_pad_keep(L.e.S);
+  switch (D) {
+    case 64: return launch_encode_epl<1>(SP, L, BH, stream);
+    case 128: return launch_encode_epl<2>(SP, L, BH, stream);
+    case 256: return launch_encode_epl<4>(SP, L, BH, stream);
+    default: return -1;
+  }
+}
+
+int launch_append(int D, const AppendArgs &A, int64_t BH, hipStream_t stream) {
+  const int SP = decode_pad_keep(A.e[0].S);
+  switch (D) {
+    case 64: return launch_append_epl<1>(SP, A, BH, stream);
+    case 128: return launch_append_epl<2>(SP, A, BH, stream);
+    case 256: return launch_append_epl<4>(SP, A, BH, stream);
+    default: return -1;
+  }
+}
+
+}  // namespace cdattn

@@ -1,0 +1,101 @@
+// Internal declarations shared by the host API and the kernel translation
+// units of libcdattn.so.  Not part of the public ABI (include/cdattn.h).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace cdattn {
+
+constexpr int kMaxR = 32;      // tokens per block
+constexpr int kMaxS = 16;      // kept frequencies
+constexpr int kDecodeWaves = 8;   // waves per decode workgroup
+constexpr int kEncodeWaves = 4;   // waves (one block each) per encode workgroup
+
+enum Fmt : int32_t { F32 = 0, BF16 = 1, I8 = 2 };
+
+// ---------------------------------------------------------------- encode --
+// Where the R tokens of a block come from.  Token i of block n of (b, h):
+//   i <  split_i : src0 + b*s0_b + h*s0_h + (n*R + i)*s0_t      (x or tail)
+//   i >= split_i : src1 + b*s1_b + h*s1_h                        (new token)
+struct EncodeArgs {
+  const void *src0;
+  int64_t s0_b, s0_h, s0_t;
+  const void *src1;
+  int64_t s1_b, s1_h;
+  int32_t split_i;        // R for a plain run of tokens, R-1 for an append
+  int32_t raw;            // Fmt of the source tokens (BF16 or F32)
+  int32_t fmt;            // Fmt of the coefficient rows
+  int32_t R, S;
+  int64_t H;              // heads (b = bh / H)
+  int64_t n_new;          // blocks to encode per (b, h)
+  int64_t n0;             // first destination slot
+  int64_t cap;            // archive capacity (blocks)
+  void *rows;             // [B][H][cap][S][D]
+  float *scales;          // [B][H][cap][S] (I8)
+  // tail copy (encode_blocks only): tokens n_new*R .. n_new*R + n_copy - 1
+  int32_t n_copy;
+  void *tail;             // [B][H][R][D], raw dtype
+};
+
+struct EncodeLaunch {
+  EncodeArgs e;
+  float M[kMaxS * kMaxR]; // analysis basis, M[j*R + i] = fp32(c_j cos(..))
+};
+
+// Append one token: tail slot t <- new token; if t + 1 == R the same launch
+// encodes the block (tail slots 0..R-2 and the new token) into slot n.
+struct AppendArgs {
+  EncodeArgs e[2];        // [0] = keys, [1] = values; src0 = tail, src1 = new
+  int32_t t;              // tail slot the new token goes to
+  int32_t complete;       // 1 if this token completes a block
+  float M[kMaxS * kMaxR]; // shared analysis basis (keys and values share R, S)
+};
+
+int launch_encode(int D, const EncodeLaunch &a, int64_t BH, hipStream_t stream);
+int launch_append(int D, const AppendArgs &a, int64_t BH, hipStream_t stream);
+
+// ---------------------------------------------------------------- decode --
+struct DecodeArgs {
+  const uint16_t *q;      // bf16 (B, Hq, 1, D)
+  int64_t q_sb, q_sh;
+  const void *krows;
+  const float *kscales;
+  const void *ktail;
+  const void *vrows;
+  const float *vscales;
+  const void *vtail;
+  int64_t k_bh_rows;      // coefficient rows per (b, h) in the key archive
+  int64_t v_bh_rows;
+  int32_t kf, vf;         // row formats
+  int32_t kraw, vraw;     // tail formats
+  int32_t H, G, NQG;      // kv heads, group size, query groups per kv head
+  int32_t R, S;
+  int64_t n_blocks;
+  int32_t n_tail;
+  int32_t ns;             // splits per (b, h, query group)
+  int64_t chunk;          // blocks per split
+  float qk_scale;         // softmax scale * log2(e)
+  void *out;
+  int64_t o_sb, o_sh;
+  int32_t out_f32;        // 1: fp32 out, 0: bf16 out
+  uint32_t *counters;     // one per (b, h, query group)
+  float *part_ml;         // [pairs][ns][GS][2]
+  float *part_acc;        // [pairs][ns][GS][D]
+  float A[kMaxR * kMaxS]; // synthesis basis A[r*SP + j], zero padded to SP
+};
+
+// Heads of one query group handled per workgroup, and padded kept rows.
+int decode_group_size(int G);
+int decode_pad_keep(int S);
+// rows of a K/V tile for head_dim D
+inline int decode_tile_rows(int D) { return 8192 / D; }
+
+int launch_decode(int D, int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
+int launch_decode_d64(int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
+int launch_decode_d128(int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
+int launch_decode_d256(int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
+
+}  // namespace cdattn

@@ -82,14 +82,15 @@ def to_bf16(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
 
 
-def ar1_sequence(B, H, T, D, rho, seed, offset_var=0.0, offset_seed=None):
-    """(B, H, T, D) bf16 CPU tensor of AR(1) sequences along T.
+def ar1_sequence(B, H, T, D, rho, seed, offset_var=0.0, offset_seed=None, dtype=torch.bfloat16):
+    """(B, H, T, D) CPU tensor of AR(1) sequences along T (bf16, or float32
+    rounded from float64 when dtype is torch.float32).
 
     Generated one batch row at a time to bound host memory.
     """
     from scipy.signal import lfilter
 
-    out = torch.empty((B, H, T, D), dtype=torch.bfloat16)
+    out = torch.empty((B, H, T, D), dtype=dtype)
     sd = 1.0 / np.sqrt(1.0 - rho * rho) if rho < 1 else 1.0
     for b in range(B):
         g = _rng(seed, b)
@@ -103,7 +104,7 @@ def ar1_sequence(B, H, T, D, rho, seed, offset_var=0.0, offset_seed=None):
         if offset_var:
             go = _rng(offset_seed if offset_seed is not None else seed + 1, b)
             x = x + go.standard_normal((H, 1, D)) * np.sqrt(offset_var)
-        out[b] = to_bf16(x)
+        out[b] = to_bf16(x) if dtype == torch.bfloat16 else torch.from_numpy(x.astype(np.float32))
     return out
 
 
@@ -131,14 +132,14 @@ def workload_query(w, step=0):
     return gaussian((w.B, w.Hq, 1, w.D), 1000 * w.index + STREAM_Q + 100 * step)
 
 
-def small_case(B, Hq, Hkv, D, T, rho=0.95, seed=7, offset_var=0.0):
-    """Ad-hoc small K, V, q for tests (bf16 CPU tensors)."""
-    k = ar1_sequence(B, Hkv, T, D, rho, seed * 10 + STREAM_K, offset_var, seed * 10 + STREAM_OFF)
-    v = ar1_sequence(B, Hkv, T, D, rho, seed * 10 + STREAM_V, offset_var, seed * 10 + STREAM_OFF + 5)
+def small_case(B, Hq, Hkv, D, T, rho=0.95, seed=7, offset_var=0.0, dtype=torch.bfloat16):
+    """Ad-hoc small K, V (bf16 or float32) and bf16 q CPU tensors for tests."""
+    k = ar1_sequence(B, Hkv, T, D, rho, seed * 10 + STREAM_K, offset_var, seed * 10 + STREAM_OFF, dtype)
+    v = ar1_sequence(B, Hkv, T, D, rho, seed * 10 + STREAM_V, offset_var, seed * 10 + STREAM_OFF + 5, dtype)
     q = gaussian((B, Hq, 1, D), seed * 10 + STREAM_Q)
     return k, v, q
 
 
 def bf16_to_numpy(t):
-    """bf16 torch tensor -> float64 numpy array holding the same values."""
+    """bf16 / float32 torch tensor -> float64 numpy array holding the same values."""
     return t.detach().to("cpu").to(torch.float32).numpy().astype(np.float64)

@@ -1,0 +1,183 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, the host-computed basis equals the oracle's bit for bit, and
+every validation error is reported before any HIP call, leaving the stream
+counters untouched.  Only calls that fail validation (or are pure host
+functions) are made here.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from compressed_domain_attention_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cdattn.h")
+
+OK, NULL, SHAPE, FORMAT, CAPACITY, STATE, WORKSPACE, UNSUPPORTED, HIP, SCALE = range(10)
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bd.library_path()), reason="libcdattn.so not built")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return bd.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^(?:int|size_t|const char \*)\s*\*?\s*(codec_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert set(names) == {"codec_basis", "codec_encode_blocks", "codec_append_step",
+                          "codec_decode_workspace_bytes", "codec_decode_attention", "codec_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    seen = set()
+    for s in range(10):
+        t = lib.codec_status_string(s).decode()
+        assert t and t not in seen
+        seen.add(t)
+    assert lib.codec_status_string(1234).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 12, 16, 31, 32])
+def test_basis_bitwise_equals_oracle(lib, R):
+    for S in range(1, min(R, 16) + 1):
+        A = (ctypes.c_float * (R * S))()
+        assert lib.codec_basis(R, S, A) == OK
+        got = np.frombuffer(A, dtype=np.float32).reshape(R, S)
+        want = O.dct_basis_f32(R, S).T
+        assert got.tobytes() == np.ascontiguousarray(want).tobytes(), (R, S)
+
+
+def test_basis_errors(lib):
+    A = (ctypes.c_float * 64)()
+    assert lib.codec_basis(8, 2, None) == NULL
+    assert lib.codec_basis(0, 1, A) == SHAPE
+    assert lib.codec_basis(8, 9, A) == SHAPE
+    assert lib.codec_basis(33, 2, A) == SHAPE
+    assert lib.codec_basis(32, 17, A) == SHAPE
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
+
+
+def stream(**kw):
+    d = bd._Stream()
+    d.block, d.keep, d.head_dim, d.fmt, d.raw_dtype, d.n_tail = 8, 2, 128, bd.FMT_I8, bd.FMT_BF16, 0
+    d.batch, d.heads, d.capacity, d.n_blocks = 2, 4, 16, 0
+    d.rows, d.scales, d.tail = FAKE, FAKE, FAKE
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def encode(lib, s, x=FAKE, strides=(4096, 1024, 128), T=40):
+    return lib.codec_encode_blocks(ctypes.byref(s) if s is not None else None, x, bd._I64_3(*strides), T, None)
+
+
+def test_encode_validation(lib):
+    assert encode(lib, None) == NULL
+    for kw, want in [({"block": 0}, SHAPE), ({"block": 33}, SHAPE), ({"keep": 9}, SHAPE), ({"keep": 17, "block": 32}, SHAPE),
+                     ({"fmt": 7}, FORMAT), ({"raw_dtype": bd.FMT_I8}, FORMAT), ({"n_tail": 3}, STATE),
+                     ({"n_tail": 8}, STATE), ({"capacity": 4}, CAPACITY), ({"head_dim": 96}, UNSUPPORTED),
+                     ({"head_dim": 0}, SHAPE), ({"batch": 0}, SHAPE), ({"tail": None}, NULL),
+                     ({"rows": None}, NULL), ({"scales": None}, NULL), ({"tail": FAKE + 4}, SHAPE),
+                     ({"n_blocks": 10, "capacity": 8}, CAPACITY)]:
+        s = stream(**kw)
+        before = (s.n_blocks, s.n_tail)
+        assert encode(lib, s, T=200) == want, kw
+        assert (s.n_blocks, s.n_tail) == before
+    s = stream()
+    assert encode(lib, s, x=None) == NULL
+    assert encode(lib, s, T=-1) == SHAPE
+    assert encode(lib, s, x=FAKE + 8) == SHAPE
+    assert encode(lib, s, strides=(4096, 1024, 3)) == SHAPE
+    assert lib.codec_encode_blocks(ctypes.byref(s), FAKE, None, 8, None) == NULL
+    # 16 blocks fit, 17 do not
+    assert encode(lib, stream(capacity=16), T=17 * 8) == CAPACITY
+    # T == 0 is a no-op that succeeds without touching the GPU
+    s = stream()
+    assert encode(lib, s, T=0) == OK and (s.n_blocks, s.n_tail) == (0, 0)
+
+
+def test_append_validation(lib):
+    two = bd._I64_2(1024, 128)
+
+    def app(k, v, kn=FAKE, vn=FAKE, ks=two, vs=two):
+        return lib.codec_append_step(ctypes.byref(k), ctypes.byref(v), kn, ks, vn, vs, None)
+
+    assert app(stream(), stream(head_dim=64)) == SHAPE
+    assert app(stream(), stream(n_tail=1)) == SHAPE
+    assert app(stream(), stream(n_blocks=1)) == SHAPE
+    assert app(stream(), stream(), kn=None) == NULL
+    assert app(stream(), stream(), vs=None) == NULL
+    assert app(stream(), stream(), kn=FAKE + 2) == SHAPE
+    assert app(stream(), stream(), ks=bd._I64_2(1024, 130)) == SHAPE
+    # completing a block with a full archive
+    k, v = stream(n_tail=7, n_blocks=16), stream(n_tail=7, n_blocks=16)
+    assert app(k, v) == CAPACITY
+    assert (k.n_blocks, k.n_tail, v.n_blocks, v.n_tail) == (16, 7, 16, 7)
+    k, v = stream(n_tail=7, n_blocks=3), stream(n_tail=7, n_blocks=3, capacity=3)
+    assert app(k, v) == CAPACITY
+
+
+def ws_bytes(lib, k, v, Hq):
+    n = ctypes.c_size_t(0)
+    rc = lib.codec_decode_workspace_bytes(ctypes.byref(k), ctypes.byref(v), Hq, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_plan(lib):
+    k = stream(n_blocks=16, capacity=16)
+    v = stream(n_blocks=16, capacity=16, fmt=bd.FMT_BF16)
+    rc, n = ws_bytes(lib, k, v, 16)
+    assert rc == OK and n > 0
+    assert ws_bytes(lib, k, v, 6)[0] == SHAPE          # 6 % 4 kv heads
+    assert ws_bytes(lib, k, stream(n_blocks=15), 16)[0] == SHAPE
+    assert ws_bytes(lib, stream(), stream(), 16)[0] == SHAPE     # empty sequence
+    assert ws_bytes(lib, stream(n_tail=1), stream(n_tail=1), 16)[0] == OK
+    assert lib.codec_decode_workspace_bytes(ctypes.byref(k), ctypes.byref(v), 16, None) == NULL
+    # the plan grows with the problem and is deterministic
+    big = stream(n_blocks=8192, capacity=8192)
+    assert ws_bytes(lib, big, big, 16) == ws_bytes(lib, big, big, 16)
+    assert ws_bytes(lib, big, big, 16)[1] >= n
+
+
+def test_decode_validation(lib):
+    k = stream(n_blocks=16, capacity=16)
+    v = stream(n_blocks=16, capacity=16)
+    two = bd._I64_2(2048, 128)
+    _, need = ws_bytes(lib, k, v, 16)
+
+    def dec(q=FAKE, Hq=16, scale=0.1, out=FAKE, odt=bd.FMT_F32, ws=FAKE, wsb=need, qs=two, kk=k, vv=v):
+        return lib.codec_decode_attention(q, qs, Hq, ctypes.byref(kk), ctypes.byref(vv), ctypes.c_float(scale),
+                                          out, two, odt, ws, wsb, None)
+
+    assert dec(q=None) == NULL
+    assert dec(out=None) == NULL
+    assert dec(Hq=6) == SHAPE
+    assert dec(Hq=0) == SHAPE
+    assert dec(scale=0.0) == SCALE
+    assert dec(scale=-1.0) == SCALE
+    assert dec(scale=float("nan")) == SCALE
+    assert dec(scale=float("inf")) == SCALE
+    assert dec(odt=bd.FMT_I8) == FORMAT
+    assert dec(ws=None) == WORKSPACE
+    assert dec(ws=FAKE + 16) == WORKSPACE
+    assert dec(wsb=need - 1) == WORKSPACE
+    assert dec(q=FAKE + 2) == SHAPE
+    assert dec(qs=bd._I64_2(2048, 100)) == SHAPE
+    assert dec(vv=stream(n_blocks=16, capacity=16, keep=3)) == SHAPE
+    assert dec(kk=stream(), vv=stream()) == SHAPE

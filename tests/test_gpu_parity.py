@@ -1,0 +1,188 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Encode: codes, scales, float rows and tail bit-exact.  Decode: on the
+identical archive, max over (b, hq) of ||o - o_ref||_inf / ||o_ref||_inf
+<= 2e-3 (fp32 accumulation, bf16 inputs).  Sizes span several tiles and
+splits with ragged ends; edge cases: empty archive (tail only), no tail,
+R = 1, S = R, GQA from 1 to 16, every row format, fp32 raw tokens.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from compressed_domain_attention_amd import binding as bd
+from compressed_domain_attention_amd import synthetic as syn
+from parity_util import TOL, assert_archive_equal, gpu_archive, make_streams, note, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+# ------------------------------------------------------------------ encode --
+ENCODE_CASES = [
+    # D, R, S, fmt, raw, B, H, T
+    (64, 8, 2, "f32", "bf16", 1, 2, 1027),
+    (128, 8, 2, "i8", "bf16", 2, 3, 8 * 37 + 5),
+    (128, 16, 4, "i8", "bf16", 1, 2, 16 * 21 + 15),
+    (128, 8, 3, "bf16", "bf16", 2, 2, 8 * 40),
+    (256, 8, 3, "i8", "bf16", 1, 2, 8 * 9 + 1),
+    (64, 1, 1, "i8", "bf16", 1, 2, 33),
+    (64, 2, 2, "f32", "f32", 2, 1, 65),
+    (128, 32, 16, "i8", "f32", 1, 2, 32 * 3 + 31),
+    (128, 5, 3, "i8", "bf16", 1, 1, 5 * 11 + 2),
+    (64, 8, 8, "f32", "bf16", 1, 1, 8 * 6),
+    (128, 8, 2, "i8", "bf16", 1, 1, 5),        # tail only
+]
+
+
+@pytest.mark.parametrize("D,R,S,fmt,raw,B,H,T", ENCODE_CASES)
+def test_encode_bitexact(D, R, S, fmt, raw, B, H, T):
+    note("encode", D, R, S, fmt, raw, B, H, T)
+    dt = torch.bfloat16 if raw == "bf16" else torch.float32
+    k, _, _ = syn.small_case(B, H, H, D, T, seed=R * 7 + S, dtype=dt, offset_var=2.0)
+    st = bd.CodecStream(B, H, D, R, S, fmt=fmt, raw_dtype=raw, device=DEV)
+    st.encode(k.to(DEV))
+    torch.cuda.synchronize()
+    assert (st.n_blocks, st.n_tail) == (T // R, T % R)
+    assert_archive_equal(gpu_archive(st), O.encode(syn.bf16_to_numpy(k), R, S, fmt))
+
+
+def test_encode_special_values():
+    # zero block (scale 0, codes 0), exact ties in the quantiser, huge and tiny magnitudes
+    note("encode special values")
+    B, H, D, R, S = 1, 1, 64, 4, 4
+    x = np.zeros((B, H, 5 * R, D), dtype=np.float32)
+    x[0, 0, R:2 * R] = 1e30 * np.linspace(-1, 1, R * D, dtype=np.float32).reshape(R, D)
+    x[0, 0, 2 * R:3 * R] = 1e-30 * np.linspace(-1, 1, R * D, dtype=np.float32).reshape(R, D)
+    x[0, 0, 3 * R:4 * R, :] = np.arange(-127, 129, dtype=np.float32)[: R * D].reshape(R, D) / 2
+    x[0, 0, 4 * R:5 * R, 0] = -0.0
+    t = torch.from_numpy(x)
+    for fmt in ("i8", "f32", "bf16"):
+        st = bd.CodecStream(B, H, D, R, S, fmt=fmt, raw_dtype="f32", device=DEV)
+        st.encode(t.to(DEV))
+        torch.cuda.synchronize()
+        assert_archive_equal(gpu_archive(st), O.encode(x.astype(np.float64), R, S, fmt))
+
+
+# ------------------------------------------------------------------ decode --
+DECODE_CASES = [
+    # B, Hq, H, D, R, S, kfmt, vfmt, T, raw
+    (1, 4, 2, 64, 8, 2, "f32", "f32", 1027, "bf16"),
+    (2, 8, 2, 128, 8, 2, "i8", "i8", 8 * 300 + 3, "bf16"),
+    (1, 8, 2, 128, 16, 4, "i8", "i8", 16 * 700 + 5, "bf16"),
+    (2, 16, 2, 128, 8, 3, "i8", "bf16", 8 * 200 + 7, "bf16"),
+    (1, 2, 2, 64, 8, 2, "i8", "i8", 8 * 100, "bf16"),          # G = 1, no tail
+    (1, 6, 2, 128, 8, 2, "bf16", "i8", 8 * 90 + 1, "bf16"),    # G = 3
+    (1, 32, 2, 128, 8, 4, "i8", "f32", 8 * 64 + 2, "bf16"),    # G = 16 -> two query groups
+    (1, 4, 1, 256, 8, 3, "i8", "i8", 8 * 130 + 6, "bf16"),
+    (1, 8, 1, 256, 16, 8, "bf16", "bf16", 16 * 50 + 9, "bf16"),
+    (1, 4, 2, 64, 1, 1, "i8", "f32", 300, "bf16"),             # R = 1
+    (1, 4, 2, 64, 8, 8, "f32", "f32", 8 * 50 + 4, "f32"),      # S = R, fp32 tokens
+    (1, 8, 2, 128, 32, 16, "i8", "i8", 32 * 40 + 31, "bf16"),
+    (1, 4, 2, 128, 8, 2, "i8", "i8", 7, "bf16"),               # tail only
+    (1, 4, 2, 128, 8, 2, "i8", "i8", 1, "bf16"),               # one token
+    (3, 24, 3, 64, 4, 1, "i8", "i8", 4 * 333 + 2, "bf16"),     # S = 1
+]
+
+
+@pytest.mark.parametrize("B,Hq,H,D,R,S,kfmt,vfmt,T,raw", DECODE_CASES)
+def test_decode_parity(B, Hq, H, D, R, S, kfmt, vfmt, T, raw):
+    note("decode", B, Hq, H, D, R, S, kfmt, vfmt, T, raw)
+    dt = torch.bfloat16 if raw == "bf16" else torch.float32
+    k, v, q = syn.small_case(B, Hq, H, D, T, seed=B * 13 + Hq + R, dtype=dt, offset_var=1.0)
+    ks, vs = make_streams(k, v, R, S, kfmt, vfmt)
+    out = bd.decode_attention(q.to(DEV), ks, vs)
+    torch.cuda.synchronize()
+    ka, va = gpu_archive(ks), gpu_archive(vs)
+    assert_archive_equal(ka, O.encode(syn.bf16_to_numpy(k), R, S, kfmt))
+    ref = O.decode_attention(syn.bf16_to_numpy(q), ka, va)
+    err = rel_err(out.cpu().numpy()[:, :, 0], ref)
+    assert err <= TOL, err
+
+
+def test_decode_bf16_out_and_strided_views():
+    note("decode bf16 out / strided q and out")
+    B, Hq, H, D, R, S, T = 2, 8, 2, 128, 8, 2, 8 * 77 + 3
+    k, v, q = syn.small_case(B, Hq, H, D, T, seed=3)
+    ks, vs = make_streams(k, v, R, S, "i8", "i8")
+    # q as a strided view: heads interleaved with padding
+    qbig = torch.zeros((B, Hq, 2, D), dtype=torch.bfloat16, device=DEV)
+    qbig[:, :, 1:2] = q.to(DEV)
+    qv = qbig[:, :, 1:2]
+    obig = torch.full((B, Hq, 3, D), float("nan"), dtype=torch.float32, device=DEV)
+    ov = obig[:, :, 2:3]
+    bd.decode_attention(qv, ks, vs, out=ov)
+    ob = bd.decode_attention(q.to(DEV), ks, vs, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = O.decode_attention(syn.bf16_to_numpy(q), gpu_archive(ks), gpu_archive(vs))
+    assert rel_err(ov.cpu().numpy()[:, :, 0], ref) <= TOL
+    assert torch.isnan(obig[:, :, :2]).all()           # nothing outside the view was written
+    assert rel_err(ob.float().cpu().numpy()[:, :, 0], ref) <= 2 ** -8 + TOL
+
+
+def test_decode_scale_argument():
+    note("decode scale")
+    B, Hq, H, D, R, S, T = 1, 4, 2, 64, 8, 2, 8 * 60 + 1
+    k, v, q = syn.small_case(B, Hq, H, D, T, seed=5)
+    ks, vs = make_streams(k, v, R, S, "i8", "i8")
+    for scale in (0.01, 0.125, 1.0, 3.0):
+        out = bd.decode_attention(q.to(DEV), ks, vs, scale=scale)
+        torch.cuda.synchronize()
+        ref = O.decode_attention(syn.bf16_to_numpy(q), gpu_archive(ks), gpu_archive(vs), scale)
+        assert rel_err(out.cpu().numpy()[:, :, 0], ref) <= TOL, scale
+
+
+def test_decode_repeatable_and_workspace_reuse():
+    # the workspace counters reset themselves: back-to-back calls, same bits
+    note("decode repeat")
+    B, Hq, H, D, R, S, T = 2, 8, 2, 128, 16, 4, 16 * 400 + 9
+    k, v, q = syn.small_case(B, Hq, H, D, T, seed=6)
+    ks, vs = make_streams(k, v, R, S, "i8", "i8")
+    qd = q.to(DEV)
+    outs = [bd.decode_attention(qd, ks, vs).clone() for _ in range(5)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+# ------------------------------------------------------------------ append --
+@pytest.mark.parametrize("R,S,kfmt,vfmt,T0,steps", [
+    (8, 3, "i8", "bf16", 8 * 10 + 5, 30),
+    (16, 4, "i8", "i8", 16 * 3, 40),
+    (4, 4, "f32", "f32", 0, 13),
+    (1, 1, "i8", "i8", 3, 5),
+])
+def test_append_matches_encode_and_never_rewrites(R, S, kfmt, vfmt, T0, steps):
+    note("append", R, S, kfmt, vfmt, T0, steps)
+    B, Hq, H, D = 2, 8, 2, 128
+    k, v, _ = syn.small_case(B, Hq, H, D, T0 + steps, seed=R + S)
+    ks = bd.CodecStream(B, H, D, R, S, fmt=kfmt, device=DEV)
+    vs = bd.CodecStream(B, H, D, R, S, fmt=vfmt, device=DEV)
+    kd, vd = k.to(DEV), v.to(DEV)
+    ks.encode(kd[:, :, :T0])
+    vs.encode(vd[:, :, :T0])
+    frozen = []
+    for t in range(T0, T0 + steps):
+        bd.append_step(ks, vs, kd[:, :, t:t + 1], vd[:, :, t:t + 1])
+        assert ks.seq_len == t + 1 and vs.seq_len == t + 1
+        n = ks.n_blocks
+        if n > len(frozen):
+            frozen.append((ks.rows[:, :, len(frozen)].clone(), None if ks.scales is None else ks.scales[:, :, len(frozen)].clone()))
+        for i, (r, s) in enumerate(frozen):
+            assert torch.equal(ks.rows[:, :, i], r)
+            if s is not None:
+                assert torch.equal(ks.scales[:, :, i], s)
+        if t % 7 == 3 or t == T0 + steps - 1:
+            q = syn.gaussian((B, Hq, 1, D), 1000 + t)
+            out = bd.decode_attention(q.to(DEV), ks, vs)
+            torch.cuda.synchronize()
+            ref = O.decode_attention(syn.bf16_to_numpy(q), gpu_archive(ks), gpu_archive(vs))
+            assert rel_err(out.cpu().numpy()[:, :, 0], ref) <= TOL
+    # the streamed archive equals one encode of the whole sequence
+    k2, v2 = make_streams(k, v, R, S, kfmt, vfmt)
+    torch.cuda.synchronize()
+    assert_archive_equal(gpu_archive(ks), gpu_archive(k2))
+    assert_archive_equal(gpu_archive(vs), gpu_archive(v2))
+    assert_archive_equal(gpu_archive(ks), O.encode(syn.bf16_to_numpy(k), R, S, kfmt))
