@@ -1,0 +1,223 @@
+"""Benchmark: compressed-domain decode attention on one MI355X.
+
+Default workload: the 128K-context layer (B=1, Hq=32, Hkv=8, D=128,
+T=131072+5, R=16, S=4, int8 K and V rows).  A step is one decode step of a
+stack of LAYERS such layers, each with its own archive at its own address
+(8 x 69 MB exceeds the 256 MB MALL, so HBM is what is measured): per layer,
+append the new token's K/V (codec_append_step, which archives a block every
+R steps) and attend (codec_decode_attention).  Each step is captured once
+as a HIP graph and the graphs are replayed in order.
+
+Prints one JSON line.  value = compressed-KV GB/s: algorithmic decode bytes
+of all layers and timed steps / wall time of the timed steps.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import compressed_domain_attention_amd as cda  # noqa: E402
+from compressed_domain_attention_amd import synthetic as syn  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+EB = {"f32": 4, "bf16": 2, "i8": 1}
+
+
+def decode_bytes(w, n_blocks, n_tail):
+    """Algorithmic bytes of one decode call: rows + scales of both archives,
+    the raw tail, q (bf16) and out (fp32)."""
+    per_bh = n_blocks * w.S * (w.D * EB[w.kfmt] + (4 if w.kfmt == "i8" else 0)) \
+        + n_blocks * w.S * (w.D * EB[w.vfmt] + (4 if w.vfmt == "i8" else 0)) \
+        + 2 * n_tail * w.D * EB[w.raw_dtype]
+    return w.B * w.Hkv * per_bh + w.B * w.Hq * w.D * (2 + 4)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("decode_impl.h", "internal.h"):
+        h.update(open(os.path.join(ROOT, "compressed_domain_attention_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM traffic per decode launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, k, v, q, budget_s=15.0):
+    """The fp64 oracle on the host cores, on a bounded sample: whole-sequence
+    decode attention for as many kv heads (with their G query heads) as fit
+    in the time budget.  Returns the JSON object."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    R, S = w.R, w.S
+    n = w.T // R
+    done, bytes_done, t_used = 0, 0, 0.0
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    qn = syn.bf16_to_numpy(q)[:, :, 0]
+    scale = w.D ** -0.5
+    for (b, h) in heads:
+        t0 = time.perf_counter()
+        kx = syn.bf16_to_numpy(k[b:b + 1, h:h + 1, :w.T])
+        vx = syn.bf16_to_numpy(v[b:b + 1, h:h + 1, :w.T])
+        ka, va = O.encode(kx, R, S, w.kfmt), O.encode(vx, R, S, w.vfmt)
+        t1 = time.perf_counter()
+        qs = qn[b:b + 1, h * w.G:(h + 1) * w.G]
+        O.decode_attention(qs, ka, va, scale)
+        t_used += time.perf_counter() - t1
+        done += 1
+        bytes_done += n * S * (w.D * EB[w.kfmt] + (4 if w.kfmt == "i8" else 0) + w.D * EB[w.vfmt]
+                               + (4 if w.vfmt == "i8" else 0)) + 2 * (w.T % R) * w.D * 2 + w.G * w.D * 6
+        if t_used + (t1 - t0) >= budget_s:
+            break
+    return {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"decode attention of {done} of {len(heads)} kv heads (each with its {w.G} query heads) "
+                      f"over the full {w.T}-token archive, fp64 numpy; {t_used:.1f}s of oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="long128k", choices=sorted(syn.WORKLOADS))
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    w = syn.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, K, W = args.layers, args.steps, args.warmup
+    extra = K + W
+    print(f"# generating {w.name}: B={w.B} Hkv={w.Hkv} T={w.T}+{extra} D={w.D}", file=sys.stderr, flush=True)
+    k, v = syn.workload_kv(w, T=w.T + extra)
+    kd, vd = k.to(dev), v.to(dev)
+    queries = [syn.workload_query(w, s).to(dev) for s in range(extra)]
+    cap = (w.T + extra) // w.R + 1
+
+    # ---- prefill: encode every layer's archive (timed; a2/a3)
+    streams = []
+    enc_ms = []
+    for _ in range(L):
+        ks = cda.CodecStream(w.B, w.Hkv, w.D, w.R, w.S, fmt=w.kfmt, device=dev, capacity=cap)
+        vs = cda.CodecStream(w.B, w.Hkv, w.D, w.R, w.S, fmt=w.vfmt, device=dev, capacity=cap)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        ks.encode(kd[:, :, :w.T])
+        vs.encode(vd[:, :, :w.T])
+        e1.record()
+        torch.cuda.synchronize()
+        enc_ms.append(e0.elapsed_time(e1))
+        streams.append((ks, vs))
+    n0, t0 = streams[0][0].n_blocks, streams[0][0].n_tail
+    enc_bytes = 2 * w.B * w.Hkv * (w.T * w.D * 2) + sum(
+        w.B * w.Hkv * n0 * w.S * (w.D * EB[f] + (4 if f == "i8" else 0)) for f in (w.kfmt, w.vfmt)) \
+        + 2 * w.B * w.Hkv * t0 * w.D * 2
+
+    outs = [torch.empty((w.B, w.Hq, 1, w.D), dtype=torch.float32, device=dev) for _ in range(L)]
+    ws = torch.zeros(max(cda.decode_workspace_bytes(ks, vs, w.Hq) for ks, vs in streams) * 2 + 4096,
+                     dtype=torch.uint8, device=dev)
+
+    # ---- capture one graph per step (append + decode for every layer)
+    print(f"# capturing {extra} step graphs x {L} layers", file=sys.stderr, flush=True)
+    graphs, step_bytes, step_qtok = [], [], []
+    cap_stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for s in range(extra):
+        g = torch.cuda.CUDAGraph()
+        nb = ntl = 0
+        with torch.cuda.graph(g, stream=cap_stream):
+            for li, (ks, vs) in enumerate(streams):
+                cda.append_step(ks, vs, kd[:, :, w.T + s:w.T + s + 1], vd[:, :, w.T + s:w.T + s + 1])
+                cda.decode_attention(queries[s], ks, vs, out=outs[li], workspace=ws)
+                nb, ntl = ks.n_blocks, ks.n_tail
+        graphs.append(g)
+        step_bytes.append(L * decode_bytes(w, nb, ntl))
+        step_qtok.append(L * w.B * w.Hq * (nb * w.R + ntl))
+
+    for s in range(W):
+        graphs[s].replay()
+    torch.cuda.synchronize()
+    t_a, t_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_a.record()
+    for s in range(W, W + K):
+        graphs[s].replay()
+    t_b.record()
+    torch.cuda.synchronize()
+    elapsed_ms = t_a.elapsed_time(t_b)
+    total_bytes = sum(step_bytes[W:])
+    gbs = total_bytes / (elapsed_ms * 1e-3) / 1e9
+    qtok = sum(step_qtok[W:]) / (elapsed_ms * 1e-3)
+
+    # ---- dominant kernel: per-launch decode duration on the launch stream
+    print("# timing decode launches", file=sys.stderr, flush=True)
+    reps = 20
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps * L)]
+    qd = queries[-1]
+    torch.cuda.synchronize()
+    for r in range(reps):
+        for li, (ks, vs) in enumerate(streams):
+            a, b = evs[r * L + li]
+            a.record()
+            cda.decode_attention(qd, ks, vs, out=outs[li], workspace=ws)
+            b.record()
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) * 1e-3 for a, b in evs]
+    avg_s = float(np.mean(durs[L:]))            # first round excluded (first touches)
+    per_launch = decode_bytes(w, streams[0][0].n_blocks, streams[0][0].n_tail)
+    achieved = per_launch / avg_s / 1e9
+    traffic = load_traffic(w.name)
+
+    res = {
+        "metric": "decode-attn compressed-KV GB/s + query-heads*tokens/s at 1 GPU; % of HBM peak",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(elapsed_ms / K, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8 rows, fp32 accumulate", "data": "synthetic AR(1) KV, N(0,1) q",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "T0": w.T,
+                   "R": w.R, "S": w.S, "k_rows": w.kfmt, "v_rows": w.vfmt, "layers_rotated": L,
+                   "step": "per layer: codec_append_step + codec_decode_attention, HIP graph per step"},
+        "query_head_tokens_per_s": round(qtok, 1),
+        "hbm_peak_fraction": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_kernel", "avg_launch_us": round(avg_s * 1e6, 3),
+                     "algorithmic_bytes_per_launch": per_launch},
+        "encode": {"avg_ms": round(float(np.mean(enc_ms[1:] or enc_ms)), 4),
+                   "bytes": enc_bytes,
+                   "GBps": round(enc_bytes / (float(np.mean(enc_ms[1:] or enc_ms)) * 1e-3) / 1e9, 2)},
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the oracle on the host cores", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, k, v, queries[0].cpu())
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

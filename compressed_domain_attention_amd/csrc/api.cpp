@@ -103,7 +103,7 @@ Plan make_plan(const codec_stream *k, int64_t Hq) {
     int64_t ns_max = (tiles + min_tiles - 1) / min_tiles;
     if (ns > ns_max) ns = ns_max;
     if (ns < 1) ns = 1;
-    if (ns > 1024) ns = 1024;
+    if (ns > 256) ns = 256;
     int64_t chunk_tiles = (tiles + ns - 1) / ns;
     p.chunk = chunk_tiles * NB;
     p.ns = (int)((n + p.chunk - 1) / p.chunk);

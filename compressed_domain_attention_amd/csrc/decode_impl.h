@@ -299,7 +299,7 @@ __device__ __forceinline__ void vphase(const void *base, int nrows, int lane, co
 // token (R = S = 1, A = [1]).  Updates the running max, rescale factors and
 // the lane's partial sum; overwrites sw with the value weights w * vscale.
 template <int GS, int SP, bool TAIL>
-__device__ __forceinline__ void logits(const DecodeArgs &a, float *sw, int nb, const float *__restrict__ vscale,
+__device__ __forceinline__ void logits(const DecodeArgs &a, const float *sA, float *sw, int nb, const float *__restrict__ vscale,
                                        int lane, float (&m_u)[GS], float &m_own, float &l_own,
                                        float (&alpha)[GS]) {
   const int S = TAIL ? 1 : a.S;
@@ -316,7 +316,7 @@ __device__ __forceinline__ void logits(const DecodeArgs &a, float *sw, int nb, c
       mx = fmaxf(mx, sv[0]);
     } else {
       for (int r = 0; r < R; ++r) {
-        const float *Ar = a.A + r * SP;
+        const float *Ar = sA + r * SP;
         float z = 0.0f;
 #pragma unroll
         for (int j = 0; j < SP; ++j) z = fmaf(Ar[j], sv[j], z);
@@ -349,7 +349,7 @@ __device__ __forceinline__ void logits(const DecodeArgs &a, float *sw, int nb, c
 #pragma unroll
       for (int j = 0; j < SP; ++j) w[j] = 0.0f;
       for (int r = 0; r < R; ++r) {
-        const float *Ar = a.A + r * SP;
+        const float *Ar = sA + r * SP;
         float z = 0.0f;
 #pragma unroll
         for (int j = 0; j < SP; ++j) z = fmaf(Ar[j], sv[j], z);
@@ -373,8 +373,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   // per-wave s / w scratch during tiles, then the workgroup merge area
   constexpr int SW_FLOATS = C::TR * GS;
   constexpr int MERGE_FLOATS = W * GS * D + W * GS * 2;
-  constexpr int LDS_FLOATS = (W * SW_FLOATS > MERGE_FLOATS) ? W * SW_FLOATS : MERGE_FLOATS;
+  constexpr int COMB_FLOATS = 2 * 256 * GS + GS;   // ns <= 256
+  constexpr int LDS_A = (W * SW_FLOATS > MERGE_FLOATS) ? W * SW_FLOATS : MERGE_FLOATS;
+  constexpr int LDS_FLOATS = LDS_A > COMB_FLOATS ? LDS_A : COMB_FLOATS;
   __shared__ float lds[LDS_FLOATS];
+  __shared__ float sA[kMaxR * SP];   // synthesis basis, copied once from the arguments
   __shared__ int last_flag;
 
   const int tid = threadIdx.x;
@@ -387,6 +390,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   const int64_t b = bh / a.H;
   const int h = (int)(bh % a.H);
   const int hq0 = h * a.G + qg * GS;
+  // kernel arguments may live in host-coherent memory: read A once, here
+  for (int i = tid; i < a.R * SP; i += 64 * W) sA[i] = a.A[i];
+  __syncthreads();
 
   // ---- query: fp16 pairs of the lane's 16 K elements, pre-scaled per head
   h2 qh[GS][8];
@@ -455,7 +461,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     else if (a.kf == BF16) kphase<D, GS, BF16>(kb, nullptr, nrows, lane, qh, cq, sw);
     else kphase<D, GS, F32>(kb, nullptr, nrows, lane, qh, cq, sw);
     wave_lds_sync();
-    logits<GS, SP, false>(a, sw, nb, vsc, lane, m_u, m_own, l_own, alpha);
+    logits<GS, SP, false>(a, sA, sw, nb, vsc, lane, m_u, m_own, l_own, alpha);
 #pragma unroll
     for (int g = 0; g < GS; ++g)
 #pragma unroll
@@ -476,7 +482,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     if (a.kraw == BF16) kphase<D, GS, BF16>(kt, nullptr, nt, lane, qh, cq, sw);
     else kphase<D, GS, F32>(kt, nullptr, nt, lane, qh, cq, sw);
     wave_lds_sync();
-    logits<GS, SP, true>(a, sw, nt, nullptr, lane, m_u, m_own, l_own, alpha);
+    logits<GS, SP, true>(a, sA, sw, nt, nullptr, lane, m_u, m_own, l_own, alpha);
 #pragma unroll
     for (int g = 0; g < GS; ++g)
 #pragma unroll
@@ -544,35 +550,58 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     }
   }
 
-  // ---- split arrival; the last workgroup of (b, h, group) combines
-  __threadfence();
+  // ---- split arrival; the last workgroup of (b, h, group) combines.
+  // Writers only release (L2 write-back); the one combining workgroup
+  // acquires (L2 invalidate).  A full fence in every workgroup would
+  // invalidate the XCD's L2 once per workgroup.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (tid == 0) {
-    const uint32_t old = atomicAdd(a.counters + pairq, 1u);
+    const uint32_t old = __hip_atomic_fetch_add(a.counters + pairq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (old == (uint32_t)(a.ns - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (!last_flag) return;
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
+  // (max, sum) of every split into LDS, one load per thread; then the
+  // per-split weights; then every (head, d) output sums its split partials
+  // with independent loads.  Partials of other workgroups are visible after
+  // the acquire fence above.
   const float *Pacc = a.part_acc + pairq * a.ns * GS * D;
   const float *Pml = a.part_ml + pairq * a.ns * GS * 2;
+  float *cml = lds;                     // [ns*GS][2]; later f = weight per split
+  float *cM = lds + 2 * a.ns * GS;      // [GS] max, [GS] 1/sum
+  for (int i = tid; i < a.ns * GS; i += 64 * W) {
+    cml[2 * i] = Pml[2 * i];
+    cml[2 * i + 1] = Pml[2 * i + 1];
+  }
+  __syncthreads();
+  if (tid < GS) {
+    float m = -INFINITY;
+    for (int sp = 0; sp < a.ns; ++sp) m = fmaxf(m, cml[2 * (sp * GS + tid)]);
+    float l = 0.0f;
+    for (int sp = 0; sp < a.ns; ++sp) {
+      const float li = cml[2 * (sp * GS + tid) + 1];
+      const float f = li > 0.0f ? __builtin_amdgcn_exp2f(cml[2 * (sp * GS + tid)] - m) : 0.0f;
+      l += li * f;
+      cml[2 * (sp * GS + tid)] = f;
+    }
+    cM[tid] = 1.0f / l;
+  }
+  __syncthreads();
   for (int idx = tid; idx < GS * D; idx += 64 * W) {
     const int g = idx / D, d = idx % D;
-    float m = -INFINITY;
-    for (int sp = 0; sp < a.ns; ++sp)
-      m = fmaxf(m, __hip_atomic_load(Pml + (sp * GS + g) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    float l = 0.0f, s = 0.0f;
-    for (int sp = 0; sp < a.ns; ++sp) {
-      const float li = __hip_atomic_load(Pml + (sp * GS + g) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (li > 0.0f) {
-        const float mi = __hip_atomic_load(Pml + (sp * GS + g) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float f = __builtin_amdgcn_exp2f(mi - m);
-        l += li * f;
-        s += __hip_atomic_load(Pacc + (sp * GS + g) * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * f;
-      }
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    int sp = 0;
+    for (; sp + 4 <= a.ns; sp += 4) {
+      s0 = fmaf(cml[2 * ((sp + 0) * GS + g)], Pacc[((sp + 0) * GS + g) * D + d], s0);
+      s1 = fmaf(cml[2 * ((sp + 1) * GS + g)], Pacc[((sp + 1) * GS + g) * D + d], s1);
+      s2 = fmaf(cml[2 * ((sp + 2) * GS + g)], Pacc[((sp + 2) * GS + g) * D + d], s2);
+      s3 = fmaf(cml[2 * ((sp + 3) * GS + g)], Pacc[((sp + 3) * GS + g) * D + d], s3);
     }
-    const float o = s / l;
+    for (; sp < a.ns; ++sp) s0 = fmaf(cml[2 * (sp * GS + g)], Pacc[(sp * GS + g) * D + d], s0);
+    const float o = ((s0 + s1) + (s2 + s3)) * cM[g];
     const int64_t off = b * a.o_sb + (int64_t)(hq0 + g) * a.o_sh + d;
     if (a.out_f32) {
       static_cast<float *>(a.out)[off] = o;

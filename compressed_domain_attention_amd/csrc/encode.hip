@@ -151,13 +151,17 @@ __device__ void encode_block(const EncodeArgs &a, const float *__restrict__ M, i
 template <int EPL, int SP>
 __global__ __launch_bounds__(64 * kEncodeWaves) void encode_kernel(EncodeLaunch L, int64_t per_bh) {
   const EncodeArgs &a = L.e;
+  // kernel arguments may live in host-coherent memory: read the basis once
+  __shared__ float sM[kMaxS * kMaxR];
+  for (int i = threadIdx.x; i < a.S * a.R; i += 64 * kEncodeWaves) sM[i] = L.M[i];
+  __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t bh = blockIdx.x / per_bh;
   const int64_t n = (blockIdx.x % per_bh) * kEncodeWaves + wave;
   const int64_t b = bh / a.H, h = bh % a.H;
   if (n < a.n_new) {
-    encode_block<EPL, SP>(a, L.M, b, h, n, lane);
+    encode_block<EPL, SP>(a, sM, b, h, n, lane);
   } else if (n == a.n_new && a.n_copy > 0) {
     // raw remainder -> tail slots 0 .. n_copy-1, verbatim
     const int d0 = lane * EPL;
@@ -179,7 +183,10 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs A) {
   if (A.complete) {
     // tail slots 0..R-2 plus the new token form the block; slot R-1 of the
     // tail is not written since the tail empties.
-    encode_block<EPL, SP>(a, A.M, b, h, 0, lane);
+    __shared__ float sM[kMaxS * kMaxR];
+    for (int i = lane; i < a.S * a.R; i += 64) sM[i] = A.M[i];
+    __syncthreads();
+    encode_block<EPL, SP>(a, sM, b, h, 0, lane);
   } else {
     const int d0 = lane * EPL;
     float x[EPL];
