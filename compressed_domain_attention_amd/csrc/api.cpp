@@ -74,6 +74,7 @@ EncodeArgs stream_encode_args(const codec_stream *s) {
 // Split plan of the decode: splits per (b, kv head, query group), blocks per
 // split, workgroups.  A pure function of the shapes.
 struct Plan {
+  bool ok;
   int GS, NQG, SP, ns;
   int64_t pairs, chunk, n_wg;
   size_t off_ml, off_acc, bytes;
@@ -81,10 +82,10 @@ struct Plan {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workgroups that fill MI355X once: 256 CUs x 2 resident 8-wave workgroups.
-constexpr int64_t kTargetWorkgroups = 512;
+// Workgroups that fill MI355X once: 256 CUs x 1 resident 8-wave workgroup.
+constexpr int64_t kTargetWorkgroups = 256;
 
-Plan make_plan(const codec_stream *k, int64_t Hq) {
+Plan make_plan(const codec_stream *k, const codec_stream *v, int64_t Hq) {
   Plan p;
   const int64_t G = Hq / k->heads;
   p.GS = decode_group_size((int)G);
@@ -92,19 +93,20 @@ Plan make_plan(const codec_stream *k, int64_t Hq) {
   p.SP = decode_pad_keep(k->keep);
   p.pairs = k->batch * k->heads * p.NQG;
   const int64_t n = k->n_blocks;
-  const int64_t NB = decode_tile_rows(k->head_dim) / k->keep;   // blocks per tile
-  if (n == 0) {
+  const int64_t NB = decode_tile_rows(k->head_dim, k->fmt, v->fmt) / k->keep;   // blocks per tile
+  p.ok = NB >= 1;
+  if (n == 0 || !p.ok) {
     p.ns = 1;
     p.chunk = 0;
   } else {
+    // one 8-wave workgroup per CU; every wave of a split gets a tile or more
     const int64_t tiles = (n + NB - 1) / NB;
-    const int64_t min_tiles = kDecodeWaves / 2;                   // tiles per split, at least
     int64_t ns = (kTargetWorkgroups + p.pairs - 1) / p.pairs;
-    int64_t ns_max = (tiles + min_tiles - 1) / min_tiles;
+    const int64_t ns_max = (tiles + kDecodeWaves - 1) / kDecodeWaves;
     if (ns > ns_max) ns = ns_max;
     if (ns < 1) ns = 1;
-    if (ns > 256) ns = 256;
-    int64_t chunk_tiles = (tiles + ns - 1) / ns;
+    if (ns > kMaxSplits) ns = kMaxSplits;
+    const int64_t chunk_tiles = (tiles + ns - 1) / ns;
     p.chunk = chunk_tiles * NB;
     p.ns = (int)((n + p.chunk - 1) / p.chunk);
   }
@@ -143,11 +145,17 @@ int decode_pad_keep(int S) {
   while (sp < S) sp *= 2;
   return sp;
 }
-int launch_decode(int D, int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
-  switch (D) {
-    case 64: return launch_decode_d64(GS, SP, a, n_wg, stream);
-    case 128: return launch_decode_d128(GS, SP, a, n_wg, stream);
-    case 256: return launch_decode_d256(GS, SP, a, n_wg, stream);
+int launch_decode(int D, int GS, int SP, int kf, int vf, const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
+  switch (kf * 3 + vf) {
+    case I8 * 3 + I8: return launch_decode_i8_i8(D, GS, SP, a, n_wg, stream);
+    case I8 * 3 + BF16: return launch_decode_i8_bf16(D, GS, SP, a, n_wg, stream);
+    case I8 * 3 + F32: return launch_decode_i8_f32(D, GS, SP, a, n_wg, stream);
+    case BF16 * 3 + I8: return launch_decode_bf16_i8(D, GS, SP, a, n_wg, stream);
+    case BF16 * 3 + BF16: return launch_decode_bf16_bf16(D, GS, SP, a, n_wg, stream);
+    case BF16 * 3 + F32: return launch_decode_bf16_f32(D, GS, SP, a, n_wg, stream);
+    case F32 * 3 + I8: return launch_decode_f32_i8(D, GS, SP, a, n_wg, stream);
+    case F32 * 3 + BF16: return launch_decode_f32_bf16(D, GS, SP, a, n_wg, stream);
+    case F32 * 3 + F32: return launch_decode_f32_f32(D, GS, SP, a, n_wg, stream);
     default: return -1;
   }
 }
@@ -269,7 +277,9 @@ int codec_decode_workspace_bytes(const codec_stream *k, const codec_stream *v, i
   if (!bytes) return CODEC_ERR_NULL;
   const int rc = check_decode(k, v, Hq);
   if (rc) return rc;
-  *bytes = make_plan(k, Hq).bytes;
+  const Plan p = make_plan(k, v, Hq);
+  if (!p.ok) return CODEC_ERR_UNSUPPORTED;
+  *bytes = p.bytes;
   return CODEC_OK;
 }
 
@@ -284,7 +294,8 @@ int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
   if (!aligned16(q) || q_stride[0] < 0 || q_stride[1] < 0 || q_stride[0] % 8 || q_stride[1] % 8)
     return CODEC_ERR_SHAPE;
   if (out_stride[0] < 0 || out_stride[1] < 0) return CODEC_ERR_SHAPE;
-  const Plan p = make_plan(k, Hq);
+  const Plan p = make_plan(k, v, Hq);
+  if (!p.ok) return CODEC_ERR_UNSUPPORTED;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < p.bytes)
     return CODEC_ERR_WORKSPACE;
 
@@ -326,7 +337,7 @@ int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
   for (int r = 0; r < k->block; ++r)
     for (int j = 0; j < p.SP; ++j) a.A[r * p.SP + j] = j < k->keep ? (float)basis_entry(k->block, j, r) : 0.0f;
   (void)hipGetLastError();
-  const int lr = launch_decode(k->head_dim, p.GS, p.SP, a, p.n_wg, stream);
+  const int lr = launch_decode(k->head_dim, p.GS, p.SP, k->fmt, v->fmt, a, p.n_wg, stream);
   if (lr < 0) return CODEC_ERR_UNSUPPORTED;
   if (lr > 0) return CODEC_ERR_HIP;
   return CODEC_OK;

@@ -7,25 +7,31 @@
 // softmax, w = p A, acc += w . rows; split over chunks of blocks, each split
 // writes (max, sum, acc) and a combine merges them (flash-decoding).
 //
-// MI355X design (one workgroup = one (b, kv head, query group, split)):
-//  * all GS query heads of a group run in one workgroup, so every
-//    coefficient byte is read from HBM once and dequantised once;
-//  * 8 waves per workgroup; each wave walks tiles of TR coefficient rows
-//    (8 KB of int8 at any head_dim) with 16-byte loads per lane;
+// MI355X design.  One workgroup = one (b, kv head, query group, split) with
+// all GS query heads of the group, so each coefficient byte is read from HBM
+// once and converted once.  8 waves per workgroup, one workgroup per CU.
+//  * Tiles of TR coefficient rows (about 8 KB of K+V) stream through
+//    registers with 16-byte buffer loads per lane; each wave keeps the next
+//    tile's loads in flight while it computes the current one (two register
+//    buffers).  Buffer loads past a tile's end return zeros, so edges need
+//    no branches.
 //  * K phase: lane = 16 consecutive head_dim elements of one row; int8 codes
 //    become exact fp16 (byte permute + one packed fp16 subtract) and are
 //    dotted with the query in fp16 pairs accumulating in fp32
 //    (v_dot2c_f32_f16); the row sum is a DPP butterfly inside 16-lane rows.
 //    The query is pre-scaled by a power of two into fp16 range (exact for
-//    every bf16 value within 2^28 of the largest |q|);
-//  * logit phase: lane = (block, head); A comes from kernel arguments
-//    (scalar loads), logits and weights stay in registers, softmax in base 2
-//    with log2(e) folded into the scale, one rescale of acc per tile;
-//  * V phase: lane = EV consecutive head_dim elements of one row, fp32 FMAs
-//    into per-lane accumulators; rows are reduced across lanes once per wave;
-//  * waves merge in LDS, the workgroup writes one partial, and the last
-//    workgroup to arrive on the (b, kv head, group) counter combines all
-//    splits and writes the output (no second launch).
+//    every bf16 value within 2^28 of the largest |q|).
+//  * Logit phase: lane = (block, head, 8 of the R tokens); the R x S basis A
+//    sits in LDS; logits stay in registers; base-2 softmax with log2(e)
+//    folded into the scale; one rescale of the accumulators per tile.
+//  * V phase: lane = EV consecutive head_dim elements of one row; the value
+//    weight w * vscale multiplies int8 codes converted by SDWA; fp32 FMAs
+//    into per-lane accumulators, reduced across lanes once per wave.
+//  * Waves merge in LDS; the workgroup publishes its partial with
+//    device-scope stores, waits for them, and bumps a per-(b, h, group)
+//    counter; the last workgroup to arrive combines all splits with
+//    device-scope loads and writes the output (no second launch, and no L2
+//    write-back or invalidate per workgroup).
 #pragma once
 
 #include <math.h>
@@ -44,26 +50,16 @@ __device__ __forceinline__ float dpp(float v) {
 
 __device__ __forceinline__ float xshfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
-// Sum over aligned groups of L consecutive lanes; every lane gets its group's sum.
-template <int L>
-__device__ __forceinline__ float group_sum(float v) {
-  if constexpr (L >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
-  if constexpr (L >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
-  if constexpr (L >= 8) v += dpp<0x141>(v);   // row_half_mirror
-  if constexpr (L >= 16) v += dpp<0x140>(v);  // row_mirror
-  if constexpr (L >= 32) v += xshfl(v, 16);
-  if constexpr (L >= 64) v += xshfl(v, 32);
-  return v;
-}
-
-template <int L>
-__device__ __forceinline__ float group_max(float v) {
-  if constexpr (L >= 2) v = fmaxf(v, dpp<0xB1>(v));
-  if constexpr (L >= 4) v = fmaxf(v, dpp<0x4E>(v));
-  if constexpr (L >= 8) v = fmaxf(v, dpp<0x141>(v));
-  if constexpr (L >= 16) v = fmaxf(v, dpp<0x140>(v));
-  if constexpr (L >= 32) v = fmaxf(v, xshfl(v, 16));
-  if constexpr (L >= 64) v = fmaxf(v, xshfl(v, 32));
+// Sum / max over aligned groups of L consecutive lanes (every lane gets it).
+template <int L, bool MAX>
+__device__ __forceinline__ float group_red(float v) {
+  auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+  if constexpr (L >= 2) v = op(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
+  if constexpr (L >= 4) v = op(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+  if constexpr (L >= 8) v = op(v, dpp<0x141>(v));   // row_half_mirror
+  if constexpr (L >= 16) v = op(v, dpp<0x140>(v));  // row_mirror
+  if constexpr (L >= 32) v = op(v, xshfl(v, 16));
+  if constexpr (L >= 64) v = op(v, xshfl(v, 32));
   return v;
 }
 
@@ -78,6 +74,15 @@ __device__ __forceinline__ float strided(float v) {
   if constexpr (L <= 16) v = op(v, xshfl(v, 16));
   if constexpr (L <= 32) v = op(v, xshfl(v, 32));
   return v;
+}
+
+// Reduce over the LR adjacent lanes of an item (LR in {1, 2, 4}), then over
+// the items of the same head (lanes congruent modulo GS * LR).
+template <int GS, bool MAX>
+__device__ __forceinline__ float head_reduce(float v, int LR) {
+  if (LR == 1) return strided<GS, MAX>(v);
+  if (LR == 2) return strided<(GS * 2 < 64 ? GS * 2 : 64), MAX>(group_red<2, MAX>(v));
+  return strided<(GS * 4 < 64 ? GS * 4 : 64), MAX>(group_red<4, MAX>(v));
 }
 
 __device__ __forceinline__ float readlane(float v, int l) {
@@ -106,9 +111,8 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Make the compiler treat the query registers as redefined here, so that
-// conversions of them are not hoisted out of the tile loop (they would each
-// hold a register for the whole loop).
+// Keep the compiler from hoisting conversions of the query registers out of
+// a loop (each would hold a register for the whole loop).
 template <int GS>
 __device__ __forceinline__ void opaque(h2 (&qh)[GS][8]) {
 #pragma unroll
@@ -121,21 +125,6 @@ __device__ __forceinline__ void opaque(h2 (&qh)[GS][8]) {
     }
 }
 
-template <int D, int GS>
-struct Cfg {
-  static constexpr int W = kDecodeWaves;
-  static constexpr int LK = D / 16;                 // lanes per K row
-  static constexpr int RK = 64 / LK;                // K rows per step
-  static constexpr int EV = (64 / GS) < 16 ? (64 / GS) : 16;   // V elements per lane
-  static constexpr int LV = D / EV;                 // lanes per V row
-  static constexpr int RV = 64 / LV;                // V rows per step
-  static constexpr int TR = 8192 / D;               // rows per tile
-  static constexpr int KSTEPS = TR / RK;
-  static constexpr int VSTEPS = TR / RV;
-};
-
-// Buffer resource over `bytes` bytes at p: loads at or past the end return 0,
-// so tile edges need no branches (raw buffer, gfx9-family descriptor word).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
@@ -150,234 +139,424 @@ __device__ __forceinline__ float bloadf(rsrc_t r, uint32_t voff, uint32_t soff) 
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
-// ----------------------------------------------------------------- K phase --
-// s[row][g] = cq[g] * kscale[row] * sum_d k[row][d] * qh[g][d], rows < nrows.
-// Lane = 16 consecutive head_dim elements (chunk c) of row rr of each step.
-template <int D, int GS, int F>
-__device__ __forceinline__ void kphase(const void *base, const float *kscale, int nrows, int lane,
-                                       const h2 (&qh)[GS][8], const float (&cq)[GS], float *sw) {
-  using C = Cfg<D, GS>;
-  constexpr int EB = F == I8 ? 1 : (F == BF16 ? 2 : 4);  // bytes per element = uint4 per lane
-  constexpr int U = (F == I8 ? 8 : (F == BF16 ? 4 : 2)) / (GS >= 8 ? 2 : 1);   // steps per load group
-  constexpr uint32_t STEP = C::RK * D * EB;              // bytes per step
-  const int rr = lane / C::LK, c = lane % C::LK;
-  const rsrc_t rk = make_rsrc(base, (uint32_t)nrows * D * EB);
-  const rsrc_t rs = make_rsrc(kscale, kscale ? (uint32_t)nrows * 4 : 0u);
-  const uint32_t voff = (uint32_t)(rr * D + c * 16) * EB;
-  for (int s0 = 0; s0 < C::KSTEPS; s0 += U) {
-    if (s0 * C::RK >= nrows) break;
-    uint4 buf[U][EB];
-    float ks[U];
+constexpr int ebytes(int F) { return F == I8 ? 1 : (F == BF16 ? 2 : 4); }
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <int D, int GS, int KF, int VF>
+struct Cfg {
+  static constexpr int W = kDecodeWaves;
+  static constexpr int EBK = ebytes(KF), EBV = ebytes(VF);
+  static constexpr int TR = decode_tile_rows(D, KF, VF);   // rows per tile (K+V ~ 8 KB)
+  static constexpr int LK = D / 16;                     // lanes per K row (16 elements each)
+  static constexpr int RK = 64 / LK;                    // K rows per step
+  static constexpr int KSTEPS = (TR + RK - 1) / RK;
+  static constexpr int KQ = EBK;                        // uint4 per lane per K step
+  static constexpr int EV = cmin(16, 64 / GS);          // V elements per lane
+  static constexpr int LV = D / EV;                     // lanes per V row
+  static constexpr int RV = 64 / LV;                    // V rows per step
+  static constexpr int VSTEPS = (TR + RV - 1) / RV;
+  static constexpr int VDW = EV * EBV / 4;              // dwords per lane per V step
+};
+
+// Registers of one in-flight tile.
+template <int D, int GS, int KF, int VF>
+struct TileBuf {
+  using C = Cfg<D, GS, KF, VF>;
+  uint4 k[C::KSTEPS][C::KQ];
+  float ks[C::KSTEPS];
+  uint32_t v[C::VSTEPS][C::VDW];
+  float vs[C::VSTEPS];
+};
+
+// Where a tile lives and how many rows it has.
+struct TileRef {
+  const char *k;
+  const char *v;
+  const float *ks;
+  const float *vs;
+  int nrows;
+};
+
+template <int D, int GS, int KF, int VF>
+__device__ __forceinline__ void issue_k(TileBuf<D, GS, KF, VF> &B, const TileRef &T, int lane) {
+  using C = Cfg<D, GS, KF, VF>;
+  const rsrc_t rk = make_rsrc(T.k, (uint32_t)T.nrows * D * C::EBK);
+  const int rrk = lane / C::LK, ck = lane % C::LK;
+  const uint32_t vk = (uint32_t)(rrk * D + ck * 16) * C::EBK;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+  for (int s = 0; s < C::KSTEPS; ++s)
 #pragma unroll
-      for (int k = 0; k < EB; ++k) buf[u][k] = bload128(rk, voff + 16 * k, (s0 + u) * STEP);
-      if constexpr (F == I8) ks[u] = bloadf(rs, (uint32_t)rr * 4, (s0 + u) * C::RK * 4);
-      else ks[u] = 1.0f;
+    for (int k = 0; k < C::KQ; ++k) B.k[s][k] = bload128(rk, vk + 16 * k, s * C::RK * D * C::EBK);
+  if constexpr (KF == I8) {
+    const rsrc_t rs = make_rsrc(T.ks, (uint32_t)T.nrows * 4);
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) B.ks[s] = bloadf(rs, (uint32_t)rrk * 4, s * C::RK * 4);
+  }
+}
+
+template <int D, int GS, int KF, int VF>
+__device__ __forceinline__ void issue_v(TileBuf<D, GS, KF, VF> &B, const TileRef &T, int lane) {
+  using C = Cfg<D, GS, KF, VF>;
+  const rsrc_t rv = make_rsrc(T.v, (uint32_t)T.nrows * D * C::EBV);
+  const int rrv = lane / C::LV, cv = lane % C::LV;
+  const uint32_t vv = (uint32_t)(rrv * D + cv * C::EV) * C::EBV;
+#pragma unroll
+  for (int s = 0; s < C::VSTEPS; ++s) {
+    if constexpr (C::VDW % 4 == 0) {
+#pragma unroll
+      for (int k = 0; k < C::VDW / 4; ++k) {
+        const uint4 t = bload128(rv, vv + 16 * k, s * C::RV * D * C::EBV);
+        B.v[s][4 * k] = t.x; B.v[s][4 * k + 1] = t.y; B.v[s][4 * k + 2] = t.z; B.v[s][4 * k + 3] = t.w;
+      }
+    } else {
+      const uint2 t = bload64(rv, vv, s * C::RV * D * C::EBV);
+      B.v[s][0] = t.x; B.v[s][1] = t.y;
     }
+  }
+  if constexpr (VF == I8) {
+    const rsrc_t rs = make_rsrc(T.vs, (uint32_t)T.nrows * 4);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if ((s0 + u) * C::RK >= nrows) break;
-      const int row = (s0 + u) * C::RK + rr;
-      float dot[GS];
+    for (int s = 0; s < C::VSTEPS; ++s) B.vs[s] = bloadf(rs, (uint32_t)rrv * 4, s * C::RV * 4);
+  }
+}
+
+template <int D, int GS, int KF, int VF>
+__device__ __forceinline__ void issue(TileBuf<D, GS, KF, VF> &B, const TileRef &T, int lane) {
+  issue_k(B, T, lane);
+  issue_v(B, T, lane);
+}
+
+// ----------------------------------------------------------------- K phase --
+// s[row][g] = cq[g] * kscale[row] * sum_d k[row][d] * q[g][d].  Format F, 16
+// elements per lane held in F's bytes (KQ uint4).
+template <int D, int GS, int F, int STEPS, int KQ>
+__device__ __forceinline__ void kcompute(const uint4 (&kb)[STEPS][KQ], const float (&ks)[STEPS], int nrows,
+                                         int lane, h2 (&qh)[GS][8], const float (&cq)[GS], float *sw,
+                                         int row_base = 0) {
+  constexpr int LK = D / 16, RK = 64 / LK;
+  const int rr = lane / LK, c = lane % LK;
 #pragma unroll
-      for (int g = 0; g < GS; ++g) dot[g] = 0.0f;
-      if constexpr (F == I8) {
-        const uint32_t wv[4] = {buf[u][0].x, buf[u][0].y, buf[u][0].z, buf[u][0].w};
+  for (int s = 0; s < STEPS; ++s) {
+    if (row_base + s * RK >= nrows) break;
+    const int row = row_base + s * RK + rr;
+    float dot[GS];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          h2 lo, hi;
-          i8x4_to_h2(wv[q4], lo, hi);
+    for (int g = 0; g < GS; ++g) dot[g] = 0.0f;
+    if constexpr (F == I8) {
+      const uint32_t wv[4] = {kb[s][0].x, kb[s][0].y, kb[s][0].z, kb[s][0].w};
 #pragma unroll
-          for (int g = 0; g < GS; ++g) {
-            dot[g] = __builtin_amdgcn_fdot2(lo, qh[g][2 * q4], dot[g], false);
-            dot[g] = __builtin_amdgcn_fdot2(hi, qh[g][2 * q4 + 1], dot[g], false);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        h2 lo, hi;
+        i8x4_to_h2(wv[q4], lo, hi);
+#pragma unroll
+        for (int g = 0; g < GS; ++g) {
+          dot[g] = __builtin_amdgcn_fdot2(lo, qh[g][2 * q4], dot[g], false);
+          dot[g] = __builtin_amdgcn_fdot2(hi, qh[g][2 * q4 + 1], dot[g], false);
+        }
+      }
+    } else {
+      opaque(qh);   // keep the fp16 -> fp32 conversion inside v_fma_mix
+      float kf[16];
+      if constexpr (F == BF16) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const uint32_t wv[4] = {kb[s][k].x, kb[s][k].y, kb[s][k].z, kb[s][k].w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            kf[8 * k + 2 * t] = bf16lo(wv[t]);
+            kf[8 * k + 2 * t + 1] = bf16hi(wv[t]);
           }
         }
       } else {
-        // keep the fp16 -> fp32 query conversions inside the FMA (v_fma_mix)
-        opaque(const_cast<h2 (&)[GS][8]>(qh));
-        float kf[16];
-        if constexpr (F == BF16) {
 #pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const uint32_t wv[4] = {buf[u][k].x, buf[u][k].y, buf[u][k].z, buf[u][k].w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              kf[8 * k + 2 * t] = bf16lo(wv[t]);
-              kf[8 * k + 2 * t + 1] = bf16hi(wv[t]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            kf[4 * k + 0] = __uint_as_float(buf[u][k].x);
-            kf[4 * k + 1] = __uint_as_float(buf[u][k].y);
-            kf[4 * k + 2] = __uint_as_float(buf[u][k].z);
-            kf[4 * k + 3] = __uint_as_float(buf[u][k].w);
-          }
+        for (int k = 0; k < 4; ++k) {
+          kf[4 * k + 0] = __uint_as_float(kb[s][k].x);
+          kf[4 * k + 1] = __uint_as_float(kb[s][k].y);
+          kf[4 * k + 2] = __uint_as_float(kb[s][k].z);
+          kf[4 * k + 3] = __uint_as_float(kb[s][k].w);
         }
-#pragma unroll
-        for (int g = 0; g < GS; ++g)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            dot[g] = fmaf((float)qh[g][e].x, kf[2 * e], dot[g]);
-            dot[g] = fmaf((float)qh[g][e].y, kf[2 * e + 1], dot[g]);
-          }
       }
 #pragma unroll
-      for (int g = 0; g < GS; ++g) dot[g] = group_sum<C::LK>(dot[g]);
-      if (c == 0 && row < nrows) {
+      for (int g = 0; g < GS; ++g)
 #pragma unroll
-        for (int g = 0; g < GS; ++g) sw[row * GS + g] = dot[g] * ks[u] * cq[g];
-      }
+        for (int e = 0; e < 8; ++e) {
+          dot[g] = fmaf((float)qh[g][e].x, kf[2 * e], dot[g]);
+          dot[g] = fmaf((float)qh[g][e].y, kf[2 * e + 1], dot[g]);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < GS; ++g) dot[g] = group_red<LK, false>(dot[g]);
+    if (c == 0 && row < nrows) {
+#pragma unroll
+      for (int g = 0; g < GS; ++g) sw[row * GS + g] = dot[g] * (F == I8 ? ks[s] * cq[g] : cq[g]);
     }
   }
 }
 
 // ----------------------------------------------------------------- V phase --
-// acc[g][e] += sum over rows of w[row][g] * v[row][c*EV + e].  Rows at or past
-// nrows load as zeros and their (finite, stale) weights contribute nothing.
-template <int D, int GS, int F>
-__device__ __forceinline__ void vphase(const void *base, int nrows, int lane, const float *sw,
-                                       float (&acc)[GS][Cfg<D, GS>::EV]) {
-  using C = Cfg<D, GS>;
-  constexpr int EV = C::EV;
-  constexpr int EB = F == I8 ? 1 : (F == BF16 ? 2 : 4);
-  constexpr int DW = EV * EB / 4;                  // dwords per lane per step
-  constexpr int U = (16 / DW) < 1 ? 1 : ((16 / DW) < C::VSTEPS ? (16 / DW) : C::VSTEPS);
-  constexpr uint32_t STEP = C::RV * D * EB;
-  const int rr = lane / C::LV, c = lane % C::LV;
-  const rsrc_t rv = make_rsrc(base, (uint32_t)nrows * D * EB);
-  const uint32_t voff = (uint32_t)(rr * D + c * EV) * EB;
-  for (int s0 = 0; s0 < C::VSTEPS; s0 += U) {
-    if (s0 * C::RV >= nrows) break;
-    uint32_t buf[U][DW];
+// acc[g][e] += sum over rows of w[row][g] * vscale[row] * v[row][c*EV + e].
+// Rows past nrows hold zero data (buffer range) and finite stale weights.
+template <int D, int GS, int F, int STEPS, int VDW, int EV>
+__device__ __forceinline__ void vcompute(const uint32_t (&vb)[STEPS][VDW], const float (&vs)[STEPS], int nrows,
+                                         int lane, const float *sw, float (&acc)[GS][EV], int row_base = 0) {
+  constexpr int LV = D / EV, RV = 64 / LV;
+  const int rr = lane / LV;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if constexpr (DW % 4 == 0) {
+  for (int s = 0; s < STEPS; ++s) {
+    if (row_base + s * RV >= nrows) break;
+    const int row = row_base + s * RV + rr;
+    float w[GS];
 #pragma unroll
-        for (int k = 0; k < DW / 4; ++k) {
-          const uint4 t = bload128(rv, voff + 16 * k, (s0 + u) * STEP);
-          buf[u][4 * k] = t.x; buf[u][4 * k + 1] = t.y; buf[u][4 * k + 2] = t.z; buf[u][4 * k + 3] = t.w;
-        }
-      } else {
-        const uint2 t = bload64(rv, voff, (s0 + u) * STEP);
-        buf[u][0] = t.x; buf[u][1] = t.y;
-      }
+    for (int g = 0; g < GS; ++g) w[g] = sw[row * GS + g];
+    if constexpr (F == I8) {
+#pragma unroll
+      for (int g = 0; g < GS; ++g) w[g] *= vs[s];
+    }
+    float v[EV];
+    if constexpr (F == I8) {
+#pragma unroll
+      for (int k = 0; k < VDW; ++k)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[4 * k + t] = i8b(vb[s][k], t);
+    } else if constexpr (F == BF16) {
+#pragma unroll
+      for (int k = 0; k < VDW; ++k) { v[2 * k] = bf16lo(vb[s][k]); v[2 * k + 1] = bf16hi(vb[s][k]); }
+    } else {
+#pragma unroll
+      for (int k = 0; k < VDW; ++k) v[k] = __uint_as_float(vb[s][k]);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if ((s0 + u) * C::RV >= nrows) break;
-      const int row = (s0 + u) * C::RV + rr;
-      float w[GS];
+    for (int g = 0; g < GS; ++g)
 #pragma unroll
-      for (int g = 0; g < GS; ++g) w[g] = sw[row * GS + g];
-      float v[EV];
-      if constexpr (F == I8) {
-#pragma unroll
-        for (int k = 0; k < DW; ++k)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) v[4 * k + t] = i8b(buf[u][k], t);
-      } else if constexpr (F == BF16) {
-#pragma unroll
-        for (int k = 0; k < DW; ++k) { v[2 * k] = bf16lo(buf[u][k]); v[2 * k + 1] = bf16hi(buf[u][k]); }
-      } else {
-#pragma unroll
-        for (int k = 0; k < DW; ++k) v[k] = __uint_as_float(buf[u][k]);
-      }
-#pragma unroll
-      for (int g = 0; g < GS; ++g)
-#pragma unroll
-        for (int e = 0; e < EV; ++e) acc[g][e] = fmaf(w[g], v[e], acc[g][e]);
-    }
+      for (int e = 0; e < EV; ++e) acc[g][e] = fmaf(w[g], v[e], acc[g][e]);
   }
 }
 
 // ------------------------------------------------------------ logit phase --
-// Items (block n, head g) with g = lane % GS.  TAIL: every "block" is one raw
-// token (R = S = 1, A = [1]).  Updates the running max, rescale factors and
-// the lane's partial sum; overwrites sw with the value weights w * vscale.
+// Items (block n, head g) laid out as lane = (n * GS + g) * LR + lr, where
+// lr picks tokens lr*8 .. lr*8+7 of the block (LR = ceil(R / 8)).  Updates
+// the running max (uniform m_u, per-lane m_own), the rescale factors and the
+// lane's partial sum; overwrites sw with the value weights w = p A.
+// TAIL: every "block" is one raw token (R = S = 1, A = [1]); the lane layout
+// keeps the LR of the archive so every lane tracks the same head throughout,
+// and only the first lane of an item contributes.
+template <int SP>
+__device__ __forceinline__ void load_row(const float *sA, int r, float (&a)[SP]) {
+  if constexpr (SP % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < SP; j += 4) {
+      const float4 t = *reinterpret_cast<const float4 *>(sA + r * SP + j);
+      a[j] = t.x; a[j + 1] = t.y; a[j + 2] = t.z; a[j + 3] = t.w;
+    }
+  } else {
+    const float2 t = *reinterpret_cast<const float2 *>(sA + r * SP);
+    a[0] = t.x; a[1] = t.y;
+  }
+}
+
 template <int GS, int SP, bool TAIL>
-__device__ __forceinline__ void logits(const DecodeArgs &a, const float *sA, float *sw, int nb, const float *__restrict__ vscale,
-                                       int lane, float (&m_u)[GS], float &m_own, float &l_own,
-                                       float (&alpha)[GS]) {
-  const int S = TAIL ? 1 : a.S;
-  const int R = TAIL ? 1 : a.R;
-  const int g = lane % GS;
+__device__ __forceinline__ void logits(const float *sA, float *sw, int nb, int R, int S, int LR, int lane,
+                                       float (&m_u)[GS], float &m_own, float &l_own, float (&alpha)[GS]) {
+  const int lr = lane % LR;
+  const int g = (lane / LR) % GS;
+  const int per_pass = 64 / LR;                 // items per pass
   const int items = nb * GS;
+  // tokens of this lane in every block: lr*8 .. lr*8 + rc - 1
+  const int rc = TAIL ? (lr == 0 ? 1 : 0) : ((R - lr * 8) < 8 ? (R - lr * 8) : 8);
+  const bool full = !TAIL && (R % 8 == 0);      // uniform: every lane has 8 tokens
   float mx = -INFINITY;
-  for (int i = lane; i < items; i += 64) {
-    const int n = i / GS;
+  float zc[8];                                   // logits of the first pass
+#pragma unroll
+  for (int r8 = 0; r8 < 8; ++r8) zc[r8] = -INFINITY;
+  for (int i0 = 0; i0 < items; i0 += per_pass) {
+    const int i = i0 + lane / LR;
+    const bool live = i < items;
+    const int n = live ? i / GS : 0;
     float sv[SP];
 #pragma unroll
     for (int j = 0; j < SP; ++j) sv[j] = (j < S) ? sw[(n * S + j) * GS + g] : 0.0f;
     if constexpr (TAIL) {
-      mx = fmaxf(mx, sv[0]);
-    } else {
-      for (int r = 0; r < R; ++r) {
-        const float *Ar = sA + r * SP;
+      if (live && rc) {
+        zc[0] = sv[0];
+        mx = fmaxf(mx, sv[0]);
+      }
+    } else if (full) {
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8) {
+        float a[SP];
+        load_row<SP>(sA, lr * 8 + r8, a);
         float z = 0.0f;
 #pragma unroll
-        for (int j = 0; j < SP; ++j) z = fmaf(Ar[j], sv[j], z);
-        mx = fmaxf(mx, z);
+        for (int j = 0; j < SP; ++j) z = fmaf(a[j], sv[j], z);
+        zc[r8] = z;
+        mx = fmaxf(mx, live ? z : -INFINITY);
+      }
+    } else {
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8) {
+        if (r8 < rc) {
+          float a[SP];
+          load_row<SP>(sA, lr * 8 + r8, a);
+          float z = 0.0f;
+#pragma unroll
+          for (int j = 0; j < SP; ++j) z = fmaf(a[j], sv[j], z);
+          zc[r8] = z;
+          mx = fmaxf(mx, live ? z : -INFINITY);
+        }
       }
     }
   }
-  mx = strided<GS, true>(mx);
+  mx = head_reduce<GS, true>(mx, LR);
   const float mnew_own = fmaxf(m_own, mx);
   const float alpha_own = __builtin_amdgcn_exp2f(m_own - mnew_own);
 #pragma unroll
   for (int gg = 0; gg < GS; ++gg) {
-    const float mn = fmaxf(m_u[gg], readlane(mx, gg));
+    const float mn = fmaxf(m_u[gg], readlane(mx, gg * LR));
     alpha[gg] = __builtin_amdgcn_exp2f(m_u[gg] - mn);
     m_u[gg] = mn;
   }
   m_own = mnew_own;
+  const bool one_pass = items <= per_pass;
   float lsum = 0.0f;
-  for (int i = lane; i < items; i += 64) {
-    const int n = i / GS;
+  for (int i0 = 0; i0 < items; i0 += per_pass) {
+    const int i = i0 + lane / LR;
+    const bool live = i < items;
+    const int n = live ? i / GS : 0;
     float sv[SP];
+    if (!one_pass) {
 #pragma unroll
-    for (int j = 0; j < SP; ++j) sv[j] = (j < S) ? sw[(n * S + j) * GS + g] : 0.0f;
+      for (int j = 0; j < SP; ++j) sv[j] = (j < S) ? sw[(n * S + j) * GS + g] : 0.0f;
+    }
     float w[SP];
+#pragma unroll
+    for (int j = 0; j < SP; ++j) w[j] = 0.0f;
     if constexpr (TAIL) {
-      const float p = __builtin_amdgcn_exp2f(sv[0] - m_own);
-      lsum += p;
-      w[0] = p;
+      if (live && rc) {
+        const float p = __builtin_amdgcn_exp2f((one_pass ? zc[0] : sv[0]) - m_own);
+        lsum += p;
+        w[0] = p;
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < SP; ++j) w[j] = 0.0f;
-      for (int r = 0; r < R; ++r) {
-        const float *Ar = sA + r * SP;
-        float z = 0.0f;
+      for (int r8 = 0; r8 < 8; ++r8) {
+        if (full || r8 < rc) {
+          float a[SP];
+          load_row<SP>(sA, lr * 8 + r8, a);
+          float z;
+          if (one_pass) {
+            z = zc[r8];
+          } else {
+            z = 0.0f;
 #pragma unroll
-        for (int j = 0; j < SP; ++j) z = fmaf(Ar[j], sv[j], z);
-        const float p = __builtin_amdgcn_exp2f(z - m_own);
-        lsum += p;
+            for (int j = 0; j < SP; ++j) z = fmaf(a[j], sv[j], z);
+          }
+          const float p = live ? __builtin_amdgcn_exp2f(z - m_own) : 0.0f;
+          lsum += p;
 #pragma unroll
-        for (int j = 0; j < SP; ++j) w[j] = fmaf(p, Ar[j], w[j]);
+          for (int j = 0; j < SP; ++j) w[j] = fmaf(p, a[j], w[j]);
+        }
       }
     }
+    if (LR == 2) {
 #pragma unroll
-    for (int j = 0; j < SP; ++j)
-      if (j < S) sw[(n * S + j) * GS + g] = w[j] * (vscale ? vscale[n * S + j] : 1.0f);
+      for (int j = 0; j < SP; ++j) w[j] = group_red<2, false>(w[j]);
+    } else if (LR == 4) {
+#pragma unroll
+      for (int j = 0; j < SP; ++j) w[j] = group_red<4, false>(w[j]);
+    }
+    if (live && lr == 0) {
+#pragma unroll
+      for (int j = 0; j < SP; ++j)
+        if (j < S) sw[(n * S + j) * GS + g] = w[j];
+    }
   }
   l_own = l_own * alpha_own + lsum;
 }
 
-template <int D, int GS, int SP>
+// acc *= alpha, skipped when no head's running max moved (the common case).
+template <int GS, int EV>
+__device__ __forceinline__ void rescale(float (&acc)[GS][EV], const float (&alpha)[GS]) {
+  bool moved = false;
+#pragma unroll
+  for (int g = 0; g < GS; ++g) moved |= alpha[g] != 1.0f;
+  if (moved) {
+#pragma unroll
+    for (int g = 0; g < GS; ++g)
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[g][e] *= alpha[g];
+  }
+}
+
+template <int D, int GS, int SP, int KF, int VF>
+__device__ __forceinline__ void process_k(const TileBuf<D, GS, KF, VF> &B, int nrows, int lane, h2 (&qh)[GS][8],
+                                          const float (&cq)[GS], float *sw) {
+  using C = Cfg<D, GS, KF, VF>;
+  kcompute<D, GS, KF, C::KSTEPS, C::KQ>(B.k, B.ks, nrows, lane, qh, cq, sw);
+  wave_lds_sync();
+}
+
+template <int D, int GS, int SP, int KF, int VF>
+__device__ __forceinline__ void process_lv(const TileBuf<D, GS, KF, VF> &B, int nrows, int S, int R, int LR,
+                                           int lane, const float *sA, float *sw, float (&m_u)[GS], float &m_own,
+                                           float &l_own, float (&acc)[GS][Cfg<D, GS, KF, VF>::EV]) {
+  using C = Cfg<D, GS, KF, VF>;
+  float alpha[GS];
+  logits<GS, SP, false>(sA, sw, nrows / S, R, S, LR, lane, m_u, m_own, l_own, alpha);
+  rescale(acc, alpha);
+  wave_lds_sync();
+  vcompute<D, GS, VF, C::VSTEPS, C::VDW, C::EV>(B.v, B.vs, nrows, lane, sw, acc);
+  wave_lds_sync();
+}
+
+// The raw tail (< R tokens of bf16 / fp32) in one wave, one load step at a
+// time so it needs few registers.  Every token is a block with R = S = 1.
+template <int D, int GS, int SP, int RAWK, int RAWV, int EV>
+__device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt, int LR, int lane, h2 (&qh)[GS][8],
+                                          const float (&cq)[GS], const float *sA, float *sw, float (&m_u)[GS],
+                                          float &m_own, float &l_own, float (&acc)[GS][EV]) {
+  constexpr int LK = D / 16, RK = 64 / LK, EBK = ebytes(RAWK), EBV = ebytes(RAWV);
+  constexpr int LV = D / EV, RV = 64 / LV, VDW = EV * EBV / 4;
+  const rsrc_t rk = make_rsrc(kt, (uint32_t)nt * D * EBK);
+  const rsrc_t rv = make_rsrc(vt, (uint32_t)nt * D * EBV);
+  const int rrk = lane / LK, ck = lane % LK;
+  const float one[1] = {1.0f};
+  for (int r0 = 0; r0 < nt; r0 += RK) {
+    uint4 kb[1][EBK];
+#pragma unroll
+    for (int k = 0; k < EBK; ++k) kb[0][k] = bload128(rk, (uint32_t)(rrk * D + ck * 16) * EBK + 16 * k, r0 * D * EBK);
+    kcompute<D, GS, RAWK, 1, EBK>(kb, one, nt, lane, qh, cq, sw, r0);
+  }
+  wave_lds_sync();
+  float alpha[GS];
+  logits<GS, SP, true>(sA, sw, nt, 1, 1, LR, lane, m_u, m_own, l_own, alpha);
+  rescale(acc, alpha);
+  wave_lds_sync();
+  const int rrv = lane / LV, cv = lane % LV;
+  const uint32_t off = (uint32_t)(rrv * D + cv * EV) * EBV;
+  for (int r0 = 0; r0 < nt; r0 += RV) {
+    uint32_t vb[1][VDW];
+#pragma unroll
+    for (int k = 0; k < VDW / 4; ++k) {
+      const uint4 t = bload128(rv, off + 16 * k, r0 * D * EBV);
+      vb[0][4 * k] = t.x; vb[0][4 * k + 1] = t.y; vb[0][4 * k + 2] = t.z; vb[0][4 * k + 3] = t.w;
+    }
+    vcompute<D, GS, RAWV, 1, VDW, EV>(vb, one, nt, lane, sw, acc, r0);
+  }
+  wave_lds_sync();
+}
+
+template <int D, int GS, int SP, int KF, int VF>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
-  using C = Cfg<D, GS>;
+  using C = Cfg<D, GS, KF, VF>;
   constexpr int W = C::W, EV = C::EV;
-  // per-wave s / w scratch during tiles, then the workgroup merge area
-  constexpr int SW_FLOATS = C::TR * GS;
+  constexpr int SWR = C::TR > kMaxR ? C::TR : kMaxR;    // tile rows or tail tokens
+  constexpr int SW_FLOATS = SWR * GS;
   constexpr int MERGE_FLOATS = W * GS * D + W * GS * 2;
-  constexpr int COMB_FLOATS = 2 * 256 * GS + GS;   // ns <= 256
-  constexpr int LDS_A = (W * SW_FLOATS > MERGE_FLOATS) ? W * SW_FLOATS : MERGE_FLOATS;
-  constexpr int LDS_FLOATS = LDS_A > COMB_FLOATS ? LDS_A : COMB_FLOATS;
+  constexpr int COMB_FLOATS = 2 * kMaxSplits * GS + GS;
+  constexpr int LDS_FLOATS = cmax(cmax(W * SW_FLOATS, MERGE_FLOATS), COMB_FLOATS);
   __shared__ float lds[LDS_FLOATS];
-  __shared__ float sA[kMaxR * SP];   // synthesis basis, copied once from the arguments
+  __shared__ __attribute__((aligned(16))) float sA[kMaxR * SP];
   __shared__ int last_flag;
 
   const int tid = threadIdx.x;
@@ -390,14 +569,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   const int64_t b = bh / a.H;
   const int h = (int)(bh % a.H);
   const int hq0 = h * a.G + qg * GS;
-  // kernel arguments may live in host-coherent memory: read A once, here
-  for (int i = tid; i < a.R * SP; i += 64 * W) sA[i] = a.A[i];
+  const int R = a.R, S = a.S;
+  const int LR = R <= 8 ? 1 : (R <= 16 ? 2 : 4);
+
+  // kernel arguments may sit in host-coherent memory: copy A to LDS once
+  for (int i = tid; i < R * SP; i += 64 * W) sA[i] = a.A[i];
+  float *sw = lds + wave * SW_FLOATS;
+  // weights of rows past a tile's end multiply zero data: keep them finite
+  for (int i = lane; i < SW_FLOATS; i += 64) sw[i] = 0.0f;
   __syncthreads();
 
-  // ---- query: fp16 pairs of the lane's 16 K elements, pre-scaled per head
+  // ---- query: fp16 pairs of the lane's 16 K elements, pre-scaled per head;
+  // done after the first tile's loads are issued so the latencies overlap
   h2 qh[GS][8];
   float cq[GS];
-  {
+  auto setup_q = [&]() {
     const int d0 = (lane % C::LK) * 16;
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
@@ -412,7 +598,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
         qf[2 * t + 1] = bf16hi(wv[t]);
         amax = fmaxf(amax, fmaxf(fabsf(qf[2 * t]), fabsf(qf[2 * t + 1])));
       }
-      amax = group_max<C::LK>(amax);
+      amax = group_red<C::LK, true>(amax);
       int E = 0;
       if (amax > 0.0f) frexpf(amax, &E);
       const float up = ldexpf(1.0f, 15 - E);
@@ -420,9 +606,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       for (int t = 0; t < 8; ++t) qh[g][t] = h2{(_Float16)(qf[2 * t] * up), (_Float16)(qf[2 * t + 1] * up)};
       cq[g] = a.qk_scale * ldexpf(1.0f, E - 15);
     }
-  }
+  };
 
-  float m_u[GS], alpha[GS];
+  float m_u[GS];
   float acc[GS][EV];
 #pragma unroll
   for (int g = 0; g < GS; ++g) {
@@ -431,74 +617,89 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     for (int e = 0; e < EV; ++e) acc[g][e] = 0.0f;
   }
   float m_own = -INFINITY, l_own = 0.0f;
-  float *sw = lds + wave * SW_FLOATS;
-  // weights of rows past a tile's end are read but multiply zero data: keep
-  // them finite from the start
-  for (int i = lane; i < SW_FLOATS; i += 64) sw[i] = 0.0f;
-  wave_lds_sync();
 
-  const int S = a.S;
+  // ---- this wave's tiles: t = wave, wave + W, ... of the split
   const int NB = C::TR / S;
   const int64_t blk0 = (int64_t)split * a.chunk;
   const int64_t blk1 = (blk0 + a.chunk < a.n_blocks) ? blk0 + a.chunk : a.n_blocks;
   const int64_t nblk = blk1 > blk0 ? blk1 - blk0 : 0;
   const int ntiles = (int)((nblk + NB - 1) / NB);
   const int64_t k_bh = bh * a.k_bh_rows, v_bh = bh * a.v_bh_rows;
-  const int kes = a.kf == I8 ? 1 : (a.kf == BF16 ? 2 : 4);
-  const int ves = a.vf == I8 ? 1 : (a.vf == BF16 ? 2 : 4);
-
-  for (int t = wave; t < ntiles; t += W) {
-    opaque(qh);
+  auto tile_ref = [&](int t) {
+    TileRef T;
     const int64_t tb0 = blk0 + (int64_t)t * NB;
     const int nb = (int)((blk1 - tb0) < NB ? (blk1 - tb0) : NB);
-    const int nrows = nb * S;
     const int64_t row0 = tb0 * S;
-    const char *kb = static_cast<const char *>(a.krows) + (k_bh + row0) * D * kes;
-    const char *vb = static_cast<const char *>(a.vrows) + (v_bh + row0) * D * ves;
-    const float *ksc = a.kf == I8 ? a.kscales + k_bh + row0 : nullptr;
-    const float *vsc = a.vf == I8 ? a.vscales + v_bh + row0 : nullptr;
-    if (a.kf == I8) kphase<D, GS, I8>(kb, ksc, nrows, lane, qh, cq, sw);
-    else if (a.kf == BF16) kphase<D, GS, BF16>(kb, nullptr, nrows, lane, qh, cq, sw);
-    else kphase<D, GS, F32>(kb, nullptr, nrows, lane, qh, cq, sw);
-    wave_lds_sync();
-    logits<GS, SP, false>(a, sA, sw, nb, vsc, lane, m_u, m_own, l_own, alpha);
-#pragma unroll
-    for (int g = 0; g < GS; ++g)
-#pragma unroll
-      for (int e = 0; e < EV; ++e) acc[g][e] *= alpha[g];
-    wave_lds_sync();
-    if (a.vf == I8) vphase<D, GS, I8>(vb, nrows, lane, sw, acc);
-    else if (a.vf == BF16) vphase<D, GS, BF16>(vb, nrows, lane, sw, acc);
-    else vphase<D, GS, F32>(vb, nrows, lane, sw, acc);
-    wave_lds_sync();
+    T.k = static_cast<const char *>(a.krows) + (k_bh + row0) * D * C::EBK;
+    T.v = static_cast<const char *>(a.vrows) + (v_bh + row0) * D * C::EBV;
+    T.ks = KF == I8 ? a.kscales + k_bh + row0 : nullptr;
+    T.vs = VF == I8 ? a.vscales + v_bh + row0 : nullptr;
+    T.nrows = nb * S;
+    return T;
+  };
+
+  if constexpr (GS <= 4) {
+    // two register buffers: tile t + W is in flight while tile t is computed
+    TileBuf<D, GS, KF, VF> bufA, bufB;
+    int t = wave;
+    if (t < ntiles) issue(bufA, tile_ref(t), lane);
+    setup_q();
+    for (; t < ntiles; t += 2 * W) {
+      const int t1 = t + W;
+      if (t1 < ntiles) issue(bufB, tile_ref(t1), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      const int n0 = tile_ref(t).nrows;
+      process_k<D, GS, SP, KF, VF>(bufA, n0, lane, qh, cq, sw);
+      process_lv<D, GS, SP, KF, VF>(bufA, n0, S, R, LR, lane, sA, sw, m_u, m_own, l_own, acc);
+      if (t1 < ntiles) {
+        const int t2 = t1 + W;
+        if (t2 < ntiles) issue(bufA, tile_ref(t2), lane);
+        __builtin_amdgcn_sched_barrier(0);
+        const int n1 = tile_ref(t1).nrows;
+        process_k<D, GS, SP, KF, VF>(bufB, n1, lane, qh, cq, sw);
+        process_lv<D, GS, SP, KF, VF>(bufB, n1, S, R, LR, lane, sA, sw, m_u, m_own, l_own, acc);
+      }
+    }
+  } else {
+    // one register buffer: the next tile's K rows are requested as soon as
+    // this tile's K phase is done, its V rows as soon as the V phase is done
+    TileBuf<D, GS, KF, VF> buf;
+    int t = wave;
+    if (t < ntiles) issue(buf, tile_ref(t), lane);
+    setup_q();
+    for (; t < ntiles; t += W) {
+      const int tn = t + W;
+      const int n0 = tile_ref(t).nrows;
+      process_k<D, GS, SP, KF, VF>(buf, n0, lane, qh, cq, sw);
+      if (tn < ntiles) issue_k(buf, tile_ref(tn), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      process_lv<D, GS, SP, KF, VF>(buf, n0, S, R, LR, lane, sA, sw, m_u, m_own, l_own, acc);
+      if (tn < ntiles) issue_v(buf, tile_ref(tn), lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
-  // the raw tail: one wave of the last split, token by token
+  // ---- the raw tail: one wave of the last split
   if (a.n_tail > 0 && split == a.ns - 1 && wave == ntiles % W) {
-    opaque(qh);
     const int nt = a.n_tail;
-    const char *kt = static_cast<const char *>(a.ktail) + bh * (int64_t)a.R * D * (a.kraw == BF16 ? 2 : 4);
-    const char *vt = static_cast<const char *>(a.vtail) + bh * (int64_t)a.R * D * (a.vraw == BF16 ? 2 : 4);
-    if (a.kraw == BF16) kphase<D, GS, BF16>(kt, nullptr, nt, lane, qh, cq, sw);
-    else kphase<D, GS, F32>(kt, nullptr, nt, lane, qh, cq, sw);
-    wave_lds_sync();
-    logits<GS, SP, true>(a, sA, sw, nt, nullptr, lane, m_u, m_own, l_own, alpha);
-#pragma unroll
-    for (int g = 0; g < GS; ++g)
-#pragma unroll
-      for (int e = 0; e < EV; ++e) acc[g][e] *= alpha[g];
-    wave_lds_sync();
-    if (a.vraw == BF16) vphase<D, GS, BF16>(vt, nt, lane, sw, acc);
-    else vphase<D, GS, F32>(vt, nt, lane, sw, acc);
-    wave_lds_sync();
+    const char *kt = static_cast<const char *>(a.ktail) + bh * (int64_t)R * D * (a.kraw == BF16 ? 2 : 4);
+    const char *vt = static_cast<const char *>(a.vtail) + bh * (int64_t)R * D * (a.vraw == BF16 ? 2 : 4);
+    if (a.kraw == BF16 && a.vraw == BF16)
+      tail_pass<D, GS, SP, BF16, BF16, EV>(kt, vt, nt, LR, lane, qh, cq, sA, sw, m_u, m_own, l_own, acc);
+    else if (a.kraw == F32 && a.vraw == F32)
+      tail_pass<D, GS, SP, F32, F32, EV>(kt, vt, nt, LR, lane, qh, cq, sA, sw, m_u, m_own, l_own, acc);
+    else if (a.kraw == BF16)
+      tail_pass<D, GS, SP, BF16, F32, EV>(kt, vt, nt, LR, lane, qh, cq, sA, sw, m_u, m_own, l_own, acc);
+    else
+      tail_pass<D, GS, SP, F32, BF16, EV>(kt, vt, nt, LR, lane, qh, cq, sA, sw, m_u, m_own, l_own, acc);
   }
 
-  // ---- wave totals: l over lanes of a head, acc over the rows of a step
+  // ---- wave totals: l over the lanes of a head, acc over the rows of a step
   float l_u[GS];
   {
-    const float lt = strided<GS, false>(l_own);
+    const float lt = head_reduce<GS, false>(l_own, LR);
 #pragma unroll
-    for (int g = 0; g < GS; ++g) l_u[g] = readlane(lt, g);
+    for (int g = 0; g < GS; ++g) l_u[g] = readlane(lt, g * LR);
   }
 #pragma unroll
   for (int g = 0; g < GS; ++g)
@@ -523,7 +724,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   }
   __syncthreads();
 
-  // ---- workgroup partial
+  // ---- the workgroup's partial, published with device-scope stores
   float *pacc = a.part_acc + (pairq * a.ns + split) * GS * D;
   float *pml = a.part_ml + (pairq * a.ns + split) * GS * 2;
   for (int idx = tid; idx < GS * D; idx += 64 * W) {
@@ -543,18 +744,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
         }
       }
     }
-    pacc[g * D + d] = s;
+    __hip_atomic_store(pacc + g * D + d, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == 0) {
-      pml[g * 2] = m;
-      pml[g * 2 + 1] = l;
+      __hip_atomic_store(pml + g * 2, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pml + g * 2 + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-
-  // ---- split arrival; the last workgroup of (b, h, group) combines.
-  // Writers only release (L2 write-back); the one combining workgroup
-  // acquires (L2 invalidate).  A full fence in every workgroup would
-  // invalidate the XCD's L2 once per workgroup.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // Device-scope stores are complete once this thread's memory counter
+  // drains; only after every thread's have drained is the arrival counted.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
     const uint32_t old = __hip_atomic_fetch_add(a.counters + pairq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -562,19 +760,16 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   }
   __syncthreads();
   if (!last_flag) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-  // (max, sum) of every split into LDS, one load per thread; then the
-  // per-split weights; then every (head, d) output sums its split partials
-  // with independent loads.  Partials of other workgroups are visible after
-  // the acquire fence above.
+  // ---- last arrival: (max, sum) of every split into LDS, weights per split,
+  // then every (head, d) sums its split partials with independent loads.
   const float *Pacc = a.part_acc + pairq * a.ns * GS * D;
   const float *Pml = a.part_ml + pairq * a.ns * GS * 2;
-  float *cml = lds;                     // [ns*GS][2]; later f = weight per split
-  float *cM = lds + 2 * a.ns * GS;      // [GS] max, [GS] 1/sum
+  float *cml = lds;                     // [ns*GS][2]; later the weight per split
+  float *cM = lds + 2 * a.ns * GS;      // [GS] 1/sum
   for (int i = tid; i < a.ns * GS; i += 64 * W) {
-    cml[2 * i] = Pml[2 * i];
-    cml[2 * i + 1] = Pml[2 * i + 1];
+    cml[2 * i] = __hip_atomic_load(Pml + 2 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    cml[2 * i + 1] = __hip_atomic_load(Pml + 2 * i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (tid < GS) {
@@ -595,12 +790,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
     int sp = 0;
     for (; sp + 4 <= a.ns; sp += 4) {
-      s0 = fmaf(cml[2 * ((sp + 0) * GS + g)], Pacc[((sp + 0) * GS + g) * D + d], s0);
-      s1 = fmaf(cml[2 * ((sp + 1) * GS + g)], Pacc[((sp + 1) * GS + g) * D + d], s1);
-      s2 = fmaf(cml[2 * ((sp + 2) * GS + g)], Pacc[((sp + 2) * GS + g) * D + d], s2);
-      s3 = fmaf(cml[2 * ((sp + 3) * GS + g)], Pacc[((sp + 3) * GS + g) * D + d], s3);
+      const float p0 = __hip_atomic_load(Pacc + ((sp + 0) * GS + g) * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float p1 = __hip_atomic_load(Pacc + ((sp + 1) * GS + g) * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float p2 = __hip_atomic_load(Pacc + ((sp + 2) * GS + g) * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float p3 = __hip_atomic_load(Pacc + ((sp + 3) * GS + g) * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s0 = fmaf(cml[2 * ((sp + 0) * GS + g)], p0, s0);
+      s1 = fmaf(cml[2 * ((sp + 1) * GS + g)], p1, s1);
+      s2 = fmaf(cml[2 * ((sp + 2) * GS + g)], p2, s2);
+      s3 = fmaf(cml[2 * ((sp + 3) * GS + g)], p3, s3);
     }
-    for (; sp < a.ns; ++sp) s0 = fmaf(cml[2 * (sp * GS + g)], Pacc[(sp * GS + g) * D + d], s0);
+    for (; sp < a.ns; ++sp)
+      s0 = fmaf(cml[2 * (sp * GS + g)],
+                __hip_atomic_load(Pacc + (sp * GS + g) * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), s0);
     const float o = ((s0 + s1) + (s2 + s3)) * cM[g];
     const int64_t off = b * a.o_sb + (int64_t)(hq0 + g) * a.o_sh + d;
     if (a.out_f32) {
@@ -611,33 +812,44 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       static_cast<uint16_t *>(a.out)[off] = (uint16_t)(u >> 16);
     }
   }
-  if (tid == 0) a.counters[pairq] = 0u;
+  if (tid == 0) __hip_atomic_store(a.counters + pairq, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int GS, int SP>
+template <int D, int GS, int SP, int KF, int VF>
 int launch_one(const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, GS, SP>), dim3((unsigned)n_wg), dim3(64 * kDecodeWaves), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<D, GS, SP, KF, VF>), dim3((unsigned)n_wg), dim3(64 * kDecodeWaves), 0, stream,
+                     a);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-template <int D, int GS>
+template <int D, int GS, int KF, int VF>
 int launch_sp(int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
   switch (SP) {
-    case 2: return launch_one<D, GS, 2>(a, n_wg, stream);
-    case 4: return launch_one<D, GS, 4>(a, n_wg, stream);
-    case 8: return launch_one<D, GS, 8>(a, n_wg, stream);
-    case 16: return launch_one<D, GS, 16>(a, n_wg, stream);
+    case 2: return launch_one<D, GS, 2, KF, VF>(a, n_wg, stream);
+    case 4: return launch_one<D, GS, 4, KF, VF>(a, n_wg, stream);
+    case 8: return launch_one<D, GS, 8, KF, VF>(a, n_wg, stream);
+    case 16: return launch_one<D, GS, 16, KF, VF>(a, n_wg, stream);
     default: return -1;
   }
 }
 
-template <int D>
-int launch_d(int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
+template <int D, int KF, int VF>
+int launch_gs(int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
   switch (GS) {
-    case 1: return launch_sp<D, 1>(SP, a, n_wg, stream);
-    case 2: return launch_sp<D, 2>(SP, a, n_wg, stream);
-    case 4: return launch_sp<D, 4>(SP, a, n_wg, stream);
-    case 8: return launch_sp<D, 8>(SP, a, n_wg, stream);
+    case 1: return launch_sp<D, 1, KF, VF>(SP, a, n_wg, stream);
+    case 2: return launch_sp<D, 2, KF, VF>(SP, a, n_wg, stream);
+    case 4: return launch_sp<D, 4, KF, VF>(SP, a, n_wg, stream);
+    case 8: return launch_sp<D, 8, KF, VF>(SP, a, n_wg, stream);
+    default: return -1;
+  }
+}
+
+template <int KF, int VF>
+int launch_fmt(int D, int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_gs<64, KF, VF>(GS, SP, a, n_wg, stream);
+    case 128: return launch_gs<128, KF, VF>(GS, SP, a, n_wg, stream);
+    case 256: return launch_gs<256, KF, VF>(GS, SP, a, n_wg, stream);
     default: return -1;
   }
 }

@@ -90,12 +90,27 @@ struct DecodeArgs {
 // Heads of one query group handled per workgroup, and padded kept rows.
 int decode_group_size(int G);
 int decode_pad_keep(int S);
-// rows of a K/V tile for head_dim D
-inline int decode_tile_rows(int D) { return 8192 / D; }
 
-int launch_decode(int D, int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
-int launch_decode_d64(int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
-int launch_decode_d128(int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
-int launch_decode_d256(int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
+constexpr int kMaxSplits = 256;   // splits per (b, kv head, query group)
+
+// Coefficient rows per decode tile: about 8 KB of key plus value rows.
+constexpr int decode_elem_bytes(int f) { return f == I8 ? 1 : (f == BF16 ? 2 : 4); }
+constexpr int decode_tile_rows(int D, int kf, int vf) {
+  return 8192 / (D * (decode_elem_bytes(kf) + decode_elem_bytes(vf)));
+}
+
+int launch_decode(int D, int GS, int SP, int kf, int vf, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
+#define CDATTN_DECL_DECODE(K, V) \
+  int launch_decode_##K##_##V(int D, int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
+CDATTN_DECL_DECODE(i8, i8)
+CDATTN_DECL_DECODE(i8, bf16)
+CDATTN_DECL_DECODE(i8, f32)
+CDATTN_DECL_DECODE(bf16, i8)
+CDATTN_DECL_DECODE(bf16, bf16)
+CDATTN_DECL_DECODE(bf16, f32)
+CDATTN_DECL_DECODE(f32, i8)
+CDATTN_DECL_DECODE(f32, bf16)
+CDATTN_DECL_DECODE(f32, f32)
+#undef CDATTN_DECL_DECODE
 
 }  // namespace cdattn
