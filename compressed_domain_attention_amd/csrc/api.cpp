@@ -334,8 +334,6 @@ int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
   a.counters = reinterpret_cast<uint32_t *>(ws);
   a.part_ml = reinterpret_cast<float *>(ws + p.off_ml);
   a.part_acc = reinterpret_cast<float *>(ws + p.off_acc);
-  for (int r = 0; r < k->block; ++r)
-    for (int j = 0; j < p.SP; ++j) a.A[r * p.SP + j] = j < k->keep ? (float)basis_entry(k->block, j, r) : 0.0f;
   (void)hipGetLastError();
   const int lr = launch_decode(k->head_dim, p.GS, p.SP, k->fmt, v->fmt, a, p.n_wg, stream);
   if (lr < 0) return CODEC_ERR_UNSUPPORTED;

@@ -9,32 +9,35 @@
 //
 // MI355X design.  One workgroup = one (b, kv head, query group, split) with
 // all GS query heads of the group, so each coefficient byte is read from HBM
-// once and converted once.  8 waves per workgroup, one workgroup per CU.
+// once.  kDecodeWaves waves per workgroup, one workgroup per CU.
 //  * Tiles of TR coefficient rows (about 8 KB of K+V) stream through
-//    registers with 16-byte buffer loads per lane; each wave keeps the next
-//    tile's loads in flight while it computes the current one (two register
-//    buffers).  Buffer loads past a tile's end return zeros, so edges need
-//    no branches.
-//  * K phase: lane = 16 consecutive head_dim elements of one row; int8 codes
-//    become exact fp16 (byte permute + one packed fp16 subtract) and are
-//    dotted with the query in fp16 pairs accumulating in fp32
-//    (v_dot2c_f32_f16); the row sum is a DPP butterfly inside 16-lane rows.
-//    The query is pre-scaled by a power of two into fp16 range (exact for
-//    every bf16 value within 2^28 of the largest |q|).
-//  * Logit phase: lane = (block, head, 8 of the R tokens); the R x S basis A
-//    sits in LDS; logits stay in registers; base-2 softmax with log2(e)
-//    folded into the scale; one rescale of the accumulators per tile.
-//  * V phase: lane = EV consecutive head_dim elements of one row; the value
-//    weight w * vscale multiplies int8 codes converted by SDWA; fp32 FMAs
-//    into per-lane accumulators, reduced across lanes once per wave.
-//  * Waves merge in LDS; the workgroup publishes its partial with
-//    device-scope stores, waits for them, and bumps a per-(b, h, group)
-//    counter; the last workgroup to arrive combines all splits with
-//    device-scope loads and writes the output (no second launch, and no L2
-//    write-back or invalidate per workgroup).
+//    registers with 16-byte buffer loads; a wave requests its next tile's K
+//    rows as soon as its K phase is done and the V rows after the V phase.
+//    Loads past a tile's end return zeros, so edges need no branches.
+//  * int8 K rows: s = codes . q on v_mfma_i32_16x16x64_i8, the bf16 query
+//    split into three signed-byte digits of a 22-bit fixed-point value per
+//    head (exact int32 sums, recombined in fp32).  bf16 / fp32 K rows: fp16
+//    query pairs against the rows on the VALU.
+//  * Logits: z = A s and w = p A on v_mfma_f32_16x16x4_f32 (items = (block,
+//    head) columns), base-2 online softmax with log2(e) folded into the
+//    scale, running max per head.
+//  * int8 V rows: the tile goes to LDS (16-byte chunks XOR-swizzled by row),
+//    ds_read_b64_tr_b8 hands out the B operand of v_mfma_i32_16x16x32_i8,
+//    and the weights w * vscale per head and 32-row chunk become three
+//    signed-byte digits of a 22-bit fixed-point value (A operand).  bf16 /
+//    fp32 V rows: fp32 FMAs on the VALU.
+//  * The raw tail (fewer than R tokens) runs on the VALU paths in one wave.
+//  * Waves merge in LDS in a fixed order; the workgroup publishes its
+//    partial with device-scope stores, waits for them, and bumps a per-(b,
+//    h, group) counter; the last workgroup to arrive combines all splits
+//    with one round of device-scope loads and writes the output (no second
+//    launch, and no L2 write-back or invalidate per workgroup).  A split
+//    that is alone writes the output directly.
 #pragma once
 
 #include <math.h>
+
+#include <type_traits>
 
 #include "internal.h"
 
@@ -76,34 +79,12 @@ __device__ __forceinline__ float strided(float v) {
   return v;
 }
 
-// Reduce over the LR adjacent lanes of an item (LR in {1, 2, 4}), then over
-// the items of the same head (lanes congruent modulo GS * LR).
-template <int GS, bool MAX>
-__device__ __forceinline__ float head_reduce(float v, int LR) {
-  if (LR == 1) return strided<GS, MAX>(v);
-  if (LR == 2) return strided<(GS * 2 < 64 ? GS * 2 : 64), MAX>(group_red<2, MAX>(v));
-  return strided<(GS * 4 < 64 ? GS * 4 : 64), MAX>(group_red<4, MAX>(v));
-}
-
 __device__ __forceinline__ float readlane(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// Four int8 codes -> two exact fp16 pairs: (c ^ 0x80) is c + 128 as a byte;
-// fp16 0x64XX = 1024 + byte, and subtracting 1152 leaves c exactly.
-__device__ __forceinline__ void i8x4_to_h2(uint32_t w, h2 &lo, h2 &hi) {
-  const uint32_t x = w ^ 0x80808080u;
-  const uint32_t p0 = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
-  const uint32_t p1 = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
-  const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  lo = __builtin_bit_cast(h2, p0) - bias;
-  hi = __builtin_bit_cast(h2, p1) - bias;
-}
-
-__device__ __forceinline__ float i8b(uint32_t w, int k) { return (float)(int8_t)(w >> (8 * k)); }
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -143,33 +124,57 @@ constexpr int ebytes(int F) { return F == I8 ? 1 : (F == BF16 ? 2 : 4); }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
 template <int D, int GS, int KF, int VF>
 struct Cfg {
   static constexpr int W = kDecodeWaves;
+  static constexpr int NBUF = 1;                     // register buffers (tiles in flight) per wave
   static constexpr int EBK = ebytes(KF), EBV = ebytes(VF);
   static constexpr int TR = decode_tile_rows(D, KF, VF);   // rows per tile (K+V ~ 8 KB)
-  static constexpr int LK = D / 16;                     // lanes per K row (16 elements each)
-  static constexpr int RK = 64 / LK;                    // K rows per step
-  static constexpr int KSTEPS = (TR + RK - 1) / RK;
-  static constexpr int KQ = EBK;                        // uint4 per lane per K step
-  static constexpr int EV = cmin(16, 64 / GS);          // V elements per lane
-  static constexpr int LV = D / EV;                     // lanes per V row
-  static constexpr int RV = 64 / LV;                    // V rows per step
-  static constexpr int VSTEPS = (TR + RV - 1) / RV;
-  static constexpr int VDW = EV * EBV / 4;              // dwords per lane per V step
+  static constexpr int SWR = cmax(cdiv(TR, 32) * 32, kMaxR);   // rows of the per-head scratch
+  static constexpr bool KM = KF == I8;                  // key rows through int8 MFMA
+  static constexpr bool VM = VF == I8;                  // value rows through int8 MFMA
+  // VALU key path: lane = 16 consecutive elements of one row
+  static constexpr int LK = D / 16, RK = 64 / LK, KSTEPS = cdiv(TR, RK), KQ = EBK;
+  // MFMA key path: 16-row groups x 64-element k steps; N blocks of 4 heads x 4 limb slots
+  static constexpr int RG = cdiv(TR, 16), KK = D / 64, NBN = cdiv(GS, 4);
+  // VALU value path: lane = EV consecutive elements of one row
+  static constexpr int EV = cmin(16, 64 / GS), LV = D / EV, RV = 64 / LV;
+  static constexpr int VSTEPS = cdiv(TR, RV), VDW = EV * EBV / 4;
+  // MFMA value path: tile staged in LDS; 32-row chunks; M blocks of 4 heads; N blocks of 16 columns
+  static constexpr int VQ = cdiv(TR * D * EBV, 1024), CH = SWR / 32, MB = cdiv(GS, 4), NBV = D / 16;
 };
 
-// Registers of one in-flight tile.
-template <int D, int GS, int KF, int VF>
-struct TileBuf {
+// ---------------------------------------------------------------- buffers --
+template <int D, int GS, int KF, int VF, bool M = Cfg<D, GS, KF, VF>::KM>
+struct KBuf {                 // VALU layout (bf16 / fp32 rows)
   using C = Cfg<D, GS, KF, VF>;
   uint4 k[C::KSTEPS][C::KQ];
-  float ks[C::KSTEPS];
+};
+template <int D, int GS, int KF, int VF>
+struct KBuf<D, GS, KF, VF, true> {   // MFMA layout: row 16*rg + lane%16, bytes 64*kk + 16*(lane/16) ..
+  using C = Cfg<D, GS, KF, VF>;
+  uint4 k[C::RG][C::KK];
+  float ks;                   // scale of row `lane` of the tile
+};
+template <int D, int GS, int KF, int VF, bool M = Cfg<D, GS, KF, VF>::VM>
+struct VBuf {                 // VALU layout (bf16 / fp32 rows)
+  using C = Cfg<D, GS, KF, VF>;
   uint32_t v[C::VSTEPS][C::VDW];
-  float vs[C::VSTEPS];
+};
+template <int D, int GS, int KF, int VF>
+struct VBuf<D, GS, KF, VF, true> {   // contiguous 16-byte chunks, copied to LDS before use
+  using C = Cfg<D, GS, KF, VF>;
+  uint4 v[C::VQ];
+  float vs;                   // scale of row `lane` of the tile
+};
+template <int D, int GS, int KF, int VF>
+struct TileBuf {
+  KBuf<D, GS, KF, VF> k;
+  VBuf<D, GS, KF, VF> v;
 };
 
-// Where a tile lives and how many rows it has.
 struct TileRef {
   const char *k;
   const char *v;
@@ -182,16 +187,20 @@ template <int D, int GS, int KF, int VF>
 __device__ __forceinline__ void issue_k(TileBuf<D, GS, KF, VF> &B, const TileRef &T, int lane) {
   using C = Cfg<D, GS, KF, VF>;
   const rsrc_t rk = make_rsrc(T.k, (uint32_t)T.nrows * D * C::EBK);
-  const int rrk = lane / C::LK, ck = lane % C::LK;
-  const uint32_t vk = (uint32_t)(rrk * D + ck * 16) * C::EBK;
+  if constexpr (C::KM) {
+    const uint32_t vk = (uint32_t)((lane % 16) * D + 16 * (lane / 16));
 #pragma unroll
-  for (int s = 0; s < C::KSTEPS; ++s)
+    for (int rg = 0; rg < C::RG; ++rg)
 #pragma unroll
-    for (int k = 0; k < C::KQ; ++k) B.k[s][k] = bload128(rk, vk + 16 * k, s * C::RK * D * C::EBK);
-  if constexpr (KF == I8) {
-    const rsrc_t rs = make_rsrc(T.ks, (uint32_t)T.nrows * 4);
+      for (int kk = 0; kk < C::KK; ++kk) B.k.k[rg][kk] = bload128(rk, vk + 64 * kk, rg * 16 * D);
+    B.k.ks = bloadf(make_rsrc(T.ks, (uint32_t)T.nrows * 4), 4 * lane, 0);
+  } else {
+    const int rrk = lane / C::LK, ck = lane % C::LK;
+    const uint32_t vk = (uint32_t)(rrk * D + ck * 16) * C::EBK;
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) B.ks[s] = bloadf(rs, (uint32_t)rrk * 4, s * C::RK * 4);
+    for (int s = 0; s < C::KSTEPS; ++s)
+#pragma unroll
+      for (int k = 0; k < C::KQ; ++k) B.k.k[s][k] = bload128(rk, vk + 16 * k, s * C::RK * D * C::EBK);
   }
 }
 
@@ -199,25 +208,26 @@ template <int D, int GS, int KF, int VF>
 __device__ __forceinline__ void issue_v(TileBuf<D, GS, KF, VF> &B, const TileRef &T, int lane) {
   using C = Cfg<D, GS, KF, VF>;
   const rsrc_t rv = make_rsrc(T.v, (uint32_t)T.nrows * D * C::EBV);
-  const int rrv = lane / C::LV, cv = lane % C::LV;
-  const uint32_t vv = (uint32_t)(rrv * D + cv * C::EV) * C::EBV;
+  if constexpr (C::VM) {
 #pragma unroll
-  for (int s = 0; s < C::VSTEPS; ++s) {
-    if constexpr (C::VDW % 4 == 0) {
+    for (int c = 0; c < C::VQ; ++c) B.v.v[c] = bload128(rv, 16 * lane, 1024 * c);
+    B.v.vs = bloadf(make_rsrc(T.vs, (uint32_t)T.nrows * 4), 4 * lane, 0);
+  } else {
+    const int rrv = lane / C::LV, cv = lane % C::LV;
+    const uint32_t vv = (uint32_t)(rrv * D + cv * C::EV) * C::EBV;
 #pragma unroll
-      for (int k = 0; k < C::VDW / 4; ++k) {
-        const uint4 t = bload128(rv, vv + 16 * k, s * C::RV * D * C::EBV);
-        B.v[s][4 * k] = t.x; B.v[s][4 * k + 1] = t.y; B.v[s][4 * k + 2] = t.z; B.v[s][4 * k + 3] = t.w;
+    for (int s = 0; s < C::VSTEPS; ++s) {
+      if constexpr (C::VDW % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < C::VDW / 4; ++k) {
+          const uint4 t = bload128(rv, vv + 16 * k, s * C::RV * D * C::EBV);
+          B.v.v[s][4 * k] = t.x; B.v.v[s][4 * k + 1] = t.y; B.v.v[s][4 * k + 2] = t.z; B.v.v[s][4 * k + 3] = t.w;
+        }
+      } else {
+        const uint2 t = bload64(rv, vv, s * C::RV * D * C::EBV);
+        B.v.v[s][0] = t.x; B.v.v[s][1] = t.y;
       }
-    } else {
-      const uint2 t = bload64(rv, vv, s * C::RV * D * C::EBV);
-      B.v[s][0] = t.x; B.v[s][1] = t.y;
     }
-  }
-  if constexpr (VF == I8) {
-    const rsrc_t rs = make_rsrc(T.vs, (uint32_t)T.nrows * 4);
-#pragma unroll
-    for (int s = 0; s < C::VSTEPS; ++s) B.vs[s] = bloadf(rs, (uint32_t)rrv * 4, s * C::RV * 4);
   }
 }
 
@@ -227,13 +237,319 @@ __device__ __forceinline__ void issue(TileBuf<D, GS, KF, VF> &B, const TileRef &
   issue_v(B, T, lane);
 }
 
-// ----------------------------------------------------------------- K phase --
-// s[row][g] = cq[g] * kscale[row] * sum_d k[row][d] * q[g][d].  Format F, 16
-// elements per lane held in F's bytes (KQ uint4).
-template <int D, int GS, int F, int STEPS, int KQ>
-__device__ __forceinline__ void kcompute(const uint4 (&kb)[STEPS][KQ], const float (&ks)[STEPS], int nrows,
-                                         int lane, h2 (&qh)[GS][8], const float (&cq)[GS], float *sw,
-                                         int row_base = 0) {
+// --------------------------------------------------------- int8 digits --
+// A value x in [-2^22, 2^22] as balanced base-256 digits x = d0 + 256 d1 +
+// 65536 d2 (d0, d1 in [-128, 127], d2 in [-64, 64]), so int8 x int8 products
+// summed in int32 reproduce x exactly.  With u = x + 0x808080 (positive),
+// digit k is byte k of u minus 128; as an int8 bit pattern that is byte k of
+// u with its top bit flipped.  biased() returns u; byte 3 (digit 3) is a
+// don't-care slot, multiplied by zero wherever it is used.
+__device__ __forceinline__ uint32_t biased(float x) { return (uint32_t)((int)__builtin_rintf(x) + 0x808080); }
+
+// Bytes `which` of four biased values, packed and turned into int8 digits.
+__device__ __forceinline__ uint32_t pack_digits(uint32_t u0, uint32_t u1, uint32_t u2, uint32_t u3, int which) {
+  const uint32_t sh = 8u * (uint32_t)which;
+  const uint32_t p = __builtin_amdgcn_ubfe(u0, sh, 8) | (__builtin_amdgcn_ubfe(u1, sh, 8) << 8) |
+                     (__builtin_amdgcn_ubfe(u2, sh, 8) << 16) | (__builtin_amdgcn_ubfe(u3, sh, 8) << 24);
+  return p ^ 0x80808080u;
+}
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------ K phase (MFMA) --
+// Query of the key MFMA: B operand of v_mfma_i32_16x16x64_i8 for k step kk
+// and N block nb: column n = lane % 16 holds head 4*nb + n/4, digit n % 4 of
+// the query scaled to 22-bit integers; rows (bytes) are the same head_dim
+// elements the codes of this lane hold.  cqq = scale * log2(e) / up.
+// Converted once per workgroup (wave nb converts N block nb) and handed to
+// every wave through LDS: the raw loads are issued before the first tile's,
+// so the conversion does not wait for tile data.
+template <int D, int GS>
+struct QStageMfma {
+  static constexpr int KK = D / 64, NBN = cdiv(GS, 4);
+  static constexpr int BYTES = KK * NBN * 64 * 16 + NBN * 16;
+  static constexpr int WAVES = NBN;
+  uint4 raw[KK][2];
+  __device__ __forceinline__ void load(const DecodeArgs &a, int64_t b, int hq0, int nb, int lane) {
+    const int n = lane % 16, G = lane / 16, g = 4 * nb + n / 4;
+    const int gl = g < GS ? g : 0;    // columns of absent heads read a live one and are zeroed below
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + b * a.q_sb + (int64_t)(hq0 + gl) * a.q_sh + 64 * kk + 16 * G);
+      raw[kk][0] = qp[0];
+      raw[kk][1] = qp[1];
+    }
+  }
+  __device__ __forceinline__ void convert(const DecodeArgs &a, int nb, int lane, char *sq) const {
+    const int n = lane % 16, g = 4 * nb + n / 4;
+    const bool live = g < GS;
+    float qf[KK][16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint32_t wv[8] = {raw[kk][0].x, raw[kk][0].y, raw[kk][0].z, raw[kk][0].w,
+                              raw[kk][1].x, raw[kk][1].y, raw[kk][1].z, raw[kk][1].w};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        qf[kk][2 * t] = live ? bf16lo(wv[t]) : 0.0f;
+        qf[kk][2 * t + 1] = live ? bf16hi(wv[t]) : 0.0f;
+        amax = fmaxf(amax, fmaxf(fabsf(qf[kk][2 * t]), fabsf(qf[kk][2 * t + 1])));
+      }
+    }
+    amax = fmaxf(amax, xshfl(amax, 16));
+    amax = fmaxf(amax, xshfl(amax, 32));
+    int E = 0;
+    if (amax > 0.0f) frexpf(amax, &E);
+    const float up = ldexpf(1.0f, 22 - E);
+    const int which = n % 4;
+    uint4 *dst = reinterpret_cast<uint4 *>(sq);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      uint32_t u[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) u[e] = biased(qf[kk][e] * up);
+      dst[(kk * NBN + nb) * 64 + lane] =
+          make_uint4(pack_digits(u[0], u[1], u[2], u[3], which), pack_digits(u[4], u[5], u[6], u[7], which),
+                     pack_digits(u[8], u[9], u[10], u[11], which), pack_digits(u[12], u[13], u[14], u[15], which));
+    }
+    // the scale is per head: the lane of digit 0 of head 4 nb + n/4 in row 0 stores it
+    if (lane < 16 && which == 0)
+      reinterpret_cast<float *>(sq + KK * NBN * 1024)[4 * nb + n / 4] = a.qk_scale * ldexpf(1.0f, E - 22);
+  }
+  __device__ static __forceinline__ void read(const char *sq, int lane, uint4 (&qB)[KK][NBN], float (&cqq)[NBN]) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < NBN; ++nb) qB[kk][nb] = reinterpret_cast<const uint4 *>(sq)[(kk * NBN + nb) * 64 + lane];
+#pragma unroll
+    for (int nb = 0; nb < NBN; ++nb) cqq[nb] = reinterpret_cast<const float *>(sq + KK * NBN * 1024)[4 * nb + (lane % 16) / 4];
+  }
+};
+
+// s[g][row] = cqq[g] * kscale[row] * sum_d code[row][d] * qint[g][d] for the
+// tile's rows; the int32 MFMA sums are exact, digits are recombined in fp32.
+template <int D, int GS, int SWR, int KF, int VF>
+__device__ __forceinline__ void kcompute_mfma(const KBuf<D, GS, KF, VF, true> &kb, int lane,
+                                              const uint4 (&qB)[D / 64][cdiv(GS, 4)], const float (&cqq)[cdiv(GS, 4)],
+                                              float *sw, const float *sks) {
+  using C = Cfg<D, GS, KF, VF>;
+  const int n = lane % 16, G = lane / 16, which = n % 4;
+  const float wdig = which == 0 ? 1.0f : (which == 1 ? 256.0f : (which == 2 ? 65536.0f : 0.0f));
+#pragma unroll
+  for (int rg = 0; rg < C::RG; ++rg) {
+#pragma unroll
+    for (int nb = 0; nb < C::NBN; ++nb) {
+      v4i acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk)
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, kb.k[rg][kk]),
+                                                     __builtin_bit_cast(v4i, qB[kk][nb]), acc, 0, 0, 0);
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = (float)acc[i] * wdig;
+        v[i] += dpp<0xB1>(v[i]);
+        v[i] += dpp<0x4E>(v[i]);
+      }
+      const int g = 4 * nb + n / 4;
+      if (which == 0 && g < GS) {
+        const float c = cqq[nb];
+        const float4 ks = *reinterpret_cast<const float4 *>(sks + 16 * rg + 4 * G);
+        *reinterpret_cast<float4 *>(sw + g * SWR + 16 * rg + 4 * G) =
+            make_float4(v[0] * ks.x * c, v[1] * ks.y * c, v[2] * ks.z * c, v[3] * ks.w * c);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------ V phase (MFMA) --
+// The tile's int8 value rows go to LDS row-major with 16-byte chunks XOR
+// swizzled by row, so the transpose reads below hit distinct banks.
+template <int D>
+__device__ __forceinline__ int vlds_off(int row, int chunk16) {
+  constexpr int NC = D / 16, SW = NC < 8 ? NC : 8;
+  return row * D + ((chunk16 ^ (row % SW)) * 16);
+}
+
+// acc[mb][nb] (lane: head 4*mb + lane/16, column 16*nb + lane%16) +=
+//   sum over the tile's rows of w[g][row] * vscale[row] * code[row][col].
+// Per 32-row chunk and M block: the weights of 4 heads become 22-bit integers
+// (scale per head and chunk) split in three signed bytes, the A operand of
+// v_mfma_i32_16x16x32_i8 (row m = head*4 + digit); the value codes come from
+// LDS through ds_read_b64_tr_b8, which hands lane i of a 16-lane group byte
+// (i % 8) of the 8 bytes addressed by lane 2j + i/8, j = 0..7: with lane k
+// of group G pointing at row 8G + k/2, columns 8*(k%2) .. of the block, lane
+// i receives column i of rows 8G .. 8G+7, the B operand of the MFMA.
+template <int D, int GS, int SWR, int KF, int VF>
+__device__ __forceinline__ void vcompute_mfma(const VBuf<D, GS, KF, VF, true> &vb, int nrows, int lane,
+                                              const float *sw, char *vl, float *svs,
+                                              float (&acc)[cdiv(GS, 4)][D / 16]) {
+  using C = Cfg<D, GS, KF, VF>;
+#pragma unroll
+  for (int c = 0; c < C::VQ; ++c) {
+    const int q = lane + 64 * c;            // 16-byte chunk of the tile
+    const int row = q / (D / 16), ch16 = q % (D / 16);
+    if (row < SWR) *reinterpret_cast<uint4 *>(vl + vlds_off<D>(row, ch16)) = vb.v[c];
+  }
+  svs[lane] = vb.vs;
+  wave_lds_sync();
+  const int m = lane % 16, G = lane / 16;
+  const int which = m % 4;
+#pragma unroll
+  for (int ch = 0; ch < C::CH; ++ch) {
+    const float4 vs0 = *reinterpret_cast<const float4 *>(svs + 32 * ch + 8 * G);
+    const float4 vs1 = *reinterpret_cast<const float4 *>(svs + 32 * ch + 8 * G + 4);
+    const float vsj[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
+    const int r0 = 32 * ch + 8 * G;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      const int g = 4 * mb + m / 4;
+      float w[8];
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = g < GS && r0 + j < nrows;
+        w[j] = ok ? sw[g * SWR + r0 + j] * vsj[j] : 0.0f;
+        amax = fmaxf(amax, fabsf(w[j]));
+      }
+      amax = fmaxf(amax, xshfl(amax, 16));
+      amax = fmaxf(amax, xshfl(amax, 32));
+      int E = 0;
+      if (amax > 0.0f) frexpf(amax, &E);
+      const float up = ldexpf(1.0f, 22 - E);
+      uint32_t u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) u[j] = biased(w[j] * up);
+      const long A = (long)pack_digits(u[0], u[1], u[2], u[3], which) |
+                     ((long)pack_digits(u[4], u[5], u[6], u[7], which) << 32);
+      // per-head scale of this chunk for the output layout (head = 4*mb + lane/16)
+      const float down = ldexpf(1.0f, E - 22);
+      const float d0 = readlane(down, 0), d1 = readlane(down, 4), d2 = readlane(down, 8), d3 = readlane(down, 12);
+      const float dn = G == 0 ? d0 : (G == 1 ? d1 : (G == 2 ? d2 : d3));
+      const int k = lane % 16;
+      const int trow = 32 * ch + 8 * G + k / 2;
+#pragma unroll
+      for (int nb = 0; nb < C::NBV; ++nb) {
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        const v2i bt = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i *)(vl + vlds_off<D>(trow, nb) + 8 * (k % 2)));
+        v4i z = {0, 0, 0, 0};
+        const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, __builtin_bit_cast(long, bt), z, 0, 0, 0);
+        acc[mb][nb] = fmaf(dn, ((float)c[0] + 256.0f * (float)c[1]) + 65536.0f * (float)c[2], acc[mb][nb]);
+      }
+    }
+  }
+  wave_lds_sync();
+}
+
+template <int GS, int MBK, int NBK>
+__device__ __forceinline__ void rescale_mfma(float (&acc)[MBK][NBK], const float (&alpha)[GS], int lane) {
+  bool moved = false;
+#pragma unroll
+  for (int g = 0; g < GS; ++g) moved |= alpha[g] != 1.0f;
+  if (!moved) return;
+  const int G = lane / 16;
+#pragma unroll
+  for (int mb = 0; mb < MBK; ++mb) {
+    float al = 1.0f;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      if (4 * mb + h < GS && G == h) al = alpha[4 * mb + h];
+#pragma unroll
+    for (int nb = 0; nb < NBK; ++nb) acc[mb][nb] *= al;
+  }
+}
+
+// ------------------------------------------------------- VALU query setup --
+// fp16 pairs of the lane's 16 key elements (lane % (D/16) picks them),
+// pre-scaled per head by a power of two into fp16 range.
+template <int D, int GS>
+__device__ __forceinline__ void setup_q_valu(const DecodeArgs &a, int64_t b, int hq0, int lane, h2 (&qh)[GS][8],
+                                             float (&cq)[GS]) {
+  constexpr int LK = D / 16;
+  const int d0 = (lane % LK) * 16;
+#pragma unroll
+  for (int g = 0; g < GS; ++g) {
+    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + b * a.q_sb + (int64_t)(hq0 + g) * a.q_sh + d0);
+    const uint4 q0 = qp[0], q1 = qp[1];
+    const uint32_t wv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    float qf[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      qf[2 * t] = bf16lo(wv[t]);
+      qf[2 * t + 1] = bf16hi(wv[t]);
+      amax = fmaxf(amax, fmaxf(fabsf(qf[2 * t]), fabsf(qf[2 * t + 1])));
+    }
+    amax = group_red<LK, true>(amax);
+    int E = 0;
+    if (amax > 0.0f) frexpf(amax, &E);
+    const float up = ldexpf(1.0f, 15 - E);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qh[g][t] = h2{(_Float16)(qf[2 * t] * up), (_Float16)(qf[2 * t + 1] * up)};
+    cq[g] = a.qk_scale * ldexpf(1.0f, E - 15);
+  }
+}
+
+// The same, converted once per workgroup (wave g converts head g for the
+// D/16 lane positions) and handed to every wave through LDS.
+template <int D, int GS>
+struct QStageValu {
+  static constexpr int LK = D / 16;
+  static constexpr int BYTES = GS * LK * 32 + cdiv(GS * 4, 16) * 16;
+  static constexpr int WAVES = GS;
+  uint4 raw[2];
+  __device__ __forceinline__ void load(const DecodeArgs &a, int64_t b, int hq0, int g, int lane) {
+    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + b * a.q_sb + (int64_t)(hq0 + g) * a.q_sh + (lane % LK) * 16);
+    raw[0] = qp[0];
+    raw[1] = qp[1];
+  }
+  __device__ __forceinline__ void convert(const DecodeArgs &a, int g, int lane, char *sq) const {
+    const uint32_t wv[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+    float qf[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      qf[2 * t] = bf16lo(wv[t]);
+      qf[2 * t + 1] = bf16hi(wv[t]);
+      amax = fmaxf(amax, fmaxf(fabsf(qf[2 * t]), fabsf(qf[2 * t + 1])));
+    }
+    amax = group_red<LK, true>(amax);
+    int E = 0;
+    if (amax > 0.0f) frexpf(amax, &E);
+    const float up = ldexpf(1.0f, 15 - E);
+    h2 qh[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qh[t] = h2{(_Float16)(qf[2 * t] * up), (_Float16)(qf[2 * t + 1] * up)};
+    if (lane < LK) {
+      uint4 *dst = reinterpret_cast<uint4 *>(sq) + (g * LK + lane) * 2;
+      dst[0] = make_uint4(__builtin_bit_cast(uint32_t, qh[0]), __builtin_bit_cast(uint32_t, qh[1]),
+                          __builtin_bit_cast(uint32_t, qh[2]), __builtin_bit_cast(uint32_t, qh[3]));
+      dst[1] = make_uint4(__builtin_bit_cast(uint32_t, qh[4]), __builtin_bit_cast(uint32_t, qh[5]),
+                          __builtin_bit_cast(uint32_t, qh[6]), __builtin_bit_cast(uint32_t, qh[7]));
+    }
+    if (lane == 0) reinterpret_cast<float *>(sq + GS * LK * 32)[g] = a.qk_scale * ldexpf(1.0f, E - 15);
+  }
+  __device__ static __forceinline__ void read(const char *sq, int lane, h2 (&qh)[GS][8], float (&cq)[GS]) {
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(sq) + (g * LK + lane % LK) * 2;
+      const uint4 x = src[0], y = src[1];
+      const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) qh[g][t] = __builtin_bit_cast(h2, w[t]);
+      cq[g] = reinterpret_cast<const float *>(sq + GS * LK * 32)[g];
+    }
+  }
+};
+// ------------------------------------------------------- K phase (VALU) --
+// bf16 / fp32 key rows and the raw tail.
+// s[g][row] = cq[g] * sum_d k[row][d] * q[g][d]; 16 elements per lane held in
+// F's bytes (KQ uint4), the query in pre-scaled fp16 pairs.
+template <int D, int GS, int SWR, int F, int STEPS, int KQ>
+__device__ __forceinline__ void kcompute(const uint4 (&kb)[STEPS][KQ], int nrows, int lane, h2 (&qh)[GS][8],
+                                         const float (&cq)[GS], float *sw, int row_base = 0) {
+  static_assert(F != I8, "int8 key rows take the MFMA path");
   constexpr int LK = D / 16, RK = 64 / LK;
   const int rr = lane / LK, c = lane % LK;
 #pragma unroll
@@ -243,63 +559,51 @@ __device__ __forceinline__ void kcompute(const uint4 (&kb)[STEPS][KQ], const flo
     float dot[GS];
 #pragma unroll
     for (int g = 0; g < GS; ++g) dot[g] = 0.0f;
-    if constexpr (F == I8) {
-      const uint32_t wv[4] = {kb[s][0].x, kb[s][0].y, kb[s][0].z, kb[s][0].w};
+    opaque(qh);   // keep the fp16 -> fp32 conversion inside v_fma_mix
+    float kf[16];
+    if constexpr (F == BF16) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        h2 lo, hi;
-        i8x4_to_h2(wv[q4], lo, hi);
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t wv[4] = {kb[s][k].x, kb[s][k].y, kb[s][k].z, kb[s][k].w};
 #pragma unroll
-        for (int g = 0; g < GS; ++g) {
-          dot[g] = __builtin_amdgcn_fdot2(lo, qh[g][2 * q4], dot[g], false);
-          dot[g] = __builtin_amdgcn_fdot2(hi, qh[g][2 * q4 + 1], dot[g], false);
+        for (int t = 0; t < 4; ++t) {
+          kf[8 * k + 2 * t] = bf16lo(wv[t]);
+          kf[8 * k + 2 * t + 1] = bf16hi(wv[t]);
         }
       }
     } else {
-      opaque(qh);   // keep the fp16 -> fp32 conversion inside v_fma_mix
-      float kf[16];
-      if constexpr (F == BF16) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const uint32_t wv[4] = {kb[s][k].x, kb[s][k].y, kb[s][k].z, kb[s][k].w};
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            kf[8 * k + 2 * t] = bf16lo(wv[t]);
-            kf[8 * k + 2 * t + 1] = bf16hi(wv[t]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          kf[4 * k + 0] = __uint_as_float(kb[s][k].x);
-          kf[4 * k + 1] = __uint_as_float(kb[s][k].y);
-          kf[4 * k + 2] = __uint_as_float(kb[s][k].z);
-          kf[4 * k + 3] = __uint_as_float(kb[s][k].w);
-        }
+      for (int k = 0; k < 4; ++k) {
+        kf[4 * k + 0] = __uint_as_float(kb[s][k].x);
+        kf[4 * k + 1] = __uint_as_float(kb[s][k].y);
+        kf[4 * k + 2] = __uint_as_float(kb[s][k].z);
+        kf[4 * k + 3] = __uint_as_float(kb[s][k].w);
       }
-#pragma unroll
-      for (int g = 0; g < GS; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          dot[g] = fmaf((float)qh[g][e].x, kf[2 * e], dot[g]);
-          dot[g] = fmaf((float)qh[g][e].y, kf[2 * e + 1], dot[g]);
-        }
     }
+#pragma unroll
+    for (int g = 0; g < GS; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dot[g] = fmaf((float)qh[g][e].x, kf[2 * e], dot[g]);
+        dot[g] = fmaf((float)qh[g][e].y, kf[2 * e + 1], dot[g]);
+      }
 #pragma unroll
     for (int g = 0; g < GS; ++g) dot[g] = group_red<LK, false>(dot[g]);
     if (c == 0 && row < nrows) {
 #pragma unroll
-      for (int g = 0; g < GS; ++g) sw[row * GS + g] = dot[g] * (F == I8 ? ks[s] * cq[g] : cq[g]);
+      for (int g = 0; g < GS; ++g) sw[g * SWR + row] = dot[g] * cq[g];
     }
   }
 }
 
-// ----------------------------------------------------------------- V phase --
-// acc[g][e] += sum over rows of w[row][g] * vscale[row] * v[row][c*EV + e].
+// ------------------------------------------------------- V phase (VALU) --
+// bf16 / fp32 value rows and the raw tail.
+// acc[g][e] += sum over rows of w[g][row] * v[row][c*EV + e].
 // Rows past nrows hold zero data (buffer range) and finite stale weights.
-template <int D, int GS, int F, int STEPS, int VDW, int EV>
-__device__ __forceinline__ void vcompute(const uint32_t (&vb)[STEPS][VDW], const float (&vs)[STEPS], int nrows,
-                                         int lane, const float *sw, float (&acc)[GS][EV], int row_base = 0) {
+template <int D, int GS, int SWR, int F, int STEPS, int VDW, int EV>
+__device__ __forceinline__ void vcompute(const uint32_t (&vb)[STEPS][VDW], int nrows, int lane, const float *sw,
+                                         float (&acc)[GS][EV], int row_base = 0) {
+  static_assert(F != I8, "int8 value rows take the MFMA path");
   constexpr int LV = D / EV, RV = 64 / LV;
   const int rr = lane / LV;
 #pragma unroll
@@ -308,18 +612,9 @@ __device__ __forceinline__ void vcompute(const uint32_t (&vb)[STEPS][VDW], const
     const int row = row_base + s * RV + rr;
     float w[GS];
 #pragma unroll
-    for (int g = 0; g < GS; ++g) w[g] = sw[row * GS + g];
-    if constexpr (F == I8) {
-#pragma unroll
-      for (int g = 0; g < GS; ++g) w[g] *= vs[s];
-    }
+    for (int g = 0; g < GS; ++g) w[g] = sw[g * SWR + row];
     float v[EV];
-    if constexpr (F == I8) {
-#pragma unroll
-      for (int k = 0; k < VDW; ++k)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) v[4 * k + t] = i8b(vb[s][k], t);
-    } else if constexpr (F == BF16) {
+    if constexpr (F == BF16) {
 #pragma unroll
       for (int k = 0; k < VDW; ++k) { v[2 * k] = bf16lo(vb[s][k]); v[2 * k + 1] = bf16hi(vb[s][k]); }
     } else {
@@ -334,144 +629,127 @@ __device__ __forceinline__ void vcompute(const uint32_t (&vb)[STEPS][VDW], const
 }
 
 // ------------------------------------------------------------ logit phase --
-// Items (block n, head g) laid out as lane = (n * GS + g) * LR + lr, where
-// lr picks tokens lr*8 .. lr*8+7 of the block (LR = ceil(R / 8)).  Updates
-// the running max (uniform m_u, per-lane m_own), the rescale factors and the
-// lane's partial sum; overwrites sw with the value weights w = p A.
-// TAIL: every "block" is one raw token (R = S = 1, A = [1]); the lane layout
-// keeps the LR of the archive so every lane tracks the same head throughout,
-// and only the first lane of an item contributes.
-template <int SP>
-__device__ __forceinline__ void load_row(const float *sA, int r, float (&a)[SP]) {
-  if constexpr (SP % 4 == 0) {
-#pragma unroll
-    for (int j = 0; j < SP; j += 4) {
-      const float4 t = *reinterpret_cast<const float4 *>(sA + r * SP + j);
-      a[j] = t.x; a[j + 1] = t.y; a[j + 2] = t.z; a[j + 3] = t.w;
-    }
-  } else {
-    const float2 t = *reinterpret_cast<const float2 *>(sA + r * SP);
-    a[0] = t.x; a[1] = t.y;
-  }
-}
+// Per tile, with s = the K-phase scores in sw (head-major, row n*S + j of
+// block n): z = A s per (block, head) item, the running max per head,
+// p = 2^(z - max), l += sum p and the value weights w = p A, written back
+// over s.  Both small products run on v_mfma_f32_16x16x4_f32 (lane l holds
+// A[l%16][l/16] and B[l/16][l%16]; result register i of lane l is
+// D[4(l/16)+i][l%16]): items (block n, head g) are the 16 columns of a
+// group, item it = n*GS + g, so the head of a lane is fixed: (l%16) % GS.
+//   z:  M = 16 tokens of a block, K = 4 coefficients per step, N = items.
+//   w:  M = items, K = 4 tokens per step, N = coefficients; step kk takes
+//       token 4(l/16) + kk from the lane that computed it, so p never moves.
+// Tokens past R and items past the tile's blocks are masked.  A first pass
+// takes the max, a second recomputes z (MFMA is cheap) and forms p and w.
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <int GS, int SP, bool TAIL>
-__device__ __forceinline__ void logits(const float *sA, float *sw, int nb, int R, int S, int LR, int lane,
-                                       float (&m_u)[GS], float &m_own, float &l_own, float (&alpha)[GS]) {
-  const int lr = lane % LR;
-  const int g = (lane / LR) % GS;
-  const int per_pass = 64 / LR;                 // items per pass
-  const int items = nb * GS;
-  // tokens of this lane in every block: lr*8 .. lr*8 + rc - 1
-  const int rc = TAIL ? (lr == 0 ? 1 : 0) : ((R - lr * 8) < 8 ? (R - lr * 8) : 8);
-  const bool full = !TAIL && (R % 8 == 0);      // uniform: every lane has 8 tokens
-  float mx = -INFINITY;
-  float zc[8];                                   // logits of the first pass
+template <int SP>
+struct Basis {
+  static constexpr int SK = SP < 4 ? 1 : SP / 4;   // 4-coefficient steps
+  float az[2][SK];   // A operand of z, token tile rt: A[16 rt + l%16][4 kk + l/16]
+  float bw[2][4];    // B operand of w, token tile rt: A[16 rt + 4 (l/16) + kk][l%16]
+  int rt_n;          // token tiles of 16: 1 if R <= 16 else 2
+  __device__ __forceinline__ void load(const float *sA, int R, int S, int lane) {
+    const int lo = lane % 16, hi = lane / 16;
+    rt_n = R > 16 ? 2 : 1;
 #pragma unroll
-  for (int r8 = 0; r8 < 8; ++r8) zc[r8] = -INFINITY;
-  for (int i0 = 0; i0 < items; i0 += per_pass) {
-    const int i = i0 + lane / LR;
-    const bool live = i < items;
-    const int n = live ? i / GS : 0;
-    float sv[SP];
+    for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-    for (int j = 0; j < SP; ++j) sv[j] = (j < S) ? sw[(n * S + j) * GS + g] : 0.0f;
-    if constexpr (TAIL) {
-      if (live && rc) {
-        zc[0] = sv[0];
-        mx = fmaxf(mx, sv[0]);
+      for (int kk = 0; kk < SK; ++kk) {
+        const int r = 16 * rt + lo, j = 4 * kk + hi;
+        az[rt][kk] = (r < R && j < S) ? sA[r * SP + j] : 0.0f;
       }
-    } else if (full) {
 #pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8) {
-        float a[SP];
-        load_row<SP>(sA, lr * 8 + r8, a);
-        float z = 0.0f;
-#pragma unroll
-        for (int j = 0; j < SP; ++j) z = fmaf(a[j], sv[j], z);
-        zc[r8] = z;
-        mx = fmaxf(mx, live ? z : -INFINITY);
-      }
-    } else {
-#pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8) {
-        if (r8 < rc) {
-          float a[SP];
-          load_row<SP>(sA, lr * 8 + r8, a);
-          float z = 0.0f;
-#pragma unroll
-          for (int j = 0; j < SP; ++j) z = fmaf(a[j], sv[j], z);
-          zc[r8] = z;
-          mx = fmaxf(mx, live ? z : -INFINITY);
-        }
+      for (int kk = 0; kk < 4; ++kk) {
+        const int r = 16 * rt + 4 * hi + kk, j = lo;
+        bw[rt][kk] = (r < R && j < S) ? sA[r * SP + j] : 0.0f;
       }
     }
   }
-  mx = head_reduce<GS, true>(mx, LR);
-  const float mnew_own = fmaxf(m_own, mx);
-  const float alpha_own = __builtin_amdgcn_exp2f(m_own - mnew_own);
+  // every token its own block (the raw tail): R = S = 1, A = [1]
+  __device__ __forceinline__ void unit(int lane) {
+    rt_n = 1;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+      for (int kk = 0; kk < SK; ++kk) az[rt][kk] = (rt == 0 && kk == 0 && lane == 0) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) bw[rt][kk] = (rt == 0 && kk == 0 && lane == 0) ? 1.0f : 0.0f;
+    }
+  }
+};
+
+template <int GS, int SP, int SWR>
+__device__ __forceinline__ void logits(const Basis<SP> &A, float *sw, int nb, int R, int S, int lane,
+                                       float (&m_u)[GS], float &m_lane, float &l_lane, float (&alpha)[GS]) {
+  constexpr int SK = Basis<SP>::SK;
+  const int col = lane % 16, hi = lane / 16;
+  const int g = col % GS;
+  const int items = nb * GS;
+  const int ngroups = (items + 15) / 16;
+  auto zgroup = [&](int ig, int rt) {
+    const int it = ig * 16 + col;
+    const bool ok = it < items;
+    const int base = g * SWR + (it / GS) * S;
+    v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < SK; ++kk) {
+      const int j = 4 * kk + hi;
+      const bool live = ok && j < S;
+      const float sv = sw[live ? base + j : 0];
+      z = __builtin_amdgcn_mfma_f32_16x16x4f32(A.az[rt][kk], live ? sv : 0.0f, z, 0, 0, 0);
+    }
+    return z;
+  };
+  float mx = -INFINITY;
+  for (int ig = 0; ig < ngroups; ++ig) {
+    const bool ok = ig * 16 + col < items;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      if (rt < A.rt_n) {
+        const v4f z = zgroup(ig, rt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = (ok && 16 * rt + 4 * hi + i < R) ? fmaxf(mx, z[i]) : mx;
+      }
+    }
+  }
+  mx = strided<GS, true>(mx);
+  const float m_new = fmaxf(m_lane, mx);
+  const float a_lane = m_new == m_lane ? 1.0f : __builtin_amdgcn_exp2f(m_lane - m_new);
 #pragma unroll
   for (int gg = 0; gg < GS; ++gg) {
-    const float mn = fmaxf(m_u[gg], readlane(mx, gg * LR));
-    alpha[gg] = __builtin_amdgcn_exp2f(m_u[gg] - mn);
-    m_u[gg] = mn;
+    alpha[gg] = readlane(a_lane, gg);
+    m_u[gg] = readlane(m_new, gg);
   }
-  m_own = mnew_own;
-  const bool one_pass = items <= per_pass;
+  m_lane = m_new;
   float lsum = 0.0f;
-  for (int i0 = 0; i0 < items; i0 += per_pass) {
-    const int i = i0 + lane / LR;
-    const bool live = i < items;
-    const int n = live ? i / GS : 0;
-    float sv[SP];
-    if (!one_pass) {
+  for (int ig = 0; ig < ngroups; ++ig) {
+    const bool ok = ig * 16 + col < items;
+    v4f w = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < SP; ++j) sv[j] = (j < S) ? sw[(n * S + j) * GS + g] : 0.0f;
-    }
-    float w[SP];
+    for (int rt = 0; rt < 2; ++rt) {
+      if (rt < A.rt_n) {
+        const v4f z = zgroup(ig, rt);
+        float p[4];
 #pragma unroll
-    for (int j = 0; j < SP; ++j) w[j] = 0.0f;
-    if constexpr (TAIL) {
-      if (live && rc) {
-        const float p = __builtin_amdgcn_exp2f((one_pass ? zc[0] : sv[0]) - m_own);
-        lsum += p;
-        w[0] = p;
-      }
-    } else {
-#pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8) {
-        if (full || r8 < rc) {
-          float a[SP];
-          load_row<SP>(sA, lr * 8 + r8, a);
-          float z;
-          if (one_pass) {
-            z = zc[r8];
-          } else {
-            z = 0.0f;
-#pragma unroll
-            for (int j = 0; j < SP; ++j) z = fmaf(a[j], sv[j], z);
-          }
-          const float p = live ? __builtin_amdgcn_exp2f(z - m_own) : 0.0f;
-          lsum += p;
-#pragma unroll
-          for (int j = 0; j < SP; ++j) w[j] = fmaf(p, a[j], w[j]);
+        for (int i = 0; i < 4; ++i) {
+          p[i] = (ok && 16 * rt + 4 * hi + i < R) ? __builtin_amdgcn_exp2f(z[i] - m_new) : 0.0f;
+          lsum += p[i];
         }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) w = __builtin_amdgcn_mfma_f32_16x16x4f32(p[kk], A.bw[rt][kk], w, 0, 0, 0);
       }
     }
-    if (LR == 2) {
+    // lane (hi, j = col) holds w of items ig*16 + 4 hi + i, coefficient j
+    if (col < S) {
 #pragma unroll
-      for (int j = 0; j < SP; ++j) w[j] = group_red<2, false>(w[j]);
-    } else if (LR == 4) {
-#pragma unroll
-      for (int j = 0; j < SP; ++j) w[j] = group_red<4, false>(w[j]);
-    }
-    if (live && lr == 0) {
-#pragma unroll
-      for (int j = 0; j < SP; ++j)
-        if (j < S) sw[(n * S + j) * GS + g] = w[j];
+      for (int i = 0; i < 4; ++i) {
+        const int it = ig * 16 + 4 * hi + i;
+        if (it < items) sw[(it % GS) * SWR + (it / GS) * S + col] = w[i];
+      }
     }
   }
-  l_own = l_own * alpha_own + lsum;
+  l_lane = l_lane * a_lane + lsum;
 }
 
 // acc *= alpha, skipped when no head's running max moved (the common case).
@@ -488,60 +766,118 @@ __device__ __forceinline__ void rescale(float (&acc)[GS][EV], const float (&alph
   }
 }
 
-template <int D, int GS, int SP, int KF, int VF>
-__device__ __forceinline__ void process_k(const TileBuf<D, GS, KF, VF> &B, int nrows, int lane, h2 (&qh)[GS][8],
-                                          const float (&cq)[GS], float *sw) {
+
+// ---------------------------------------------------------------- phases --
+template <int D, int GS, int KF, int VF>
+struct Acc {
   using C = Cfg<D, GS, KF, VF>;
-  kcompute<D, GS, KF, C::KSTEPS, C::KQ>(B.k, B.ks, nrows, lane, qh, cq, sw);
+  float v[C::VM ? 1 : GS][C::VM ? 1 : C::EV];     // VALU value path: [head][lane's EV columns]
+  float m[C::VM ? C::MB : 1][C::VM ? C::NBV : 1];  // MFMA value path: head 4*mb + lane/16, column 16*nb + lane%16
+};
+
+template <int D, int GS>
+struct Query {
+  h2 qh[GS][8];                          // VALU key path
+  float cq[GS];
+  uint4 qB[D / 64][cdiv(GS, 4)];         // MFMA key path
+  float cqq[cdiv(GS, 4)];
+};
+
+// Per-wave LDS: scores / weights (head-major), the tile's K and V row
+// scales, and the int8 value tile of the MFMA path.
+template <int D, int GS, int KF, int VF>
+struct WaveLds {
+  using C = Cfg<D, GS, KF, VF>;
+  static constexpr int SW_BYTES = C::SWR * GS * 4;
+  static constexpr int SC_BYTES = 2 * 64 * 4;
+  static constexpr int VT_BYTES = C::VM ? C::SWR * D : 0;
+  static constexpr int BYTES = SW_BYTES + SC_BYTES + VT_BYTES;
+  float *sw;
+  float *sks;
+  float *svs;
+  char *vl;
+  __device__ __forceinline__ WaveLds(char *base) {
+    sw = reinterpret_cast<float *>(base);
+    sks = reinterpret_cast<float *>(base + SW_BYTES);
+    svs = sks + 64;
+    vl = base + SW_BYTES + SC_BYTES;
+  }
+};
+
+template <int D, int GS, int SP, int KF, int VF>
+__device__ __forceinline__ void process_k(const TileBuf<D, GS, KF, VF> &B, int nrows, int lane, Query<D, GS> &Q,
+                                          const WaveLds<D, GS, KF, VF> &L) {
+  using C = Cfg<D, GS, KF, VF>;
+  if constexpr (C::KM) {
+    L.sks[lane] = B.k.ks;
+    wave_lds_sync();
+    kcompute_mfma<D, GS, C::SWR, KF, VF>(B.k, lane, Q.qB, Q.cqq, L.sw, L.sks);
+  } else {
+    kcompute<D, GS, C::SWR, KF, C::KSTEPS, C::KQ>(B.k.k, nrows, lane, Q.qh, Q.cq, L.sw);
+  }
   wave_lds_sync();
 }
 
 template <int D, int GS, int SP, int KF, int VF>
-__device__ __forceinline__ void process_lv(const TileBuf<D, GS, KF, VF> &B, int nrows, int S, int R, int LR,
-                                           int lane, const float *sA, float *sw, float (&m_u)[GS], float &m_own,
-                                           float &l_own, float (&acc)[GS][Cfg<D, GS, KF, VF>::EV]) {
+__device__ __forceinline__ void process_lv(const TileBuf<D, GS, KF, VF> &B, int nrows, int S, int R, int lane,
+                                           const Basis<SP> &bas, const WaveLds<D, GS, KF, VF> &L, float (&m_u)[GS],
+                                           float &m_lane, float &l_lane, Acc<D, GS, KF, VF> &acc) {
   using C = Cfg<D, GS, KF, VF>;
   float alpha[GS];
-  logits<GS, SP, false>(sA, sw, nrows / S, R, S, LR, lane, m_u, m_own, l_own, alpha);
-  rescale(acc, alpha);
+  logits<GS, SP, C::SWR>(bas, L.sw, nrows / S, R, S, lane, m_u, m_lane, l_lane, alpha);
+  if constexpr (C::VM)
+    rescale_mfma<GS>(acc.m, alpha, lane);
+  else
+    rescale(acc.v, alpha);
   wave_lds_sync();
-  vcompute<D, GS, VF, C::VSTEPS, C::VDW, C::EV>(B.v, B.vs, nrows, lane, sw, acc);
+  if constexpr (C::VM)
+    vcompute_mfma<D, GS, C::SWR, KF, VF>(B.v, nrows, lane, L.sw, L.vl, L.svs, acc.m);
+  else
+    vcompute<D, GS, C::SWR, VF, C::VSTEPS, C::VDW, C::EV>(B.v.v, nrows, lane, L.sw, acc.v);
   wave_lds_sync();
 }
 
 // The raw tail (< R tokens of bf16 / fp32) in one wave, one load step at a
 // time so it needs few registers.  Every token is a block with R = S = 1.
-template <int D, int GS, int SP, int RAWK, int RAWV, int EV>
-__device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt, int LR, int lane, h2 (&qh)[GS][8],
-                                          const float (&cq)[GS], const float *sA, float *sw, float (&m_u)[GS],
-                                          float &m_own, float &l_own, float (&acc)[GS][EV]) {
+// acc (VALU layout) is rescaled here; alpha is returned for other
+// accumulators of the same heads.
+template <int D, int GS, int SP, int SWR, int RAWK, int RAWV, int EV>
+__device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt, int lane, h2 (&qh)[GS][8],
+                                          const float (&cq)[GS], float *sw, float (&m_u)[GS], float &m_lane,
+                                          float &l_lane, float (&acc)[GS][EV], float (&alpha)[GS]) {
   constexpr int LK = D / 16, RK = 64 / LK, EBK = ebytes(RAWK), EBV = ebytes(RAWV);
   constexpr int LV = D / EV, RV = 64 / LV, VDW = EV * EBV / 4;
+  static_assert(kMaxR % RV == 0 && kMaxR % RK == 0, "tail steps must tile the tail rows");
   const rsrc_t rk = make_rsrc(kt, (uint32_t)nt * D * EBK);
   const rsrc_t rv = make_rsrc(vt, (uint32_t)nt * D * EBV);
   const int rrk = lane / LK, ck = lane % LK;
-  const float one[1] = {1.0f};
   for (int r0 = 0; r0 < nt; r0 += RK) {
     uint4 kb[1][EBK];
 #pragma unroll
     for (int k = 0; k < EBK; ++k) kb[0][k] = bload128(rk, (uint32_t)(rrk * D + ck * 16) * EBK + 16 * k, r0 * D * EBK);
-    kcompute<D, GS, RAWK, 1, EBK>(kb, one, nt, lane, qh, cq, sw, r0);
+    kcompute<D, GS, SWR, RAWK, 1, EBK>(kb, nt, lane, qh, cq, sw, r0);
   }
   wave_lds_sync();
-  float alpha[GS];
-  logits<GS, SP, true>(sA, sw, nt, 1, 1, LR, lane, m_u, m_own, l_own, alpha);
+  Basis<SP> unit;
+  unit.unit(lane);
+  logits<GS, SP, SWR>(unit, sw, nt, 1, 1, lane, m_u, m_lane, l_lane, alpha);
   rescale(acc, alpha);
   wave_lds_sync();
   const int rrv = lane / LV, cv = lane % LV;
   const uint32_t off = (uint32_t)(rrv * D + cv * EV) * EBV;
   for (int r0 = 0; r0 < nt; r0 += RV) {
     uint32_t vb[1][VDW];
+    if constexpr (VDW % 4 == 0) {
 #pragma unroll
-    for (int k = 0; k < VDW / 4; ++k) {
-      const uint4 t = bload128(rv, off + 16 * k, r0 * D * EBV);
-      vb[0][4 * k] = t.x; vb[0][4 * k + 1] = t.y; vb[0][4 * k + 2] = t.z; vb[0][4 * k + 3] = t.w;
+      for (int k = 0; k < VDW / 4; ++k) {
+        const uint4 t = bload128(rv, off + 16 * k, r0 * D * EBV);
+        vb[0][4 * k] = t.x; vb[0][4 * k + 1] = t.y; vb[0][4 * k + 2] = t.z; vb[0][4 * k + 3] = t.w;
+      }
+    } else {
+      const uint2 t = bload64(rv, off, r0 * D * EBV);
+      vb[0][0] = t.x; vb[0][1] = t.y;
     }
-    vcompute<D, GS, RAWV, 1, VDW, EV>(vb, one, nt, lane, sw, acc, r0);
+    vcompute<D, GS, SWR, RAWV, 1, VDW, EV>(vb, nt, lane, sw, acc, r0);
   }
   wave_lds_sync();
 }
@@ -549,19 +885,22 @@ __device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt
 template <int D, int GS, int SP, int KF, int VF>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
   using C = Cfg<D, GS, KF, VF>;
-  constexpr int W = C::W, EV = C::EV;
-  constexpr int SWR = C::TR > kMaxR ? C::TR : kMaxR;    // tile rows or tail tokens
-  constexpr int SW_FLOATS = SWR * GS;
-  constexpr int MERGE_FLOATS = W * GS * D + W * GS * 2;
-  constexpr int COMB_FLOATS = 2 * kMaxSplits * GS + GS;
-  constexpr int LDS_FLOATS = cmax(cmax(W * SW_FLOATS, MERGE_FLOATS), COMB_FLOATS);
-  __shared__ float lds[LDS_FLOATS];
+  using WL = WaveLds<D, GS, KF, VF>;
+  constexpr int W = C::W, EV = C::EV, SWR = C::SWR, NT = 64 * W;
+  static_assert(C::TR <= 64, "one scale per lane and tile");
+  static_assert(C::TR <= SWR && C::KSTEPS * C::RK <= SWR && C::VSTEPS * C::RV <= SWR, "tile exceeds scratch");
+  static_assert(!C::KM || C::RG * 16 <= SWR, "key MFMA rows exceed scratch");
+  static_assert(!C::VM || (C::CH * 32 == SWR && C::VQ * 1024 <= SWR * D), "value tile exceeds scratch");
+  constexpr int MERGE_BYTES = (W * GS * D + W * GS * 2) * 4;
+  constexpr int LDS_BYTES = cmax(W * WL::BYTES, MERGE_BYTES);
+  __shared__ __attribute__((aligned(16))) char lds_raw[LDS_BYTES];
   __shared__ __attribute__((aligned(16))) float sA[kMaxR * SP];
   __shared__ int last_flag;
+  float *lds = reinterpret_cast<float *>(lds_raw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile addresses live in SGPRs
   const int split = blockIdx.x % a.ns;
   const int64_t pairq = blockIdx.x / a.ns;
   const int qg = (int)(pairq % a.NQG);
@@ -570,53 +909,26 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   const int h = (int)(bh % a.H);
   const int hq0 = h * a.G + qg * GS;
   const int R = a.R, S = a.S;
-  const int LR = R <= 8 ? 1 : (R <= 16 ? 2 : 4);
 
-  // kernel arguments may sit in host-coherent memory: copy A to LDS once
-  for (int i = tid; i < R * SP; i += 64 * W) sA[i] = a.A[i];
-  float *sw = lds + wave * SW_FLOATS;
-  // weights of rows past a tile's end multiply zero data: keep them finite
-  for (int i = lane; i < SW_FLOATS; i += 64) sw[i] = 0.0f;
-  __syncthreads();
-
-  // ---- query: fp16 pairs of the lane's 16 K elements, pre-scaled per head;
-  // done after the first tile's loads are issued so the latencies overlap
-  h2 qh[GS][8];
-  float cq[GS];
-  auto setup_q = [&]() {
-    const int d0 = (lane % C::LK) * 16;
-#pragma unroll
-    for (int g = 0; g < GS; ++g) {
-      const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + b * a.q_sb + (int64_t)(hq0 + g) * a.q_sh + d0);
-      const uint4 q0 = qp[0], q1 = qp[1];
-      const uint32_t wv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-      float qf[16];
-      float amax = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        qf[2 * t] = bf16lo(wv[t]);
-        qf[2 * t + 1] = bf16hi(wv[t]);
-        amax = fmaxf(amax, fmaxf(fabsf(qf[2 * t]), fabsf(qf[2 * t + 1])));
-      }
-      amax = group_red<C::LK, true>(amax);
-      int E = 0;
-      if (amax > 0.0f) frexpf(amax, &E);
-      const float up = ldexpf(1.0f, 15 - E);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) qh[g][t] = h2{(_Float16)(qf[2 * t] * up), (_Float16)(qf[2 * t + 1] * up)};
-      cq[g] = a.qk_scale * ldexpf(1.0f, E - 15);
-    }
-  };
-
+  const WL L(lds_raw + wave * WL::BYTES);
+  Basis<SP> bas;
+  Query<D, GS> Q;
+  Acc<D, GS, KF, VF> acc;
   float m_u[GS];
-  float acc[GS][EV];
 #pragma unroll
-  for (int g = 0; g < GS; ++g) {
-    m_u[g] = -INFINITY;
+  for (int g = 0; g < GS; ++g) m_u[g] = -INFINITY;
+  if constexpr (C::VM) {
 #pragma unroll
-    for (int e = 0; e < EV; ++e) acc[g][e] = 0.0f;
+    for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NBV; ++j) acc.m[i][j] = 0.0f;
+  } else {
+#pragma unroll
+    for (int g = 0; g < GS; ++g)
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc.v[g][e] = 0.0f;
   }
-  float m_own = -INFINITY, l_own = 0.0f;
+  float m_lane = -INFINITY, l_lane = 0.0f;   // running max and sum of this lane's head, (lane % 16) % GS
 
   // ---- this wave's tiles: t = wave, wave + W, ... of the split
   const int NB = C::TR / S;
@@ -625,10 +937,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   const int64_t nblk = blk1 > blk0 ? blk1 - blk0 : 0;
   const int ntiles = (int)((nblk + NB - 1) / NB);
   const int64_t k_bh = bh * a.k_bh_rows, v_bh = bh * a.v_bh_rows;
+  // Tiles past the split's end are empty (zero rows): their loads are out of
+  // range and return zeros without touching memory, so every buffer is
+  // re-requested unconditionally and the number of loads in flight is the
+  // same on every path (the compiler's wait counts stay exact).
   auto tile_ref = [&](int t) {
     TileRef T;
     const int64_t tb0 = blk0 + (int64_t)t * NB;
-    const int nb = (int)((blk1 - tb0) < NB ? (blk1 - tb0) : NB);
+    const int64_t left = blk1 - tb0;
+    const int nb = (int)(left < 0 ? 0 : (left < NB ? left : NB));
     const int64_t row0 = tb0 * S;
     T.k = static_cast<const char *>(a.krows) + (k_bh + row0) * D * C::EBK;
     T.v = static_cast<const char *>(a.vrows) + (v_bh + row0) * D * C::EBV;
@@ -638,82 +955,139 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     return T;
   };
 
-  if constexpr (GS <= 4) {
-    // two register buffers: tile t + W is in flight while tile t is computed
-    TileBuf<D, GS, KF, VF> bufA, bufB;
-    int t = wave;
-    if (t < ntiles) issue(bufA, tile_ref(t), lane);
-    setup_q();
-    for (; t < ntiles; t += 2 * W) {
-      const int t1 = t + W;
-      if (t1 < ntiles) issue(bufB, tile_ref(t1), lane);
-      __builtin_amdgcn_sched_barrier(0);
+  // Tiles stream through NBUF register buffers per wave, so a wave has
+  // several tiles in flight while it computes.  The small set-up loads
+  // (query, A from the kernel arguments) are issued before the first tiles',
+  // and the set-up work runs while they are in flight.
+  using QS = typename std::conditional<C::KM, QStageMfma<D, GS>, QStageValu<D, GS>>::type;
+  static_assert(QS::BYTES <= W * WL::BYTES && QS::WAVES <= W, "query staging exceeds the scratch");
+  QS qs;
+  const bool q_wave = wave < QS::WAVES;
+  if (q_wave) qs.load(a, b, hq0, wave, lane);
+  // A[r][j] = c_j cos(pi (2r + 1) j / (2R)), the orthonormal DCT-II synthesis
+  // (flashcodec-kv README, "Math"), evaluated in fp64 and rounded to fp32
+  // like the encoder's basis; entry r * SP + j per thread, zero padded.
+  float a_arg = 0.0f;
+  if (tid < R * SP && tid % SP < S) {
+    const int r = tid / SP, j = tid % SP;
+    const double cj = j == 0 ? sqrt(1.0 / R) : sqrt(2.0 / R);
+    a_arg = (float)(cj * cos(M_PI * (2 * r + 1) * j / (2.0 * R)));
+  }
+  // NBUF register buffers per wave: the first NBUF tiles are requested at once
+  TileBuf<D, GS, KF, VF> bufs[C::NBUF];
+#pragma unroll
+  for (int i = 0; i < C::NBUF; ++i) issue(bufs[i], tile_ref(wave + i * W), lane);
+  if (tid < kMaxR * SP) sA[tid] = a_arg;
+  if (q_wave) qs.convert(a, wave, lane, lds_raw);
+  __syncthreads();
+  if constexpr (C::KM)
+    QS::read(lds_raw, lane, Q.qB, Q.cqq);
+  else
+    QS::read(lds_raw, lane, Q.qh, Q.cq);
+  bas.load(sA, R, S, lane);
+  __syncthreads();   // the staging area becomes wave scratch
+  // weights of rows past a tile's end multiply zero data: keep them finite
+  for (int i = lane; i < SWR * GS; i += 64) L.sw[i] = 0.0f;
+  for (int t0 = wave; t0 < ntiles; t0 += C::NBUF * W) {
+#pragma unroll
+    for (int i = 0; i < C::NBUF; ++i) {
+      // the buffer's next tile: K rows requested once the K phase is done,
+      // V rows once the V phase is done
+      const int t = t0 + i * W;
+      const int tn = t + C::NBUF * W;
       const int n0 = tile_ref(t).nrows;
-      process_k<D, GS, SP, KF, VF>(bufA, n0, lane, qh, cq, sw);
-      process_lv<D, GS, SP, KF, VF>(bufA, n0, S, R, LR, lane, sA, sw, m_u, m_own, l_own, acc);
-      if (t1 < ntiles) {
-        const int t2 = t1 + W;
-        if (t2 < ntiles) issue(bufA, tile_ref(t2), lane);
-        __builtin_amdgcn_sched_barrier(0);
-        const int n1 = tile_ref(t1).nrows;
-        process_k<D, GS, SP, KF, VF>(bufB, n1, lane, qh, cq, sw);
-        process_lv<D, GS, SP, KF, VF>(bufB, n1, S, R, LR, lane, sA, sw, m_u, m_own, l_own, acc);
-      }
-    }
-  } else {
-    // one register buffer: the next tile's K rows are requested as soon as
-    // this tile's K phase is done, its V rows as soon as the V phase is done
-    TileBuf<D, GS, KF, VF> buf;
-    int t = wave;
-    if (t < ntiles) issue(buf, tile_ref(t), lane);
-    setup_q();
-    for (; t < ntiles; t += W) {
-      const int tn = t + W;
-      const int n0 = tile_ref(t).nrows;
-      process_k<D, GS, SP, KF, VF>(buf, n0, lane, qh, cq, sw);
-      if (tn < ntiles) issue_k(buf, tile_ref(tn), lane);
+      if (n0 > 0) process_k<D, GS, SP, KF, VF>(bufs[i], n0, lane, Q, L);
+      issue_k(bufs[i], tile_ref(tn), lane);
       __builtin_amdgcn_sched_barrier(0);
-      process_lv<D, GS, SP, KF, VF>(buf, n0, S, R, LR, lane, sA, sw, m_u, m_own, l_own, acc);
-      if (tn < ntiles) issue_v(buf, tile_ref(tn), lane);
+      if (n0 > 0) process_lv<D, GS, SP, KF, VF>(bufs[i], n0, S, R, lane, bas, L, m_u, m_lane, l_lane, acc);
+      issue_v(bufs[i], tile_ref(tn), lane);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // ---- the raw tail: one wave of the last split
-  if (a.n_tail > 0 && split == a.ns - 1 && wave == ntiles % W) {
+  // ---- the raw tail: one wave of the last split, on the VALU paths
+  const bool tail_wave = a.n_tail > 0 && split == a.ns - 1 && wave == ntiles % W;
+  // tail accumulator beside the MFMA layout: ET columns per lane, few registers
+  constexpr int ET = C::VM ? cmax(D / 64, 16 / GS) : 1, LT = D / ET;
+  float acct[C::VM ? GS : 1][ET];
+#pragma unroll
+  for (int g = 0; g < (C::VM ? GS : 1); ++g)
+#pragma unroll
+    for (int e = 0; e < ET; ++e) acct[g][e] = 0.0f;
+  if (tail_wave) {
+    if constexpr (C::KM) setup_q_valu<D, GS>(a, b, hq0, lane, Q.qh, Q.cq);
     const int nt = a.n_tail;
     const char *kt = static_cast<const char *>(a.ktail) + bh * (int64_t)R * D * (a.kraw == BF16 ? 2 : 4);
     const char *vt = static_cast<const char *>(a.vtail) + bh * (int64_t)R * D * (a.vraw == BF16 ? 2 : 4);
-    if (a.kraw == BF16 && a.vraw == BF16)
-      tail_pass<D, GS, SP, BF16, BF16, EV>(kt, vt, nt, LR, lane, qh, cq, sA, sw, m_u, m_own, l_own, acc);
-    else if (a.kraw == F32 && a.vraw == F32)
-      tail_pass<D, GS, SP, F32, F32, EV>(kt, vt, nt, LR, lane, qh, cq, sA, sw, m_u, m_own, l_own, acc);
-    else if (a.kraw == BF16)
-      tail_pass<D, GS, SP, BF16, F32, EV>(kt, vt, nt, LR, lane, qh, cq, sA, sw, m_u, m_own, l_own, acc);
-    else
-      tail_pass<D, GS, SP, F32, BF16, EV>(kt, vt, nt, LR, lane, qh, cq, sA, sw, m_u, m_own, l_own, acc);
+    float alpha[GS];
+    auto run = [&](auto &tacc) {
+      constexpr int E = sizeof(tacc[0]) / sizeof(float);
+      if (a.kraw == BF16 && a.vraw == BF16)
+        tail_pass<D, GS, SP, SWR, BF16, BF16, E>(kt, vt, nt, lane, Q.qh, Q.cq, L.sw, m_u, m_lane, l_lane, tacc, alpha);
+      else if (a.kraw == F32 && a.vraw == F32)
+        tail_pass<D, GS, SP, SWR, F32, F32, E>(kt, vt, nt, lane, Q.qh, Q.cq, L.sw, m_u, m_lane, l_lane, tacc, alpha);
+      else if (a.kraw == BF16)
+        tail_pass<D, GS, SP, SWR, BF16, F32, E>(kt, vt, nt, lane, Q.qh, Q.cq, L.sw, m_u, m_lane, l_lane, tacc, alpha);
+      else
+        tail_pass<D, GS, SP, SWR, F32, BF16, E>(kt, vt, nt, lane, Q.qh, Q.cq, L.sw, m_u, m_lane, l_lane, tacc, alpha);
+    };
+    if constexpr (C::VM) {
+      run(acct);
+      rescale_mfma<GS>(acc.m, alpha, lane);
+    } else {
+      run(acc.v);
+    }
   }
 
   // ---- wave totals: l over the lanes of a head, acc over the rows of a step
   float l_u[GS];
   {
-    const float lt = head_reduce<GS, false>(l_own, LR);
+    const float lt = strided<GS, false>(l_lane);
 #pragma unroll
-    for (int g = 0; g < GS; ++g) l_u[g] = readlane(lt, g * LR);
+    for (int g = 0; g < GS; ++g) l_u[g] = readlane(lt, g);
   }
-#pragma unroll
-  for (int g = 0; g < GS; ++g)
-#pragma unroll
-    for (int e = 0; e < EV; ++e) acc[g][e] = strided<C::LV, false>(acc[g][e]);
-
-  __syncthreads();   // all waves done with their sw scratch
-  float *macc = lds;                    // [W][GS][D]
-  float *mml = lds + W * GS * D;        // [W][GS][2]
-  if (lane < C::LV) {
+  if constexpr (!C::VM) {
 #pragma unroll
     for (int g = 0; g < GS; ++g)
 #pragma unroll
-      for (int e = 0; e < EV; ++e) macc[(wave * GS + g) * D + lane * EV + e] = acc[g][e];
+      for (int e = 0; e < EV; ++e) acc.v[g][e] = strided<C::LV, false>(acc.v[g][e]);
+  } else if (tail_wave) {
+#pragma unroll
+    for (int g = 0; g < GS; ++g)
+#pragma unroll
+      for (int e = 0; e < ET; ++e) acct[g][e] = strided<LT, false>(acct[g][e]);
+  }
+
+  // ---- merge the waves in LDS, in a fixed order (the result does not
+  // depend on timing): each wave's raw accumulator and (max, sum) per head.
+  __syncthreads();   // all waves done with their scratch
+  float *macc = lds;                    // [W][GS][D]
+  float *mml = lds + W * GS * D;        // [W][GS][2]
+  if constexpr (C::VM) {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      const int g = 4 * mb + lane / 16;
+      if (g < GS) {
+#pragma unroll
+        for (int nb = 0; nb < C::NBV; ++nb) macc[(wave * GS + g) * D + 16 * nb + lane % 16] = acc.m[mb][nb];
+      }
+    }
+    if (tail_wave) {
+      wave_lds_sync();
+      if (lane < LT) {
+#pragma unroll
+        for (int g = 0; g < GS; ++g)
+#pragma unroll
+          for (int e = 0; e < ET; ++e) macc[(wave * GS + g) * D + lane * ET + e] += acct[g][e];
+      }
+    }
+  } else {
+    if (lane < C::LV) {
+#pragma unroll
+      for (int g = 0; g < GS; ++g)
+#pragma unroll
+        for (int e = 0; e < EV; ++e) macc[(wave * GS + g) * D + lane * EV + e] = acc.v[g][e];
+    }
   }
   if (lane == 0) {
 #pragma unroll
@@ -723,31 +1097,54 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     }
   }
   __syncthreads();
+  // workgroup (max, sum, acc) of head g at column d
+  auto wg_partial = [&](int g, int d, float &m, float &l, float &sacc) {
+    m = -INFINITY;
+    for (int w = 0; w < W; ++w) m = fmaxf(m, mml[(w * GS + g) * 2]);
+    l = 0.0f;
+    sacc = 0.0f;
+    for (int w = 0; w < W; ++w) {
+      const float lw = mml[(w * GS + g) * 2 + 1];
+      if (lw > 0.0f) {
+        const float f = __builtin_amdgcn_exp2f(mml[(w * GS + g) * 2] - m);
+        l += lw * f;
+        sacc += macc[(w * GS + g) * D + d] * f;
+      }
+    }
+  };
+
+  auto store_out = [&](int g, int d, float o) {
+    const int64_t off = b * a.o_sb + (int64_t)(hq0 + g) * a.o_sh + d;
+    if (a.out_f32) {
+      static_cast<float *>(a.out)[off] = o;
+    } else {
+      uint32_t u = __float_as_uint(o);
+      u += 0x7FFFu + ((u >> 16) & 1u);
+      static_cast<uint16_t *>(a.out)[off] = (uint16_t)(u >> 16);
+    }
+  };
+
+  if (a.ns == 1) {
+    // the only split of its (b, h, group): normalise and write directly
+    for (int idx = tid; idx < GS * D; idx += NT) {
+      float m, l, sacc;
+      wg_partial(idx / D, idx % D, m, l, sacc);
+      store_out(idx / D, idx % D, sacc / l);
+    }
+    return;
+  }
 
   // ---- the workgroup's partial, published with device-scope stores
   float *pacc = a.part_acc + (pairq * a.ns + split) * GS * D;
   float *pml = a.part_ml + (pairq * a.ns + split) * GS * 2;
-  for (int idx = tid; idx < GS * D; idx += 64 * W) {
+  for (int idx = tid; idx < GS * D; idx += NT) {
     const int g = idx / D, d = idx % D;
-    float m = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < W; ++w) m = fmaxf(m, mml[(w * GS + g) * 2]);
-    float l = 0.0f, s = 0.0f;
-    if (m != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        const float lw = mml[(w * GS + g) * 2 + 1];
-        if (lw > 0.0f) {
-          const float f = __builtin_amdgcn_exp2f(mml[(w * GS + g) * 2] - m);
-          l += lw * f;
-          s += macc[(w * GS + g) * D + d] * f;
-        }
-      }
-    }
-    __hip_atomic_store(pacc + g * D + d, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float m, l, sacc;
+    wg_partial(g, d, m, l, sacc);
+    __hip_atomic_store(pacc + idx, sacc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == 0) {
-      __hip_atomic_store(pml + g * 2, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(pml + g * 2 + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pml + 2 * g, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pml + 2 * g + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   // Device-scope stores are complete once this thread's memory counter
@@ -761,56 +1158,43 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   __syncthreads();
   if (!last_flag) return;
 
-  // ---- last arrival: (max, sum) of every split into LDS, weights per split,
-  // then every (head, d) sums its split partials with independent loads.
-  const float *Pacc = a.part_acc + pairq * a.ns * GS * D;
-  const float *Pml = a.part_ml + pairq * a.ns * GS * 2;
-  float *cml = lds;                     // [ns*GS][2]; later the weight per split
-  float *cM = lds + 2 * a.ns * GS;      // [GS] 1/sum
-  for (int i = tid; i < a.ns * GS; i += 64 * W) {
-    cml[2 * i] = __hip_atomic_load(Pml + 2 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    cml[2 * i + 1] = __hip_atomic_load(Pml + 2 * i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (tid < GS) {
-    float m = -INFINITY;
-    for (int sp = 0; sp < a.ns; ++sp) m = fmaxf(m, cml[2 * (sp * GS + tid)]);
-    float l = 0.0f;
-    for (int sp = 0; sp < a.ns; ++sp) {
-      const float li = cml[2 * (sp * GS + tid) + 1];
-      const float f = li > 0.0f ? __builtin_amdgcn_exp2f(cml[2 * (sp * GS + tid)] - m) : 0.0f;
-      l += li * f;
-      cml[2 * (sp * GS + tid)] = f;
-    }
-    cM[tid] = 1.0f / l;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < GS * D; idx += 64 * W) {
+  // ---- last arrival: every (head, column) loads the (max, sum) and the
+  // partial of up to CB splits per round of device-scope loads (one round
+  // for CB or fewer splits) and folds them into a running (max, sum, acc).
+  constexpr int CB = 32;
+  const int ns = a.ns;
+  const float *Pacc = a.part_acc + pairq * ns * GS * D;
+  const float *Pml = a.part_ml + pairq * ns * GS * 2;
+  for (int idx = tid; idx < GS * D; idx += NT) {
     const int g = idx / D, d = idx % D;
-    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-    int sp = 0;
-    for (; sp + 4 <= a.ns; sp += 4) {
-      const float p0 = __hip_atomic_load(Pacc + ((sp + 0) * GS + g) * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float p1 = __hip_atomic_load(Pacc + ((sp + 1) * GS + g) * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float p2 = __hip_atomic_load(Pacc + ((sp + 2) * GS + g) * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float p3 = __hip_atomic_load(Pacc + ((sp + 3) * GS + g) * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s0 = fmaf(cml[2 * ((sp + 0) * GS + g)], p0, s0);
-      s1 = fmaf(cml[2 * ((sp + 1) * GS + g)], p1, s1);
-      s2 = fmaf(cml[2 * ((sp + 2) * GS + g)], p2, s2);
-      s3 = fmaf(cml[2 * ((sp + 3) * GS + g)], p3, s3);
+    float M = -INFINITY, Lsum = 0.0f, sacc = 0.0f;
+    for (int sp0 = 0; sp0 < ns; sp0 += CB) {
+      float m[CB], l[CB], p[CB];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const int sp = sp0 + u < ns ? sp0 + u : ns - 1;   // in range; duplicates are masked below
+        m[u] = __hip_atomic_load(Pml + 2 * (sp * GS + g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        l[u] = __hip_atomic_load(Pml + 2 * (sp * GS + g) + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        p[u] = __hip_atomic_load(Pacc + (int64_t)sp * GS * D + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      float Mn = M;
+#pragma unroll
+      for (int u = 0; u < CB; ++u)
+        if (sp0 + u < ns && l[u] > 0.0f) Mn = fmaxf(Mn, m[u]);
+      const float fo = Mn == M ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+      Lsum *= fo;
+      sacc *= fo;
+      M = Mn;
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        if (sp0 + u < ns && l[u] > 0.0f) {
+          const float f = __builtin_amdgcn_exp2f(m[u] - M);
+          Lsum = fmaf(l[u], f, Lsum);
+          sacc = fmaf(p[u], f, sacc);
+        }
+      }
     }
-    for (; sp < a.ns; ++sp)
-      s0 = fmaf(cml[2 * (sp * GS + g)],
-                __hip_atomic_load(Pacc + (sp * GS + g) * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), s0);
-    const float o = ((s0 + s1) + (s2 + s3)) * cM[g];
-    const int64_t off = b * a.o_sb + (int64_t)(hq0 + g) * a.o_sh + d;
-    if (a.out_f32) {
-      static_cast<float *>(a.out)[off] = o;
-    } else {
-      uint32_t u = __float_as_uint(o);
-      u += 0x7FFFu + ((u >> 16) & 1u);
-      static_cast<uint16_t *>(a.out)[off] = (uint16_t)(u >> 16);
-    }
+    store_out(g, d, sacc / Lsum);
   }
   if (tid == 0) __hip_atomic_store(a.counters + pairq, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -84,7 +84,6 @@ struct DecodeArgs {
   uint32_t *counters;     // one per (b, h, query group)
   float *part_ml;         // [pairs][ns][GS][2]
   float *part_acc;        // [pairs][ns][GS][D]
-  float A[kMaxR * kMaxS]; // synthesis basis A[r*SP + j], zero padded to SP
 };
 
 // Heads of one query group handled per workgroup, and padded kept rows.
