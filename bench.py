@@ -61,6 +61,74 @@ def load_traffic(workload):
     return d.get("traffic_bytes_per_launch")
 
 
+CALIB_ELEMS = 64 << 20      # fp32 elements of the calibration copy (256 MiB read + 256 MiB written)
+
+
+def profile_run(w, n):
+    """Launch sequence for rocprofv3 counter passes: one decode of the
+    workload (eager, so every launch is its own dispatch) n times, then a
+    plain elementwise copy of known size n times to calibrate the counters."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    k, v = syn.workload_kv(w)
+    q = syn.workload_query(w, 0).to(dev)
+    ks = cda.CodecStream(w.B, w.Hkv, w.D, w.R, w.S, fmt=w.kfmt, device=dev)
+    vs = cda.CodecStream(w.B, w.Hkv, w.D, w.R, w.S, fmt=w.vfmt, device=dev)
+    ks.encode(k.to(dev))
+    vs.encode(v.to(dev))
+    del k, v
+    out = torch.empty((w.B, w.Hq, 1, w.D), dtype=torch.float32, device=dev)
+    ws = torch.zeros(cda.decode_workspace_bytes(ks, vs, w.Hq), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    a = torch.ones(CALIB_ELEMS, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(n):
+        flush.fill_(1)                      # the archive is read from HBM, not the MALL
+        cda.decode_attention(q, ks, vs, out=out, workspace=ws)
+    for _ in range(n):
+        torch.neg(a, out=b)                 # reads and writes CALIB_ELEMS * 4 bytes
+    torch.cuda.synchronize()
+    print(f"# profile run done: {n} decodes, {n} calibration copies", flush=True)
+
+
+def traffic_summary(w, fetch_csv, write_csv, command):
+    """HBM bytes per decode launch from two rocprofv3 --pmc runs (FETCH_SIZE,
+    WRITE_SIZE; KiB per dispatch), each scaled by what the same counter reads
+    for the calibration copy of known size.  Writes the committed summary."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {"decode": [], "copy": []}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            if "decode_kernel" in name:
+                vals["decode"].append(float(r["Counter_Value"]))
+            elif "neg_kernel" in name:
+                vals["copy"].append(float(r["Counter_Value"]))
+        return {key: statistics.median(x) if x else None for key, x in vals.items()}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    wr = per_kernel(write_csv, "WRITE_SIZE")
+    calib = CALIB_ELEMS * 4
+    f_factor = calib / (f["copy"] * 1024.0)
+    w_factor = calib / (wr["copy"] * 1024.0)
+    fetch_b = f["decode"] * 1024.0 * f_factor
+    write_b = wr["decode"] * 1024.0 * w_factor
+    d = {"workload": w.name, "kernel": "decode_kernel", "kernel_source_hash": kernel_source_hash(),
+         "fetch_kib_per_launch": f["decode"], "write_kib_per_launch": wr["decode"],
+         "copy_fetch_kib": f["copy"], "copy_write_kib": wr["copy"], "copy_bytes_each_way": calib,
+         "fetch_factor": f_factor, "write_factor": w_factor,
+         "traffic_bytes_per_launch": fetch_b + write_b,
+         "algorithmic_bytes_per_launch": decode_bytes(w, w.n_blocks, w.n_tail), "command": command}
+    path = os.path.join(ROOT, "profiles", f"decode_{w.name}_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(d, fh, indent=1)
+    print(json.dumps(d, indent=1))
+
+
 def cpu_baseline(w, k, v, q, budget_s=15.0):
     """The fp64 oracle on the host cores, on a bounded sample: whole-sequence
     decode attention for as many kv heads (with their G query heads) as fit
@@ -104,12 +172,22 @@ def main():
     ap.add_argument("--workload", default="long128k", choices=sorted(syn.WORKLOADS))
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", type=int, default=0, metavar="N",
+                    help="launch sequence for rocprofv3 counter passes: N decodes and N calibration copies")
+    ap.add_argument("--traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="summarise two rocprofv3 --pmc runs into profiles/decode_<workload>_traffic.json")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     w = syn.WORKLOADS[args.workload]
+    if args.traffic:
+        traffic_summary(w, *args.traffic)
+        return
+    if args.profile:
+        profile_run(w, args.profile)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     L, K, W = args.layers, args.steps, args.warmup
@@ -176,21 +254,26 @@ def main():
     gbs = total_bytes / (elapsed_ms * 1e-3) / 1e9
     qtok = sum(step_qtok[W:]) / (elapsed_ms * 1e-3)
 
-    # ---- dominant kernel: per-launch decode duration on the launch stream
+    # ---- dominant kernel: average decode launch duration.  A graph of decode
+    # launches only (every layer, several rounds) is replayed on the capture
+    # stream and timed with events recorded on that stream.
     print("# timing decode launches", file=sys.stderr, flush=True)
-    reps = 20
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps * L)]
+    rounds = 4
     qd = queries[-1]
+    gd = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gd, stream=cap_stream):
+        for _ in range(rounds):
+            for li, (ks, vs) in enumerate(streams):
+                cda.decode_attention(qd, ks, vs, out=outs[li], workspace=ws)
+    with torch.cuda.stream(cap_stream):
+        gd.replay()
+        e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e_a.record(cap_stream)
+        for _ in range(5):
+            gd.replay()
+        e_b.record(cap_stream)
     torch.cuda.synchronize()
-    for r in range(reps):
-        for li, (ks, vs) in enumerate(streams):
-            a, b = evs[r * L + li]
-            a.record()
-            cda.decode_attention(qd, ks, vs, out=outs[li], workspace=ws)
-            b.record()
-    torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) * 1e-3 for a, b in evs]
-    avg_s = float(np.mean(durs[L:]))            # first round excluded (first touches)
+    avg_s = e_a.elapsed_time(e_b) * 1e-3 / (5 * rounds * L)
     per_launch = decode_bytes(w, streams[0][0].n_blocks, streams[0][0].n_tail)
     achieved = per_launch / avg_s / 1e9
     traffic = load_traffic(w.name)
@@ -199,7 +282,9 @@ def main():
         "metric": "decode-attn compressed-KV GB/s + query-heads*tokens/s at 1 GPU; % of HBM peak",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(elapsed_ms / K, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "int8 rows, fp32 accumulate", "data": "synthetic AR(1) KV, N(0,1) q",
+        "vs_baseline": None, "dtype": "f32",
+        "arith": "int8 x int8 MFMA products summed exactly in int32 (int8 rows, query and weights as int8 digits); "
+                 "fp32 softmax, scaling and accumulation", "data": "synthetic AR(1) KV, N(0,1) q",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "T0": w.T,
                    "R": w.R, "S": w.S, "k_rows": w.kfmt, "v_rows": w.vfmt, "layers_rotated": L,
                    "step": "per layer: codec_append_step + codec_decode_attention, HIP graph per step"},
