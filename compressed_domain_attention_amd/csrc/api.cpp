@@ -111,7 +111,12 @@ Plan make_plan(const codec_stream *k, const codec_stream *v, int64_t Hq) {
     p.ns = (int)((n + p.chunk - 1) / p.chunk);
   }
   p.n_wg = p.pairs * p.ns;
-  const size_t counters = align256((size_t)p.pairs * 4);
+  // Arrival counters live in a fixed region at the start of every workspace,
+  // so calls of different shapes that share one workspace never see another
+  // call's partials where they expect a zero counter.  More than one split
+  // only happens below kTargetWorkgroups pairs, which bounds the region.
+  if (p.ns > 1 && p.pairs > kTargetWorkgroups) p.ok = false;
+  const size_t counters = (size_t)kTargetWorkgroups * kCounterStride * 4;
   const size_t ml = align256((size_t)p.pairs * p.ns * p.GS * 2 * 4);
   const size_t acc = (size_t)p.pairs * p.ns * p.GS * k->head_dim * 4;
   p.off_ml = counters;

@@ -260,69 +260,63 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // Query of the key MFMA: B operand of v_mfma_i32_16x16x64_i8 for k step kk
 // and N block nb: column n = lane % 16 holds head 4*nb + n/4, digit n % 4 of
 // the query scaled to 22-bit integers; rows (bytes) are the same head_dim
-// elements the codes of this lane hold.  cqq = scale * log2(e) / up.
-// Converted once per workgroup (wave nb converts N block nb) and handed to
-// every wave through LDS: the raw loads are issued before the first tile's,
-// so the conversion does not wait for tile data.
+// elements the codes of this lane hold.  cqq = scale * log2(e) / up for the
+// lane's head.  Every wave converts its own copy: the raw loads are issued
+// before the first tile's, the conversion runs once they have landed.
 template <int D, int GS>
-struct QStageMfma {
+struct QRegMfma {
   static constexpr int KK = D / 64, NBN = cdiv(GS, 4);
-  static constexpr int BYTES = KK * NBN * 64 * 16 + NBN * 16;
-  static constexpr int WAVES = NBN;
-  uint4 raw[KK][2];
-  __device__ __forceinline__ void load(const DecodeArgs &a, int64_t b, int hq0, int nb, int lane) {
-    const int n = lane % 16, G = lane / 16, g = 4 * nb + n / 4;
-    const int gl = g < GS ? g : 0;    // columns of absent heads read a live one and are zeroed below
+  uint4 raw[NBN][KK][2];
+  __device__ __forceinline__ void load(const DecodeArgs &a, int b, int hq0, int lane) {
+    const int n = lane % 16, G = lane / 16;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + b * a.q_sb + (int64_t)(hq0 + gl) * a.q_sh + 64 * kk + 16 * G);
-      raw[kk][0] = qp[0];
-      raw[kk][1] = qp[1];
-    }
-  }
-  __device__ __forceinline__ void convert(const DecodeArgs &a, int nb, int lane, char *sq) const {
-    const int n = lane % 16, g = 4 * nb + n / 4;
-    const bool live = g < GS;
-    float qf[KK][16];
-    float amax = 0.0f;
+    for (int nb = 0; nb < NBN; ++nb) {
+      const int g = 4 * nb + n / 4;
+      const int gl = g < GS ? g : 0;   // columns of absent heads read a live one and are zeroed below
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const uint32_t wv[8] = {raw[kk][0].x, raw[kk][0].y, raw[kk][0].z, raw[kk][0].w,
-                              raw[kk][1].x, raw[kk][1].y, raw[kk][1].z, raw[kk][1].w};
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        qf[kk][2 * t] = live ? bf16lo(wv[t]) : 0.0f;
-        qf[kk][2 * t + 1] = live ? bf16hi(wv[t]) : 0.0f;
-        amax = fmaxf(amax, fmaxf(fabsf(qf[kk][2 * t]), fabsf(qf[kk][2 * t + 1])));
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (int64_t)b * a.q_sb + (int64_t)(hq0 + gl) * a.q_sh +
+                                                          64 * kk + 16 * G);
+        raw[nb][kk][0] = qp[0];
+        raw[nb][kk][1] = qp[1];
       }
     }
-    amax = fmaxf(amax, xshfl(amax, 16));
-    amax = fmaxf(amax, xshfl(amax, 32));
-    int E = 0;
-    if (amax > 0.0f) frexpf(amax, &E);
-    const float up = ldexpf(1.0f, 22 - E);
-    const int which = n % 4;
-    uint4 *dst = reinterpret_cast<uint4 *>(sq);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      uint32_t u[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) u[e] = biased(qf[kk][e] * up);
-      dst[(kk * NBN + nb) * 64 + lane] =
-          make_uint4(pack_digits(u[0], u[1], u[2], u[3], which), pack_digits(u[4], u[5], u[6], u[7], which),
-                     pack_digits(u[8], u[9], u[10], u[11], which), pack_digits(u[12], u[13], u[14], u[15], which));
-    }
-    // the scale is per head: the lane of digit 0 of head 4 nb + n/4 in row 0 stores it
-    if (lane < 16 && which == 0)
-      reinterpret_cast<float *>(sq + KK * NBN * 1024)[4 * nb + n / 4] = a.qk_scale * ldexpf(1.0f, E - 22);
   }
-  __device__ static __forceinline__ void read(const char *sq, int lane, uint4 (&qB)[KK][NBN], float (&cqq)[NBN]) {
+  __device__ __forceinline__ void convert(const DecodeArgs &a, int lane, uint4 (&qB)[KK][NBN],
+                                          float (&cqq)[NBN]) const {
+    const int n = lane % 16, which = n % 4;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int nb = 0; nb < NBN; ++nb) {
+      const bool live = 4 * nb + n / 4 < GS;
+      float qf[KK][16];
+      float amax = 0.0f;
 #pragma unroll
-      for (int nb = 0; nb < NBN; ++nb) qB[kk][nb] = reinterpret_cast<const uint4 *>(sq)[(kk * NBN + nb) * 64 + lane];
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint32_t wv[8] = {raw[nb][kk][0].x, raw[nb][kk][0].y, raw[nb][kk][0].z, raw[nb][kk][0].w,
+                                raw[nb][kk][1].x, raw[nb][kk][1].y, raw[nb][kk][1].z, raw[nb][kk][1].w};
 #pragma unroll
-    for (int nb = 0; nb < NBN; ++nb) cqq[nb] = reinterpret_cast<const float *>(sq + KK * NBN * 1024)[4 * nb + (lane % 16) / 4];
+        for (int t = 0; t < 8; ++t) {
+          qf[kk][2 * t] = live ? bf16lo(wv[t]) : 0.0f;
+          qf[kk][2 * t + 1] = live ? bf16hi(wv[t]) : 0.0f;
+          amax = fmaxf(amax, fmaxf(fabsf(qf[kk][2 * t]), fabsf(qf[kk][2 * t + 1])));
+        }
+      }
+      amax = fmaxf(amax, xshfl(amax, 16));
+      amax = fmaxf(amax, xshfl(amax, 32));
+      int E = 0;
+      if (amax > 0.0f) frexpf(amax, &E);
+      const float up = ldexpf(1.0f, 22 - E);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        uint32_t u[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) u[e] = biased(qf[kk][e] * up);
+        qB[kk][nb] = make_uint4(pack_digits(u[0], u[1], u[2], u[3], which), pack_digits(u[4], u[5], u[6], u[7], which),
+                                pack_digits(u[8], u[9], u[10], u[11], which),
+                                pack_digits(u[12], u[13], u[14], u[15], which));
+      }
+      cqq[nb] = a.qk_scale * ldexpf(1.0f, E - 22);
+    }
   }
 };
 
@@ -491,54 +485,40 @@ __device__ __forceinline__ void setup_q_valu(const DecodeArgs &a, int64_t b, int
   }
 }
 
-// The same, converted once per workgroup (wave g converts head g for the
-// D/16 lane positions) and handed to every wave through LDS.
+// The same, loads issued ahead of the tiles and converted afterwards.
 template <int D, int GS>
-struct QStageValu {
+struct QRegValu {
   static constexpr int LK = D / 16;
-  static constexpr int BYTES = GS * LK * 32 + cdiv(GS * 4, 16) * 16;
-  static constexpr int WAVES = GS;
-  uint4 raw[2];
-  __device__ __forceinline__ void load(const DecodeArgs &a, int64_t b, int hq0, int g, int lane) {
-    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + b * a.q_sb + (int64_t)(hq0 + g) * a.q_sh + (lane % LK) * 16);
-    raw[0] = qp[0];
-    raw[1] = qp[1];
-  }
-  __device__ __forceinline__ void convert(const DecodeArgs &a, int g, int lane, char *sq) const {
-    const uint32_t wv[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
-    float qf[16];
-    float amax = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      qf[2 * t] = bf16lo(wv[t]);
-      qf[2 * t + 1] = bf16hi(wv[t]);
-      amax = fmaxf(amax, fmaxf(fabsf(qf[2 * t]), fabsf(qf[2 * t + 1])));
-    }
-    amax = group_red<LK, true>(amax);
-    int E = 0;
-    if (amax > 0.0f) frexpf(amax, &E);
-    const float up = ldexpf(1.0f, 15 - E);
-    h2 qh[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) qh[t] = h2{(_Float16)(qf[2 * t] * up), (_Float16)(qf[2 * t + 1] * up)};
-    if (lane < LK) {
-      uint4 *dst = reinterpret_cast<uint4 *>(sq) + (g * LK + lane) * 2;
-      dst[0] = make_uint4(__builtin_bit_cast(uint32_t, qh[0]), __builtin_bit_cast(uint32_t, qh[1]),
-                          __builtin_bit_cast(uint32_t, qh[2]), __builtin_bit_cast(uint32_t, qh[3]));
-      dst[1] = make_uint4(__builtin_bit_cast(uint32_t, qh[4]), __builtin_bit_cast(uint32_t, qh[5]),
-                          __builtin_bit_cast(uint32_t, qh[6]), __builtin_bit_cast(uint32_t, qh[7]));
-    }
-    if (lane == 0) reinterpret_cast<float *>(sq + GS * LK * 32)[g] = a.qk_scale * ldexpf(1.0f, E - 15);
-  }
-  __device__ static __forceinline__ void read(const char *sq, int lane, h2 (&qh)[GS][8], float (&cq)[GS]) {
+  uint4 raw[GS][2];
+  __device__ __forceinline__ void load(const DecodeArgs &a, int b, int hq0, int lane) {
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(sq) + (g * LK + lane % LK) * 2;
-      const uint4 x = src[0], y = src[1];
-      const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+      const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (int64_t)b * a.q_sb + (int64_t)(hq0 + g) * a.q_sh +
+                                                        (lane % LK) * 16);
+      raw[g][0] = qp[0];
+      raw[g][1] = qp[1];
+    }
+  }
+  __device__ __forceinline__ void convert(const DecodeArgs &a, int lane, h2 (&qh)[GS][8], float (&cq)[GS]) const {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) qh[g][t] = __builtin_bit_cast(h2, w[t]);
-      cq[g] = reinterpret_cast<const float *>(sq + GS * LK * 32)[g];
+    for (int g = 0; g < GS; ++g) {
+      const uint32_t wv[8] = {raw[g][0].x, raw[g][0].y, raw[g][0].z, raw[g][0].w,
+                              raw[g][1].x, raw[g][1].y, raw[g][1].z, raw[g][1].w};
+      float qf[16];
+      float amax = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        qf[2 * t] = bf16lo(wv[t]);
+        qf[2 * t + 1] = bf16hi(wv[t]);
+        amax = fmaxf(amax, fmaxf(fabsf(qf[2 * t]), fabsf(qf[2 * t + 1])));
+      }
+      amax = group_red<LK, true>(amax);
+      int E = 0;
+      if (amax > 0.0f) frexpf(amax, &E);
+      const float up = ldexpf(1.0f, 15 - E);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) qh[g][t] = h2{(_Float16)(qf[2 * t] * up), (_Float16)(qf[2 * t + 1] * up)};
+      cq[g] = a.qk_scale * ldexpf(1.0f, E - 15);
     }
   }
 };
@@ -701,7 +681,12 @@ __device__ __forceinline__ void logits(const Basis<SP> &A, float *sw, int nb, in
     }
     return z;
   };
+  // First pass: the lane's max.  The running max is only moved when some
+  // logit exceeds it by more than kSlack (base 2): otherwise p <= 2^kSlack,
+  // harmless in fp32, and neither the head reduction nor a rescale is needed.
+  constexpr float kSlack = 8.0f;
   float mx = -INFINITY;
+#pragma unroll 2
   for (int ig = 0; ig < ngroups; ++ig) {
     const bool ok = ig * 16 + col < items;
 #pragma unroll
@@ -713,16 +698,19 @@ __device__ __forceinline__ void logits(const Basis<SP> &A, float *sw, int nb, in
       }
     }
   }
-  mx = strided<GS, true>(mx);
-  const float m_new = fmaxf(m_lane, mx);
-  const float a_lane = m_new == m_lane ? 1.0f : __builtin_amdgcn_exp2f(m_lane - m_new);
+  float m_new = m_lane, a_lane = 1.0f;
+  if (__builtin_amdgcn_ballot_w64(mx > m_lane + kSlack) != 0) {
+    mx = strided<GS, true>(mx);
+    m_new = fmaxf(m_lane, mx);
+    a_lane = m_new == m_lane ? 1.0f : __builtin_amdgcn_exp2f(m_lane - m_new);
 #pragma unroll
-  for (int gg = 0; gg < GS; ++gg) {
-    alpha[gg] = readlane(a_lane, gg);
-    m_u[gg] = readlane(m_new, gg);
+    for (int gg = 0; gg < GS; ++gg) m_u[gg] = readlane(m_new, gg);
   }
+#pragma unroll
+  for (int gg = 0; gg < GS; ++gg) alpha[gg] = readlane(a_lane, gg);
   m_lane = m_new;
   float lsum = 0.0f;
+#pragma unroll 2
   for (int ig = 0; ig < ngroups; ++ig) {
     const bool ok = ig * 16 + col < items;
     v4f w = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -901,12 +889,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile addresses live in SGPRs
-  const int split = blockIdx.x % a.ns;
-  const int64_t pairq = blockIdx.x / a.ns;
-  const int qg = (int)(pairq % a.NQG);
-  const int64_t bh = pairq / a.NQG;
-  const int64_t b = bh / a.H;
-  const int h = (int)(bh % a.H);
+  // grid: x = split, y = kv head * query groups + query group, z = batch row
+  const int split = blockIdx.x;
+  const int qg = (int)(blockIdx.y % (unsigned)a.NQG);
+  const int h = (int)(blockIdx.y / (unsigned)a.NQG);
+  const int b = blockIdx.z;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int64_t pairq = bh * a.NQG + qg;
   const int hq0 = h * a.G + qg * GS;
   const int R = a.R, S = a.S;
 
@@ -934,8 +923,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   const int NB = C::TR / S;
   const int64_t blk0 = (int64_t)split * a.chunk;
   const int64_t blk1 = (blk0 + a.chunk < a.n_blocks) ? blk0 + a.chunk : a.n_blocks;
-  const int64_t nblk = blk1 > blk0 ? blk1 - blk0 : 0;
-  const int ntiles = (int)((nblk + NB - 1) / NB);
+  const int nblk = blk1 > blk0 ? (int)(blk1 - blk0) : 0;   // a split holds < 2^31 blocks
+  const int ntiles = (nblk + NB - 1) / NB;
   const int64_t k_bh = bh * a.k_bh_rows, v_bh = bh * a.v_bh_rows;
   // Tiles past the split's end are empty (zero rows): their loads are out of
   // range and return zeros without touching memory, so every buffer is
@@ -955,39 +944,33 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     return T;
   };
 
-  // Tiles stream through NBUF register buffers per wave, so a wave has
-  // several tiles in flight while it computes.  The small set-up loads
-  // (query, A from the kernel arguments) are issued before the first tiles',
-  // and the set-up work runs while they are in flight.
-  using QS = typename std::conditional<C::KM, QStageMfma<D, GS>, QStageValu<D, GS>>::type;
-  static_assert(QS::BYTES <= W * WL::BYTES && QS::WAVES <= W, "query staging exceeds the scratch");
-  QS qs;
-  const bool q_wave = wave < QS::WAVES;
-  if (q_wave) qs.load(a, b, hq0, wave, lane);
+  // Tiles stream through NBUF register buffers per wave.  The query loads
+  // are issued before the first tile's, and the set-up work (basis, query
+  // conversion) runs while the tile is in flight.
+  using QR = typename std::conditional<C::KM, QRegMfma<D, GS>, QRegValu<D, GS>>::type;
+  QR qr;
+  qr.load(a, b, hq0, lane);
   // A[r][j] = c_j cos(pi (2r + 1) j / (2R)), the orthonormal DCT-II synthesis
-  // (flashcodec-kv README, "Math"), evaluated in fp64 and rounded to fp32
-  // like the encoder's basis; entry r * SP + j per thread, zero padded.
+  // (flashcodec-kv README, "Math"), entry r * SP + j per thread, zero padded.
   float a_arg = 0.0f;
   if (tid < R * SP && tid % SP < S) {
     const int r = tid / SP, j = tid % SP;
-    const double cj = j == 0 ? sqrt(1.0 / R) : sqrt(2.0 / R);
-    a_arg = (float)(cj * cos(M_PI * (2 * r + 1) * j / (2.0 * R)));
+    const float cj = j == 0 ? sqrtf(1.0f / (float)R) : sqrtf(2.0f / (float)R);
+    a_arg = cj * cospif((float)((2 * r + 1) * j) / (float)(2 * R));
   }
   // NBUF register buffers per wave: the first NBUF tiles are requested at once
   TileBuf<D, GS, KF, VF> bufs[C::NBUF];
 #pragma unroll
   for (int i = 0; i < C::NBUF; ++i) issue(bufs[i], tile_ref(wave + i * W), lane);
   if (tid < kMaxR * SP) sA[tid] = a_arg;
-  if (q_wave) qs.convert(a, wave, lane, lds_raw);
-  __syncthreads();
-  if constexpr (C::KM)
-    QS::read(lds_raw, lane, Q.qB, Q.cqq);
-  else
-    QS::read(lds_raw, lane, Q.qh, Q.cq);
-  bas.load(sA, R, S, lane);
-  __syncthreads();   // the staging area becomes wave scratch
   // weights of rows past a tile's end multiply zero data: keep them finite
   for (int i = lane; i < SWR * GS; i += 64) L.sw[i] = 0.0f;
+  __syncthreads();
+  bas.load(sA, R, S, lane);
+  if constexpr (C::KM)
+    qr.convert(a, lane, Q.qB, Q.cqq);
+  else
+    qr.convert(a, lane, Q.qh, Q.cq);
   for (int t0 = wave; t0 < ntiles; t0 += C::NBUF * W) {
 #pragma unroll
     for (int i = 0; i < C::NBUF; ++i) {
@@ -1152,7 +1135,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(a.counters + pairq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old =
+        __hip_atomic_fetch_add(a.counters + pairq * kCounterStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (old == (uint32_t)(a.ns - 1)) ? 1 : 0;
   }
   __syncthreads();
@@ -1196,13 +1180,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     }
     store_out(g, d, sacc / Lsum);
   }
-  if (tid == 0) __hip_atomic_store(a.counters + pairq, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(a.counters + pairq * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int GS, int SP, int KF, int VF>
 int launch_one(const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, GS, SP, KF, VF>), dim3((unsigned)n_wg), dim3(64 * kDecodeWaves), 0, stream,
-                     a);
+  const unsigned gy = (unsigned)(a.H * a.NQG);
+  const unsigned gz = (unsigned)(n_wg / ((int64_t)a.ns * gy));
+  hipLaunchKernelGGL((decode_kernel<D, GS, SP, KF, VF>), dim3((unsigned)a.ns, gy, gz), dim3(64 * kDecodeWaves), 0,
+                     stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

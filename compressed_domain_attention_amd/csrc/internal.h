@@ -81,7 +81,7 @@ struct DecodeArgs {
   void *out;
   int64_t o_sb, o_sh;
   int32_t out_f32;        // 1: fp32 out, 0: bf16 out
-  uint32_t *counters;     // one per (b, h, query group)
+  uint32_t *counters;     // one per (b, h, query group), kCounterStride apart
   float *part_ml;         // [pairs][ns][GS][2]
   float *part_acc;        // [pairs][ns][GS][D]
 };
@@ -91,6 +91,7 @@ int decode_group_size(int G);
 int decode_pad_keep(int S);
 
 constexpr int kMaxSplits = 256;   // splits per (b, kv head, query group)
+constexpr int kCounterStride = 64; // uint32 slots between arrival counters (256 bytes)
 
 // Coefficient rows per decode tile: about 8 KB of key plus value rows.
 constexpr int decode_elem_bytes(int f) { return f == I8 ? 1 : (f == BF16 ? 2 : 4); }

@@ -153,10 +153,12 @@ int codec_append_step(codec_stream *k, codec_stream *v,
 /*
  * codec_decode_workspace_bytes -- workspace needed by codec_decode_attention
  * for these streams and Hq query heads (a pure function of the shapes).
- * The workspace holds the per-split (max, sum, acc) partials and one
- * arrival counter per (b, kv head, query group).  It must be zero-filled
- * once before its first use; every completed decode call leaves the
- * counters at zero again, so it can be reused without clearing.
+ * The workspace holds a fixed 64 KiB region of arrival counters (one per
+ * (b, kv head, query group), 256 bytes apart) followed by the per-split
+ * (max, sum, acc) partials.  It must be zero-filled once before its first
+ * use; every completed decode call leaves the counters at zero again, so
+ * one workspace (of the largest size needed) can be reused without clearing
+ * by calls of any shape, one call at a time.
  * Errors: NULL, SHAPE, FORMAT, UNSUPPORTED.
  */
 int codec_decode_workspace_bytes(const codec_stream *k, const codec_stream *v,
