@@ -97,7 +97,9 @@ def ar1_sequence(B, H, T, D, rho, seed, offset_var=0.0, offset_seed=None, dtype=
         x0 = g.standard_normal((H, 1, D)) * sd
         if T > 1:
             eps = g.standard_normal((H, T - 1, D))
-            rest = lfilter([1.0], [1.0, -rho], eps, axis=1, zi=rho * x0)[0]
+            # the filter runs along the last axis (contiguous): same values, faster
+            rest = lfilter([1.0], [1.0, -rho], np.ascontiguousarray(eps.transpose(0, 2, 1)), axis=-1,
+                           zi=rho * x0.transpose(0, 2, 1))[0].transpose(0, 2, 1)
             x = np.concatenate([x0, rest], axis=1)
         else:
             x = x0[:, :T]
@@ -124,6 +126,60 @@ def workload_kv(w, T=None):
                      w.offset_var, 1000 * w.index + STREAM_OFF)
     v = ar1_sequence(w.B, w.Hkv, T, w.D, w.rho, 1000 * w.index + STREAM_V,
                      w.offset_var, 1000 * w.index + STREAM_OFF + 10)
+    return k, v
+
+
+def ar1_sequence_device(B, H, T, D, rho, seed, offset_var=0.0, offset_seed=None, device="cuda"):
+    """(B, H, T, D) bf16 device tensor of the same AR(1) process, drawn on the
+    device (torch Philox generator seeded with `seed`; offsets from
+    `offset_seed`) for the full-size workloads, where host generation is slow.
+
+    The recurrence is evaluated exactly in float64 in chunks of L steps: inside
+    a chunk y = P e with P[i][j] = rho^(i-j) (i >= j), then the carried state
+    adds rho^(i+1) * x_end(previous chunk).
+    """
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(seed))
+    sd = 1.0 / np.sqrt(1.0 - rho * rho) if rho < 1 else 1.0
+    x0 = torch.randn((B, H, 1, D), generator=g, device=dev, dtype=torch.float64) * sd
+    L = 256
+    n_rest = T - 1
+    C = (n_rest + L - 1) // L
+    out = torch.empty((B, H, T, D), dtype=torch.bfloat16, device=dev)
+    out[:, :, 0:1] = x0.to(torch.float32).to(torch.bfloat16)
+    if n_rest > 0:
+        i = torch.arange(L, device=dev, dtype=torch.float64)
+        P = torch.tril(torch.pow(torch.tensor(rho, dtype=torch.float64, device=dev), i[:, None] - i[None, :]))
+        carry_pow = torch.pow(torch.tensor(rho, dtype=torch.float64, device=dev), i + 1)   # rho^(i+1)
+        state = x0[:, :, 0, :]                                     # (B, H, D)
+        if offset_var:
+            go = torch.Generator(device=dev)
+            go.manual_seed(int(offset_seed if offset_seed is not None else seed + 1))
+            off = torch.randn((B, H, 1, D), generator=go, device=dev, dtype=torch.float64) * np.sqrt(offset_var)
+            out[:, :, 0:1] = (x0 + off).to(torch.float32).to(torch.bfloat16)
+        else:
+            off = None
+        for c in range(C):
+            n = min(L, n_rest - c * L)
+            e = torch.randn((B, H, n, D), generator=g, device=dev, dtype=torch.float64)
+            y = torch.matmul(P[:n, :n], e)                         # (B, H, n, D), zero initial state
+            y += carry_pow[:n, None] * state[:, :, None, :]
+            state = y[:, :, n - 1, :]
+            if off is not None:
+                y = y + off
+            out[:, :, 1 + c * L:1 + c * L + n] = y.to(torch.float32).to(torch.bfloat16)
+    return out
+
+
+def workload_kv_device(w, T=None, device="cuda"):
+    """(K, V) bf16 device tensors (B, Hkv, T, D) for workload `w`, drawn on
+    the device (see ar1_sequence_device)."""
+    T = (w.T + w.steps) if T is None else T
+    k = ar1_sequence_device(w.B, w.Hkv, T, w.D, w.rho, 1000 * w.index + STREAM_K,
+                            w.offset_var, 1000 * w.index + STREAM_OFF, device)
+    v = ar1_sequence_device(w.B, w.Hkv, T, w.D, w.rho, 1000 * w.index + STREAM_V,
+                            w.offset_var, 1000 * w.index + STREAM_OFF + 10, device)
     return k, v
 
 

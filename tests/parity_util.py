@@ -37,6 +37,16 @@ def gpu_archive(st):
     return dict(fmt=FMT_NAME[st.fmt], R=st.R, S=st.S, rows=rows, scales=scales, tail=tail, n_blocks=n)
 
 
+def gpu_head_archive(st, b, h):
+    """One (b, kv head) of the GPU stream's archive in the oracle's dict form,
+    shaped as a batch of one with one head."""
+    n = st.n_blocks
+    rows = rows_to_numpy(st.rows[b:b + 1, h:h + 1, :n], st.fmt)
+    scales = st.scales[b:b + 1, h:h + 1, :n].detach().cpu().numpy() if st.fmt == bd.FMT_I8 else None
+    tail = syn.bf16_to_numpy(st.tail[b:b + 1, h:h + 1, :st.n_tail].cpu())
+    return dict(fmt=FMT_NAME[st.fmt], R=st.R, S=st.S, rows=rows, scales=scales, tail=tail, n_blocks=n)
+
+
 def assert_archive_equal(got, want, blocks=None):
     """Bit-exact rows / scales / tail (optionally only for listed (b, h, n))."""
     if blocks is None:

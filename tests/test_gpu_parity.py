@@ -147,6 +147,64 @@ def test_decode_repeatable_and_workspace_reuse():
         assert torch.equal(o, outs[0])
 
 
+def test_one_workspace_for_calls_of_different_shapes():
+    """One explicit workspace serves decodes whose (b, kv head, group) pair
+    counts and split counts differ, interleaved: every result matches the
+    oracle (the arrival counters must never meet another call's partials)."""
+    note("decode shared workspace")
+    cases = []
+    for (B, Hq, H, T, seed) in ((1, 32, 8, 16 * 2000 + 3, 21), (4, 32, 8, 16 * 300 + 1, 22), (2, 8, 2, 16 * 900, 23)):
+        k, v, q = syn.small_case(B, Hq, H, 128, T, seed=seed)
+        ks, vs = make_streams(k, v, 16, 4, "i8", "i8")
+        cases.append((q.to(DEV), ks, vs))
+    need = max(bd.decode_workspace_bytes(ks, vs, q.shape[1]) for (q, ks, vs) in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    refs = [O.decode_attention(syn.bf16_to_numpy(q), gpu_archive(ks), gpu_archive(vs)) for (q, ks, vs) in cases]
+    for order in ((0, 1, 2), (2, 0, 1), (1, 1, 0, 2, 0)):
+        for i in order:
+            q, ks, vs = cases[i]
+            out = bd.decode_attention(q, ks, vs, workspace=ws)
+            torch.cuda.synchronize()
+            assert rel_err(out.cpu().numpy()[:, :, 0], refs[i]) <= TOL, (order, i)
+
+
+def test_graph_replay_matches_eager():
+    """append + decode captured in a HIP graph and replayed several times
+    with eager work in between: every replay equals the eager result of the
+    same step (the graph holds no memset nodes; the counters self-reset)."""
+    note("graph replay")
+    B, Hq, H, D, R, S, T0 = 2, 8, 2, 128, 8, 2, 8 * 200 + 7
+    k, v, q = syn.small_case(B, Hq, H, D, T0 + 8, seed=31)
+    kd, vd, qd = k.to(DEV), v.to(DEV), q.to(DEV)
+    # eager reference: append the token at T0 (completes a block), then decode
+    ks, vs = make_streams(k[:, :, :T0], v[:, :, :T0], R, S, "i8", "i8", capacity=T0 // R + 4)
+    bd.append_step(ks, vs, kd[:, :, T0:T0 + 1], vd[:, :, T0:T0 + 1])
+    ref = bd.decode_attention(qd, ks, vs).clone()
+    torch.cuda.synchronize()
+    # graph: the same step on fresh streams, replayed after restoring the state
+    gs_k, gs_v = make_streams(k[:, :, :T0], v[:, :, :T0], R, S, "i8", "i8", capacity=T0 // R + 4)
+    snap = [t.clone() for t in (gs_k.rows, gs_k.scales, gs_k.tail, gs_v.rows, gs_v.scales, gs_v.tail)]
+    n0, t0 = gs_k.n_blocks, gs_k.n_tail
+    ws = torch.zeros(bd.decode_workspace_bytes(gs_k, gs_v, Hq), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, 1, D), dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        bd.append_step(gs_k, gs_v, kd[:, :, T0:T0 + 1], vd[:, :, T0:T0 + 1])
+        bd.decode_attention(qd, gs_k, gs_v, out=out, workspace=ws)
+    for rep in range(4):
+        for dst, src in zip((gs_k.rows, gs_k.scales, gs_k.tail, gs_v.rows, gs_v.scales, gs_v.tail), snap):
+            dst.copy_(src)
+        noise = torch.randn(1 << 20, device=DEV).sum()        # eager work between replays
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep
+        assert float(noise) == float(noise)
+    assert (gs_k.n_blocks, gs_k.n_tail) != (n0, t0)            # host counters advanced once, at capture
+
+
 # ------------------------------------------------------------------ append --
 @pytest.mark.parametrize("R,S,kfmt,vfmt,T0,steps", [
     (8, 3, "i8", "bf16", 8 * 10 + 5, 30),
