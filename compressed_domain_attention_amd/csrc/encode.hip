@@ -91,7 +91,7 @@ __device__ inline int8_t quantise(double c, float s32, double inv) {
 
 // Encode block `n` (call-relative) of stream row (b, h) into archive slot
 // a.n0 + n.  One wave; lane owns head_dim elements [lane*EPL, lane*EPL+EPL).
-template <int EPL, int SP>
+template <int EPL, int SP, bool PIPE>
 __device__ void encode_block(const EncodeArgs &a, const float *__restrict__ M, int64_t b, int64_t h,
                              int64_t n, int lane) {
   constexpr int D = EPL * 64;
@@ -103,18 +103,35 @@ __device__ void encode_block(const EncodeArgs &a, const float *__restrict__ M, i
 #pragma unroll
     for (int e = 0; e < EPL; ++e) c[j][e] = 0.0;  // +0.0
 
-  for (int i = 0; i < R; ++i) {
-    float x[EPL];
-    if (i < a.split_i)
-      load_raw<EPL>(a.src0, b * a.s0_b + h * a.s0_h + (n * R + i) * a.s0_t + d0, a.raw, x);
-    else
-      load_raw<EPL>(a.src1, b * a.s1_b + h * a.s1_h + d0, a.raw, x);
+  // PIPE (a lone block, latency-bound): tokens are loaded eight at a time, all
+  // requests in flight together.  Otherwise (many blocks in flight, register
+  // bound) one token at a time.  Products are added in token order either way
+  // (the contract's summation order).
+  constexpr int U = PIPE ? 8 : 1;
+  for (int i0 = 0; i0 < R; i0 += U) {
+    float x[U][EPL];
 #pragma unroll
-    for (int j = 0; j < SP; ++j) {
-      if (j < S) {
-        const double m = (double)M[j * R + i];
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u;
+      if (i < R) {
+        if (i < a.split_i)
+          load_raw<EPL>(a.src0, b * a.s0_b + h * a.s0_h + (n * R + i) * a.s0_t + d0, a.raw, x[u]);
+        else
+          load_raw<EPL>(a.src1, b * a.s1_b + h * a.s1_h + d0, a.raw, x[u]);
+      }
+    }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) c[j][e] = fma(m, (double)x[e], c[j][e]);
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u;
+      if (i < R) {
+#pragma unroll
+        for (int j = 0; j < SP; ++j) {
+          if (j < S) {
+            const double m = (double)M[j * R + i];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) c[j][e] = fma(m, (double)x[u][e], c[j][e]);
+          }
+        }
       }
     }
   }
@@ -161,7 +178,7 @@ __global__ __launch_bounds__(64 * kEncodeWaves) void encode_kernel(EncodeLaunch 
   const int64_t n = (blockIdx.x % per_bh) * kEncodeWaves + wave;
   const int64_t b = bh / a.H, h = bh % a.H;
   if (n < a.n_new) {
-    encode_block<EPL, SP>(a, sM, b, h, n, lane);
+    encode_block<EPL, SP, false>(a, sM, b, h, n, lane);
   } else if (n == a.n_new && a.n_copy > 0) {
     // raw remainder -> tail slots 0 .. n_copy-1, verbatim
     const int d0 = lane * EPL;
@@ -186,7 +203,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs A) {
     __shared__ float sM[kMaxS * kMaxR];
     for (int i = lane; i < a.S * a.R; i += 64) sM[i] = A.M[i];
     __syncthreads();
-    encode_block<EPL, SP>(a, sM, b, h, 0, lane);
+    encode_block<EPL, SP, true>(a, sM, b, h, 0, lane);
   } else {
     const int d0 = lane * EPL;
     float x[EPL];
