@@ -660,7 +660,7 @@ struct Basis {
 };
 
 template <int GS, int SP, int SWR>
-__device__ __forceinline__ void logits(const Basis<SP> &A, float *sw, int nb, int R, int S, int lane,
+__device__ __forceinline__ void logits_any(const Basis<SP> &A, float *sw, int nb, int R, int S, int lane,
                                        float (&m_u)[GS], float &m_lane, float &l_lane, float (&alpha)[GS]) {
   constexpr int SK = Basis<SP>::SK;
   const int col = lane % 16, hi = lane / 16;
@@ -740,6 +740,87 @@ __device__ __forceinline__ void logits(const Basis<SP> &A, float *sw, int nb, in
   l_lane = l_lane * a_lane + lsum;
 }
 
+// Tile version: at most NG groups (a compile-time bound for the tile's
+// blocks), one token tile (R <= 16).  z is computed once and kept in
+// registers between the max and the exponentials; the four w products of a
+// group go to independent accumulators.  Other shapes take logits_any.
+template <int GS, int SP, int SWR, int NG>
+__device__ __forceinline__ void logits(const Basis<SP> &A, float *sw, int nb, int R, int S, int lane,
+                                       float (&m_u)[GS], float &m_lane, float &l_lane, float (&alpha)[GS]) {
+  constexpr int SK = Basis<SP>::SK;
+  const int items = nb * GS;
+  const int ngroups = (items + 15) / 16;
+  if (A.rt_n != 1 || ngroups > NG) {
+    logits_any<GS, SP, SWR>(A, sw, nb, R, S, lane, m_u, m_lane, l_lane, alpha);
+    return;
+  }
+  const int col = lane % 16, hi = lane / 16;
+  const int g = col % GS;
+  constexpr float kSlack = 8.0f;
+  v4f z[NG];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int ig = 0; ig < NG; ++ig) {
+    if (ig < ngroups) {
+      const int it = ig * 16 + col;
+      const bool ok = it < items;
+      const int base = g * SWR + (it / GS) * S;
+      v4f zz = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < SK; ++kk) {
+        const int j = 4 * kk + hi;
+        const bool live = ok && j < S;
+        const float sv = sw[live ? base + j : 0];
+        zz = __builtin_amdgcn_mfma_f32_16x16x4f32(A.az[0][kk], live ? sv : 0.0f, zz, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool v = ok && 4 * hi + i < R;
+        zz[i] = v ? zz[i] : -INFINITY;
+        mx = fmaxf(mx, zz[i]);
+      }
+      z[ig] = zz;
+    }
+  }
+  float m_new = m_lane, a_lane = 1.0f;
+  if (__builtin_amdgcn_ballot_w64(mx > m_lane + kSlack) != 0) {
+    mx = strided<GS, true>(mx);
+    m_new = fmaxf(m_lane, mx);
+    a_lane = m_new == m_lane ? 1.0f : __builtin_amdgcn_exp2f(m_lane - m_new);
+#pragma unroll
+    for (int gg = 0; gg < GS; ++gg) m_u[gg] = readlane(m_new, gg);
+  }
+#pragma unroll
+  for (int gg = 0; gg < GS; ++gg) alpha[gg] = readlane(a_lane, gg);
+  m_lane = m_new;
+  float lsum = 0.0f;
+#pragma unroll
+  for (int ig = 0; ig < NG; ++ig) {
+    if (ig < ngroups) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(z[ig][i] - m_new);   // masked tokens: exp2(-inf) = 0
+        lsum += p[i];
+      }
+      v4f w0 = {0.0f, 0.0f, 0.0f, 0.0f}, w1 = w0, w2 = w0, w3 = w0;
+      w0 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[0], A.bw[0][0], w0, 0, 0, 0);
+      w1 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[1], A.bw[0][1], w1, 0, 0, 0);
+      w2 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[2], A.bw[0][2], w2, 0, 0, 0);
+      w3 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[3], A.bw[0][3], w3, 0, 0, 0);
+      // lane (hi, j = col) holds w of items ig*16 + 4 hi + i, coefficient j
+      if (col < S) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int it = ig * 16 + 4 * hi + i;
+          if (it < items) sw[(it % GS) * SWR + (it / GS) * S + col] = (w0[i] + w1[i]) + (w2[i] + w3[i]);
+        }
+      }
+    }
+  }
+  l_lane = l_lane * a_lane + lsum;
+}
+
 // acc *= alpha, skipped when no head's running max moved (the common case).
 template <int GS, int EV>
 __device__ __forceinline__ void rescale(float (&acc)[GS][EV], const float (&alpha)[GS]) {
@@ -812,7 +893,11 @@ __device__ __forceinline__ void process_lv(const TileBuf<D, GS, KF, VF> &B, int 
                                            float &m_lane, float &l_lane, Acc<D, GS, KF, VF> &acc) {
   using C = Cfg<D, GS, KF, VF>;
   float alpha[GS];
-  logits<GS, SP, C::SWR>(bas, L.sw, nrows / S, R, S, lane, m_u, m_lane, l_lane, alpha);
+  // groups of 16 (block, head) items in a tile: the fewest kept rows a
+  // padded keep count SP allows is SP / 2 + 1 (S = 1 when SP = 2)
+  constexpr int kSmin = SP == 2 ? 1 : SP / 2 + 1;
+  constexpr int NG = cmax(1, cdiv((C::TR / kSmin) * GS, 16));
+  logits<GS, SP, C::SWR, NG>(bas, L.sw, nrows / S, R, S, lane, m_u, m_lane, l_lane, alpha);
   if constexpr (C::VM)
     rescale_mfma<GS>(acc.m, alpha, lane);
   else
@@ -848,7 +933,7 @@ __device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt
   wave_lds_sync();
   Basis<SP> unit;
   unit.unit(lane);
-  logits<GS, SP, SWR>(unit, sw, nt, 1, 1, lane, m_u, m_lane, l_lane, alpha);
+  logits_any<GS, SP, SWR>(unit, sw, nt, 1, 1, lane, m_u, m_lane, l_lane, alpha);
   rescale(acc, alpha);
   wave_lds_sync();
   const int rrv = lane / LV, cv = lane % LV;
