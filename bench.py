@@ -129,10 +129,11 @@ def traffic_summary(w, fetch_csv, write_csv, command):
     print(json.dumps(d, indent=1))
 
 
-def cpu_baseline(w, k, v, q, budget_s=15.0):
+def cpu_baseline(w, k, v, q, budget_s=12.0):
     """The fp64 oracle on the host cores, on a bounded sample: whole-sequence
-    decode attention for as many kv heads (with their G query heads) as fit
-    in the time budget.  Returns the JSON object."""
+    decode attention of one kv head (with its G query heads) at a time,
+    cycling over the kv heads until the time budget is spent (the archives
+    are encoded once, outside the timed part).  Returns the JSON object."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -141,27 +142,28 @@ def cpu_baseline(w, k, v, q, budget_s=15.0):
         cores = 1
     R, S = w.R, w.S
     n = w.T // R
-    done, bytes_done, t_used = 0, 0, 0.0
-    heads = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    per_head = n * S * (w.D * EB[w.kfmt] + (4 if w.kfmt == "i8" else 0) + w.D * EB[w.vfmt]
+                        + (4 if w.vfmt == "i8" else 0)) + 2 * (w.T % R) * w.D * 2 + w.G * w.D * 6
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hkv)][:16]
     qn = syn.bf16_to_numpy(q)[:, :, 0]
     scale = w.D ** -0.5
+    arch = []
     for (b, h) in heads:
-        t0 = time.perf_counter()
         kx = syn.bf16_to_numpy(k[b:b + 1, h:h + 1, :w.T])
         vx = syn.bf16_to_numpy(v[b:b + 1, h:h + 1, :w.T])
-        ka, va = O.encode(kx, R, S, w.kfmt), O.encode(vx, R, S, w.vfmt)
-        t1 = time.perf_counter()
+        arch.append((b, h, O.encode(kx, R, S, w.kfmt), O.encode(vx, R, S, w.vfmt)))
+    done, t_used = 0, 0.0
+    while t_used < budget_s:
+        b, h, ka, va = arch[done % len(arch)]
         qs = qn[b:b + 1, h * w.G:(h + 1) * w.G]
+        t1 = time.perf_counter()
         O.decode_attention(qs, ka, va, scale)
         t_used += time.perf_counter() - t1
         done += 1
-        bytes_done += n * S * (w.D * EB[w.kfmt] + (4 if w.kfmt == "i8" else 0) + w.D * EB[w.vfmt]
-                               + (4 if w.vfmt == "i8" else 0)) + 2 * (w.T % R) * w.D * 2 + w.G * w.D * 6
-        if t_used + (t1 - t0) >= budget_s:
-            break
-    return {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"decode attention of {done} of {len(heads)} kv heads (each with its {w.G} query heads) "
-                      f"over the full {w.T}-token archive, fp64 numpy; {t_used:.1f}s of oracle time"}
+    return {"value": round(done * per_head / t_used / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} whole-archive decodes ({w.T} tokens, one kv head with its {w.G} query heads each), "
+                      f"cycling over {len(arch)} of the {w.B * w.Hkv} kv heads; fp64 numpy; "
+                      f"{t_used:.1f}s of oracle time"}
 
 
 def main():
