@@ -79,6 +79,17 @@ __device__ __forceinline__ float strided(float v) {
   return v;
 }
 
+// Maximum over lanes l and l ^ 32 (l ^ 16): the gfx950 half-wave (row pair)
+// swaps exchange the two halves, so max(copy, swapped copy) is the pair max.
+__device__ __forceinline__ uint32_t umax_x32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(r[0], r[1]);
+}
+__device__ __forceinline__ uint32_t umax_x16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max(r[0], r[1]);
+}
+
 __device__ __forceinline__ float readlane(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
@@ -398,16 +409,22 @@ __device__ __forceinline__ void vcompute_mfma(const VBuf<D, GS, KF, VF, true> &v
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
       const int g = 4 * mb + m / 4;
+      // the lane's 8 weights: two aligned 16-byte reads (absent heads read
+      // head 0), rows past the tile's end and absent heads selected to zero
+      const float *wp = sw + (g < GS ? g : 0) * SWR + r0;
+      const float4 wa = *reinterpret_cast<const float4 *>(wp);
+      const float4 wb = *reinterpret_cast<const float4 *>(wp + 4);
+      const float wr[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
       float w[8];
-      float amax = 0.0f;
+      uint32_t ubits = 0;   // max |w| as bits: non-negative floats order like their bit patterns
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const bool ok = g < GS && r0 + j < nrows;
-        w[j] = ok ? sw[g * SWR + r0 + j] * vsj[j] : 0.0f;
-        amax = fmaxf(amax, fabsf(w[j]));
+        w[j] = ok ? wr[j] * vsj[j] : 0.0f;
+        ubits = max(ubits, __float_as_uint(fabsf(w[j])));
       }
-      amax = fmaxf(amax, xshfl(amax, 16));
-      amax = fmaxf(amax, xshfl(amax, 32));
+      ubits = umax_x16(umax_x32(ubits));
+      const float amax = __uint_as_float(ubits);
       int E = 0;
       if (amax > 0.0f) frexpf(amax, &E);
       const float up = ldexpf(1.0f, 22 - E);
@@ -788,10 +805,14 @@ __device__ __forceinline__ void logits(const Basis<SP> &A, float *sw, int nb, in
     m_new = fmaxf(m_lane, mx);
     a_lane = m_new == m_lane ? 1.0f : __builtin_amdgcn_exp2f(m_lane - m_new);
 #pragma unroll
-    for (int gg = 0; gg < GS; ++gg) m_u[gg] = readlane(m_new, gg);
-  }
+    for (int gg = 0; gg < GS; ++gg) {
+      m_u[gg] = readlane(m_new, gg);
+      alpha[gg] = readlane(a_lane, gg);
+    }
+  } else {
 #pragma unroll
-  for (int gg = 0; gg < GS; ++gg) alpha[gg] = readlane(a_lane, gg);
+    for (int gg = 0; gg < GS; ++gg) alpha[gg] = 1.0f;
+  }
   m_lane = m_new;
   float lsum = 0.0f;
 #pragma unroll
@@ -808,13 +829,13 @@ __device__ __forceinline__ void logits(const Basis<SP> &A, float *sw, int nb, in
       w1 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[1], A.bw[0][1], w1, 0, 0, 0);
       w2 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[2], A.bw[0][2], w2, 0, 0, 0);
       w3 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[3], A.bw[0][3], w3, 0, 0, 0);
-      // lane (hi, j = col) holds w of items ig*16 + 4 hi + i, coefficient j
-      if (col < S) {
+      // lane (hi, j = col) holds w of items ig*16 + 4 hi + i, coefficient j;
+      // lanes without a live (item, coefficient) store to the junk slots
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int it = ig * 16 + 4 * hi + i;
-          if (it < items) sw[(it % GS) * SWR + (it / GS) * S + col] = (w0[i] + w1[i]) + (w2[i] + w3[i]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int it = ig * 16 + 4 * hi + i;
+        const bool ok = col < S && it < items;
+        sw[ok ? (it % GS) * SWR + (it / GS) * S + col : GS * SWR + lane] = (w0[i] + w1[i]) + (w2[i] + w3[i]);
       }
     }
   }
@@ -857,7 +878,7 @@ struct Query {
 template <int D, int GS, int KF, int VF>
 struct WaveLds {
   using C = Cfg<D, GS, KF, VF>;
-  static constexpr int SW_BYTES = C::SWR * GS * 4;
+  static constexpr int SW_BYTES = C::SWR * GS * 4 + 64 * 4;   // + 64 junk slots for masked stores
   static constexpr int SC_BYTES = 2 * 64 * 4;
   static constexpr int VT_BYTES = C::VM ? C::SWR * D : 0;
   static constexpr int BYTES = SW_BYTES + SC_BYTES + VT_BYTES;
