@@ -167,7 +167,7 @@ template <int D, int GS, int KF, int VF>
 struct KBuf<D, GS, KF, VF, true> {   // MFMA layout: row 16*rg + lane%16, bytes 64*kk + 16*(lane/16) ..
   using C = Cfg<D, GS, KF, VF>;
   uint4 k[C::RG][C::KK];
-  float ks;                   // scale of row `lane` of the tile
+  float ks[C::RG];            // scale of row 16*rg + lane%16
 };
 template <int D, int GS, int KF, int VF, bool M = Cfg<D, GS, KF, VF>::VM>
 struct VBuf {                 // VALU layout (bf16 / fp32 rows)
@@ -204,7 +204,9 @@ __device__ __forceinline__ void issue_k(TileBuf<D, GS, KF, VF> &B, const TileRef
     for (int rg = 0; rg < C::RG; ++rg)
 #pragma unroll
       for (int kk = 0; kk < C::KK; ++kk) B.k.k[rg][kk] = bload128(rk, vk + 64 * kk, rg * 16 * D);
-    B.k.ks = bloadf(make_rsrc(T.ks, (uint32_t)T.nrows * 4), 4 * lane, 0);
+    const rsrc_t rs = make_rsrc(T.ks, (uint32_t)T.nrows * 4);
+#pragma unroll
+    for (int rg = 0; rg < C::RG; ++rg) B.k.ks[rg] = bloadf(rs, 4 * (lane % 16), 64 * rg);
   } else {
     const int rrk = lane / C::LK, ck = lane % C::LK;
     const uint32_t vk = (uint32_t)(rrk * D + ck * 16) * C::EBK;
@@ -268,12 +270,13 @@ __device__ __forceinline__ uint32_t pack_digits(uint32_t u0, uint32_t u1, uint32
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------ K phase (MFMA) --
-// Query of the key MFMA: B operand of v_mfma_i32_16x16x64_i8 for k step kk
-// and N block nb: column n = lane % 16 holds head 4*nb + n/4, digit n % 4 of
-// the query scaled to 22-bit integers; rows (bytes) are the same head_dim
+// Query of the key MFMA: A operand of v_mfma_i32_16x16x64_i8 for k step kk
+// and block nb: row n = lane % 16 holds head 4*nb + n/4, digit n % 4 of the
+// query scaled to 22-bit integers; the k bytes are the same head_dim
 // elements the codes of this lane hold.  cqq = scale * log2(e) / up for the
-// lane's head.  Every wave converts its own copy: the raw loads are issued
-// before the first tile's, the conversion runs once they have landed.
+// output head of the MFMA at this lane, 4*nb + lane/16.  Every wave converts
+// its own copy: the raw loads are issued before the first tile's, the
+// conversion runs once they have landed.
 template <int D, int GS>
 struct QRegMfma {
   static constexpr int KK = D / 64, NBN = cdiv(GS, 4);
@@ -326,20 +329,22 @@ struct QRegMfma {
                                 pack_digits(u[8], u[9], u[10], u[11], which),
                                 pack_digits(u[12], u[13], u[14], u[15], which));
       }
-      cqq[nb] = a.qk_scale * ldexpf(1.0f, E - 22);
+      // lane 4*(lane/16) holds head 4*nb + lane/16 in its row group
+      cqq[nb] = __shfl(a.qk_scale * ldexpf(1.0f, E - 22), 4 * (lane / 16), 64);
     }
   }
 };
 
 // s[g][row] = cqq[g] * kscale[row] * sum_d code[row][d] * qint[g][d] for the
-// tile's rows; the int32 MFMA sums are exact, digits are recombined in fp32.
+// tile's rows.  The query digits are the A operand (row 4*head + digit) and
+// the codes the B operand, so lane l receives the three digit sums of head
+// 4*nb + l/16 and row 16*rg + l%16 in its own registers; the int32 sums are
+// exact and recombined in fp32.  Absent heads store to the junk slots.
 template <int D, int GS, int SWR, int KF, int VF>
 __device__ __forceinline__ void kcompute_mfma(const KBuf<D, GS, KF, VF, true> &kb, int lane,
                                               const uint4 (&qB)[D / 64][cdiv(GS, 4)], const float (&cqq)[cdiv(GS, 4)],
-                                              float *sw, const float *sks) {
+                                              float *sw) {
   using C = Cfg<D, GS, KF, VF>;
-  const int n = lane % 16, G = lane / 16, which = n % 4;
-  const float wdig = which == 0 ? 1.0f : (which == 1 ? 256.0f : (which == 2 ? 65536.0f : 0.0f));
 #pragma unroll
   for (int rg = 0; rg < C::RG; ++rg) {
 #pragma unroll
@@ -347,22 +352,11 @@ __device__ __forceinline__ void kcompute_mfma(const KBuf<D, GS, KF, VF, true> &k
       v4i acc = {0, 0, 0, 0};
 #pragma unroll
       for (int kk = 0; kk < C::KK; ++kk)
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, kb.k[rg][kk]),
-                                                     __builtin_bit_cast(v4i, qB[kk][nb]), acc, 0, 0, 0);
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[i] = (float)acc[i] * wdig;
-        v[i] += dpp<0xB1>(v[i]);
-        v[i] += dpp<0x4E>(v[i]);
-      }
-      const int g = 4 * nb + n / 4;
-      if (which == 0 && g < GS) {
-        const float c = cqq[nb];
-        const float4 ks = *reinterpret_cast<const float4 *>(sks + 16 * rg + 4 * G);
-        *reinterpret_cast<float4 *>(sw + g * SWR + 16 * rg + 4 * G) =
-            make_float4(v[0] * ks.x * c, v[1] * ks.y * c, v[2] * ks.z * c, v[3] * ks.w * c);
-      }
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, qB[kk][nb]),
+                                                     __builtin_bit_cast(v4i, kb.k[rg][kk]), acc, 0, 0, 0);
+      const float sv = ((float)acc[0] + 256.0f * (float)acc[1]) + 65536.0f * (float)acc[2];
+      const int g = 4 * nb + lane / 16;
+      sw[g < GS ? g * SWR + 16 * rg + lane % 16 : GS * SWR + lane] = sv * kb.ks[rg] * cqq[nb];
     }
   }
 }
@@ -873,23 +867,21 @@ struct Query {
   float cqq[cdiv(GS, 4)];
 };
 
-// Per-wave LDS: scores / weights (head-major), the tile's K and V row
-// scales, and the int8 value tile of the MFMA path.
+// Per-wave LDS: scores / weights (head-major) and junk slots for masked
+// stores, the tile's V row scales, and the int8 value tile of the MFMA path.
 template <int D, int GS, int KF, int VF>
 struct WaveLds {
   using C = Cfg<D, GS, KF, VF>;
-  static constexpr int SW_BYTES = C::SWR * GS * 4 + 64 * 4;   // + 64 junk slots for masked stores
-  static constexpr int SC_BYTES = 2 * 64 * 4;
+  static constexpr int SW_BYTES = C::SWR * GS * 4 + 64 * 4;
+  static constexpr int SC_BYTES = 64 * 4;
   static constexpr int VT_BYTES = C::VM ? C::SWR * D : 0;
   static constexpr int BYTES = SW_BYTES + SC_BYTES + VT_BYTES;
   float *sw;
-  float *sks;
   float *svs;
   char *vl;
   __device__ __forceinline__ WaveLds(char *base) {
     sw = reinterpret_cast<float *>(base);
-    sks = reinterpret_cast<float *>(base + SW_BYTES);
-    svs = sks + 64;
+    svs = reinterpret_cast<float *>(base + SW_BYTES);
     vl = base + SW_BYTES + SC_BYTES;
   }
 };
@@ -899,9 +891,7 @@ __device__ __forceinline__ void process_k(const TileBuf<D, GS, KF, VF> &B, int n
                                           const WaveLds<D, GS, KF, VF> &L) {
   using C = Cfg<D, GS, KF, VF>;
   if constexpr (C::KM) {
-    L.sks[lane] = B.k.ks;
-    wave_lds_sync();
-    kcompute_mfma<D, GS, C::SWR, KF, VF>(B.k, lane, Q.qB, Q.cqq, L.sw, L.sks);
+    kcompute_mfma<D, GS, C::SWR, KF, VF>(B.k, lane, Q.qB, Q.cqq, L.sw);
   } else {
     kcompute<D, GS, C::SWR, KF, C::KSTEPS, C::KQ>(B.k.k, nrows, lane, Q.qh, Q.cq, L.sw);
   }
