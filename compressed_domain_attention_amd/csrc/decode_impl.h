@@ -1241,9 +1241,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   // ---- last arrival: every (head, column) loads the (max, sum) and the
   // partial of up to CB splits per round of device-scope loads (one round
   // for CB or fewer splits) and folds them into a running (max, sum, acc).
-  constexpr int CB = 32;
+  // The partial accumulators are read with system-scope (sc0 sc1) buffer
+  // loads: coherent across the XCDs like device-scope ones, and measured
+  // faster for this just-written data; the (max, sum) pairs, the same
+  // address across a wave, with device-scope loads.
+  constexpr int CB = 32, kSysScope = 1 | 16;
   const int ns = a.ns;
-  const float *Pacc = a.part_acc + pairq * ns * GS * D;
+  const rsrc_t racc = make_rsrc(a.part_acc + pairq * ns * GS * D, (uint32_t)ns * GS * D * 4);
   const float *Pml = a.part_ml + pairq * ns * GS * 2;
   for (int idx = tid; idx < GS * D; idx += NT) {
     const int g = idx / D, d = idx % D;
@@ -1255,7 +1259,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
         const int sp = sp0 + u < ns ? sp0 + u : ns - 1;   // in range; duplicates are masked below
         m[u] = __hip_atomic_load(Pml + 2 * (sp * GS + g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         l[u] = __hip_atomic_load(Pml + 2 * (sp * GS + g) + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        p[u] = __hip_atomic_load(Pacc + (int64_t)sp * GS * D + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        p[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(racc, 4 * (sp * GS * D + idx), 0, kSysScope));
       }
       float Mn = M;
 #pragma unroll
