@@ -43,6 +43,10 @@ Readings where the pages are silent (each also listed in the design notes)
 7. Softmax uses the natural exponential, max-subtracted; default
    scale = D ** -0.5 (triton_attention.py host wrapper).
 8. n = 0 complete blocks is allowed (tail-only attention); T = 0 is an error.
+9. The materialised view is the fp64 reconstruction rounded to the view's
+   format like a float row (reading 4); a crop that cuts into the archive
+   re-exposes the boundary block's first tokens from that view, in the
+   stream's raw format.
 """
 
 import math
@@ -208,6 +212,83 @@ def materialise(archive):
     C = dequantize(archive["rows"], archive["scales"], archive["fmt"])
     X = reconstruct(C, archive["R"])
     return np.concatenate([X, np.asarray(archive["tail"], dtype=np.float64)], axis=-2)
+
+
+def round_to(x, fmt):
+    """fp64 values rounded to a stored float format: float32 array for F32,
+    uint16 bf16 patterns (of the fp32 rounding) for BF16 (reading 4)."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if fmt == F32:
+        return x32
+    if fmt == BF16:
+        return f32_to_bf16_bits(x32)
+    raise ValueError(f"view format must be f32 or bf16, not {fmt!r}")
+
+
+def view(archive, out_fmt, block_begin=0):
+    """The reconstructed (materialised) view in a float format.
+
+    cache.py ``_CodecStream.read``: the archived blocks decoded (X_hat =
+    M^T C, ``reconstruct`` above: products of the fp32 basis and the
+    dequantised rows in fp64, summed over j = 0..S-1 from +0.0), restored to
+    the stream's dtype, then the raw tail.  ``_decode_pending`` decodes only
+    blocks archived since the last read; ``block_begin`` selects that range:
+    the result covers tokens block_begin*R .. n*R + t - 1.  Rounding fp64 ->
+    out_fmt follows reading 4 (bf16 through fp32).
+    """
+    R = archive["R"]
+    n = archive["n_blocks"]
+    rows = archive["rows"][..., block_begin:n, :, :]
+    scales = None if archive["scales"] is None else archive["scales"][..., block_begin:n, :]
+    X = reconstruct(dequantize(rows, scales, archive["fmt"]), R)
+    X = np.concatenate([X, np.asarray(archive["tail"], dtype=np.float64)], axis=-2)
+    return round_to(X, out_fmt)
+
+
+def crop(archive, new_len, raw_fmt):
+    """Remove trailing tokens exactly (cache.py ``_CodecStream.crop``).
+
+    With keep = new_len, keep_blocks = keep // R and t = keep mod R:
+    archived blocks below keep_blocks stay verbatim (never re-compressed);
+    when the cut falls inside the archive, the block at the boundary leaves
+    it and its first t tokens become the raw tail, taken from the decoded
+    view in the stream's dtype (raw_fmt); when it falls inside the raw tail,
+    the tail is truncated.  Returns a new archive dict (tail as fp64 values).
+    """
+    R = archive["R"]
+    n = archive["n_blocks"]
+    t_old = archive["tail"].shape[-2]
+    if not (0 <= new_len <= n * R + t_old):
+        raise ValueError("crop keeps between 0 and all tokens")
+    kb, t = divmod(new_len, R)
+    out = dict(archive)
+    if kb < n:
+        blk = dict(archive)
+        blk["rows"] = archive["rows"][..., kb:kb + 1, :, :]
+        blk["scales"] = None if archive["scales"] is None else archive["scales"][..., kb:kb + 1, :]
+        blk["n_blocks"] = 1
+        blk["tail"] = archive["tail"][..., :0, :]
+        v = view(blk, raw_fmt)[..., :t, :]
+        tail = v.astype(np.float64) if raw_fmt == F32 else bf16_bits_to_f64(v)
+        out["rows"] = archive["rows"][..., :kb, :, :].copy()
+        out["scales"] = None if archive["scales"] is None else archive["scales"][..., :kb, :].copy()
+        out["n_blocks"] = kb
+        out["tail"] = tail
+    else:
+        out["tail"] = np.asarray(archive["tail"], dtype=np.float64)[..., :t, :].copy()
+    return out
+
+
+def select_batch(archive, idx):
+    """Gather batch rows (cache.py ``_CodecStream.select_batch``, beam
+    reorder): row i of the result is row idx[i] of the archive, for the
+    archived rows, their scales and the raw tail alike."""
+    idx = np.asarray(idx, dtype=np.int64)
+    out = dict(archive)
+    out["rows"] = archive["rows"][idx].copy()
+    out["scales"] = None if archive["scales"] is None else archive["scales"][idx].copy()
+    out["tail"] = np.asarray(archive["tail"])[idx].copy()
+    return out
 
 
 def attention(q, K, V, scale):

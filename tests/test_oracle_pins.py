@@ -309,3 +309,130 @@ def test_storage_matches_printed_tables(golden_dir):
             raw = 2 * BH * seq * D * 4
             assert abs(comp / 2 ** 20 - mb) <= 0.05 + 1e-9, row
             assert abs(comp / raw - ratio) <= 0.005 + 1e-9, row
+
+
+# ------------------------------------------------ view / crop / batch gather ----
+def _bf16_values(x):
+    return O.bf16_bits_to_f64(O.f32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
+
+
+def _f32_archive(x, R, S):
+    return O.encode(np.asarray(x, dtype=np.float32).astype(np.float64), R, S, O.F32)
+
+
+@pytest.mark.parametrize("R", [1, 2, 4, 8, 16])
+def test_view_all_frequencies_returns_tokens(R):
+    # S = R with fp32 rows: the orthonormal inverse gives the tokens back up
+    # to the fp32 rounding of rows and basis (a transposed basis or a wrong
+    # sum would miss by O(1)).
+    rng = np.random.default_rng(R)
+    x = rng.standard_normal((2, 3, 5 * R + 3, 8)).astype(np.float32)
+    a = _f32_archive(x, R, R)
+    v = O.view(a, O.F32)
+    assert v.shape == x.shape and v.dtype == np.float32
+    err = np.abs(v.astype(np.float64) - x).max()
+    assert err <= 4 * R * 2.0 ** -24 * np.abs(x).max() + 1e-7
+    # the raw tail comes back verbatim
+    nR = (x.shape[-2] // R) * R
+    assert np.array_equal(v[..., nR:, :], x[..., nR:, :])
+
+
+@pytest.mark.parametrize("R,S", [(8, 2), (16, 4), (12, 5)])
+def test_view_equals_scipy_idct_of_kept_rows(R, S):
+    # Block synthesis = inverse orthonormal DCT-II (scipy's type-2 'ortho'
+    # inverse) of the kept rows padded with zeros.
+    rng = np.random.default_rng(R + S)
+    x = rng.standard_normal((1, 1, 4 * R, 6))
+    a = _f32_archive(x, R, S)
+    rows = a["rows"].astype(np.float64)                      # (1,1,4,S,6)
+    pad = np.zeros((1, 1, 4, R, 6))
+    pad[..., :S, :] = rows
+    ref = scipy.fft.idct(pad, type=2, norm="ortho", axis=3).reshape(1, 1, 4 * R, 6)
+    v = O.view(a, O.F32).astype(np.float64)
+    assert np.abs(v - ref).max() <= 8 * R * 2.0 ** -24 * (np.abs(rows).max() + 1)
+
+
+def test_view_identity_codec_is_exact():
+    # R = S = 1: M = [1], the view is the stored rows bit for bit.
+    x = np.random.default_rng(3).standard_normal((2, 2, 9, 8)).astype(np.float32)
+    a = _f32_archive(x, 1, 1)
+    assert np.array_equal(O.view(a, O.F32), x)
+
+
+@pytest.mark.parametrize("fmt", [O.F32, O.BF16, O.I8])
+def test_view_prefix_is_append_only(fmt):
+    # Causal-safety design: the decoded prefix never changes as tokens are
+    # appended, and decoding only the blocks since block k gives the same
+    # values as the full decode from token k*R on (the memoised read).
+    R, S = 8, 3
+    x = _bf16_values(np.random.default_rng(5).standard_normal((2, 2, 70, 16)))
+    st = O.Stream(R, S, fmt)
+    st.append(x[..., :37, :])
+    v1 = O.view(st.archive(), O.BF16)
+    st.append(x[..., 37:, :])
+    a2 = st.archive()
+    v2 = O.view(a2, O.BF16)
+    assert np.array_equal(v2[..., :32, :], v1[..., :32, :])
+    assert np.array_equal(O.view(a2, O.BF16, block_begin=3), v2[..., 24:, :])
+
+
+def test_crop_cases_by_hand():
+    R, S = 4, 4                                   # lossless, fp32 rows
+    x = np.arange(2 * 1 * 14 * 2, dtype=np.float64).reshape(2, 1, 14, 2) / 8.0
+    a = _f32_archive(x, R, S)                     # 3 blocks + 2 tail tokens
+    # into the raw tail: plain truncation
+    c = O.crop(a, 13, O.F32)
+    assert c["n_blocks"] == 3 and np.array_equal(c["tail"], x[..., 12:13, :])
+    # at a block boundary: archive prefix verbatim, empty tail
+    c = O.crop(a, 8, O.F32)
+    assert c["n_blocks"] == 2 and c["tail"].shape[-2] == 0
+    assert np.array_equal(c["rows"], a["rows"][..., :2, :, :])
+    # into the archive: the boundary block's tokens come back (lossless here)
+    c = O.crop(a, 6, O.F32)
+    assert c["n_blocks"] == 1 and c["tail"].shape[-2] == 2
+    np.testing.assert_allclose(c["tail"], x[..., 4:6, :], rtol=0, atol=1e-5)
+    # nothing left
+    c = O.crop(a, 0, O.F32)
+    assert c["n_blocks"] == 0 and c["tail"].shape[-2] == 0
+    with pytest.raises(ValueError):
+        O.crop(a, 15, O.F32)
+
+
+@pytest.mark.parametrize("fmt", [O.BF16, O.I8])
+def test_crop_is_path_independent_and_idempotent(fmt):
+    # README / cache.py: a crop never re-compresses the history, so repeated
+    # crops are idempotent and crops compose: crop(crop(a, L1), L2) = crop(a, L2).
+    R, S = 8, 2
+    x = _bf16_values(np.random.default_rng(9).standard_normal((2, 2, 45, 16)))
+    a = O.encode(x, R, S, fmt)
+    for L1 in (45, 40, 37, 16, 9):
+        c1 = O.crop(a, L1, O.BF16)
+        c11 = O.crop(c1, L1, O.BF16)
+        for k in ("rows", "tail"):
+            assert np.array_equal(c11[k], c1[k])
+        for L2 in range(0, L1 + 1, 3):
+            d1, d2 = O.crop(c1, L2, O.BF16), O.crop(a, L2, O.BF16)
+            assert d1["n_blocks"] == d2["n_blocks"]
+            for k in ("rows", "scales", "tail"):
+                if d1[k] is not None:
+                    assert np.array_equal(d1[k], d2[k]), (L1, L2, k)
+    # the re-exposed tail is the view of the same tokens, in the raw format
+    c = O.crop(a, 21, O.BF16)
+    assert np.array_equal(O.f32_to_bf16_bits(c["tail"]), O.view(a, O.BF16)[..., 16:21, :])
+
+
+def test_select_batch_invariants():
+    R, S = 8, 2
+    x = _bf16_values(np.random.default_rng(11).standard_normal((4, 2, 30, 16)))
+    a = O.encode(x, R, S, O.I8)
+    same = O.select_batch(a, [0, 1, 2, 3])
+    for k in ("rows", "scales", "tail"):
+        assert np.array_equal(same[k], a[k])
+    # gathering commutes with decoding: the view of a gathered archive is the
+    # gathered view (and so is the archive of gathered tokens)
+    idx = [3, 3, 0, 2, 1]
+    g = O.select_batch(a, idx)
+    assert np.array_equal(O.view(g, O.BF16), O.view(a, O.BF16)[idx])
+    e = O.encode(x[idx], R, S, O.I8)
+    for k in ("rows", "scales", "tail"):
+        assert np.array_equal(g[k], e[k])
