@@ -66,10 +66,14 @@ def _lib():
         lib.codec_decode_workspace_bytes.argtypes = [P, P, i64, ctypes.POINTER(ctypes.c_size_t)]
         lib.codec_decode_attention.argtypes = [vp, LP, i64, P, P, f32, vp, LP, i32,
                                                vp, ctypes.c_size_t, vp]
+        lib.codec_materialise.argtypes = [P, i64, vp, LP, i32, vp]
+        lib.codec_crop.argtypes = [P, i64, vp]
+        lib.codec_select_batch.argtypes = [P, P, LP, i64, vp]
         lib.codec_status_string.argtypes = [ctypes.c_int]
         lib.codec_status_string.restype = ctypes.c_char_p
         for name in ("codec_basis", "codec_encode_blocks", "codec_append_step",
-                     "codec_decode_workspace_bytes", "codec_decode_attention"):
+                     "codec_decode_workspace_bytes", "codec_decode_attention",
+                     "codec_materialise", "codec_crop", "codec_select_batch"):
             getattr(lib, name).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -120,6 +124,7 @@ class CodecStream:
         self.tail = torch.zeros((self.B, self.H, self.R, self.D), dtype=_TORCH_DTYPE[self.raw_dtype],
                                 device=self.device)
         self._grow(max(int(capacity), INITIAL_BLOCKS))
+        self.discard_view()
 
     # cache.py ``_CodecStream._grow``: start at 16 blocks and double until the
     # request fits; archived blocks are copied over verbatim.
@@ -166,6 +171,44 @@ class CodecStream:
         """Archive a (B, H, T, D) run of raw tokens; the tail must be empty."""
         return encode_blocks(self, x, stream)
 
+    # ---- the materialised view (cache.py ``read`` / ``_decode_pending``)
+    def discard_view(self):
+        """Drop the memoised view (rebuilt on the next ``read``)."""
+        self._rec, self._rec_blocks, self._rec_cap = None, 0, 0
+
+    def read(self, dtype=None, stream=None):
+        """The decoded (B, H, seq_len, D) view in the raw dtype (or `dtype`).
+
+        Memoised and append-only: only blocks archived since the last read
+        are decoded (codec_materialise from the memo's block count), then the
+        raw tail is written after them.  The archived prefix of a returned
+        tensor never changes; its last n_tail tokens are rewritten by later
+        reads once more tokens arrive.
+        """
+        fmt = self.raw_dtype if dtype is None else _fmt(dtype)
+        tdt = _TORCH_DTYPE[fmt]
+        if self._rec is not None and self._rec.dtype != tdt:
+            self.discard_view()
+        need = self.seq_len
+        if self._rec is None or self._rec_cap < need:
+            cap = max(need, 2 * self._rec_cap, INITIAL_BLOCKS * self.R)
+            new = torch.empty((self.B, self.H, cap, self.D), dtype=tdt, device=self.device)
+            done = self._rec_blocks * self.R
+            if self._rec is not None and done:
+                new[:, :, :done].copy_(self._rec[:, :, :done])
+            self._rec, self._rec_cap = new, cap
+        materialise(self, self._rec, block_begin=self._rec_blocks, stream=stream)
+        self._rec_blocks = self.n_blocks
+        return self._rec[:, :, :need]
+
+    def crop(self, new_len, stream=None):
+        """Keep the first new_len tokens exactly (codec_crop)."""
+        crop(self, new_len, stream)
+
+    def select_batch(self, idx, stream=None):
+        """Gather batch rows idx (beam reorder) into new buffers (codec_select_batch)."""
+        select_batch(self, idx, stream)
+
 
 def encode_blocks(s, x, stream=None):
     if x.dtype != _TORCH_DTYPE[s.raw_dtype] or x.dim() != 4 or x.stride(3) != 1:
@@ -196,6 +239,51 @@ def append_step(k, v, k_new, v_new, stream=None):
                                     st), "codec_append_step")
     k._sync(dk)
     v._sync(dv)
+
+
+def materialise(s, dst, block_begin=0, stream=None):
+    """Decode blocks block_begin.. of s into dst (B, H, >= seq_len, D) and
+    write the raw tail after them (codec_materialise)."""
+    if dst.dim() != 4 or dst.stride(3) != 1 or dst.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("dst must be (B, H, T, D) float32 / bfloat16 with unit d stride")
+    fmt = FMT_F32 if dst.dtype == torch.float32 else FMT_BF16
+    d = s._desc()
+    st = _hip_stream(s.device) if stream is None else ctypes.c_void_p(stream)
+    _check(_lib().codec_materialise(ctypes.byref(d), int(block_begin), ctypes.c_void_p(dst.data_ptr()),
+                                    _I64_3(dst.stride(0), dst.stride(1), dst.stride(2)), fmt, st),
+           "codec_materialise")
+    return dst
+
+
+def crop(s, new_len, stream=None):
+    d = s._desc()
+    st = _hip_stream(s.device) if stream is None else ctypes.c_void_p(stream)
+    _check(_lib().codec_crop(ctypes.byref(d), int(new_len), st), "codec_crop")
+    s._sync(d)
+    s._rec_blocks = min(s._rec_blocks, s.n_blocks)
+
+
+def select_batch(s, idx, stream=None):
+    """Batch row i of s becomes its old row idx[i]; new buffers are allocated
+    (rows keep their capacity), the memoised view is dropped."""
+    idx = [int(i) for i in (idx.tolist() if hasattr(idx, "tolist") else idx)]
+    n = len(idx)
+    rows = torch.empty((n, s.H, s.capacity, s.S, s.D), dtype=_TORCH_DTYPE[s.fmt], device=s.device)
+    scales = (torch.empty((n, s.H, s.capacity, s.S), dtype=torch.float32, device=s.device)
+              if s.fmt == FMT_I8 else None)
+    tail = torch.empty((n, s.H, s.R, s.D), dtype=_TORCH_DTYPE[s.raw_dtype], device=s.device)
+    src = s._desc()
+    dst = s._desc()
+    dst.batch = n
+    dst.rows = rows.data_ptr()
+    dst.scales = scales.data_ptr() if scales is not None else None
+    dst.tail = tail.data_ptr()
+    ia = (ctypes.c_int64 * max(n, 1))(*idx)
+    st = _hip_stream(s.device) if stream is None else ctypes.c_void_p(stream)
+    _check(_lib().codec_select_batch(ctypes.byref(src), ctypes.byref(dst), ia, n, st), "codec_select_batch")
+    s.B, s.rows, s.scales, s.tail = n, rows, scales, tail
+    s._sync(dst)
+    s.discard_view()
 
 
 def decode_workspace_bytes(k, v, Hq):

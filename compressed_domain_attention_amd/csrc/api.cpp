@@ -346,4 +346,137 @@ int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
   return CODEC_OK;
 }
 
+namespace {
+
+// Arguments of the view kernel for one stream (rows, scales, tail, basis).
+ViewArgs stream_view_args(const codec_stream *s) {
+  ViewArgs a;
+  memset(&a, 0, sizeof(a));
+  a.rows = s->rows;
+  a.scales = s->scales;
+  a.tail = s->tail;
+  a.rf = s->fmt;
+  a.raw = s->raw_dtype;
+  a.R = s->block;
+  a.S = s->keep;
+  a.D = s->head_dim;
+  a.H = s->heads;
+  a.BH = s->batch * s->heads;
+  a.cap = s->capacity;
+  for (int i = 0; i < s->block; ++i)
+    for (int j = 0; j < s->keep; ++j) a.A[i * s->keep + j] = (float)basis_entry(s->block, j, i);
+  return a;
+}
+
+}  // namespace
+
+int codec_materialise(const codec_stream *s, int64_t block_begin, void *dst, const int64_t dst_stride[3],
+                      int32_t dst_dtype, hipStream_t stream) {
+  int rc = check_stream(s);
+  if (rc) return rc;
+  if (!dst || !dst_stride) return CODEC_ERR_NULL;
+  if (!raw_ok(dst_dtype)) return CODEC_ERR_FORMAT;
+  if (block_begin < 0 || block_begin > s->n_blocks) return CODEC_ERR_STATE;
+  if (!aligned16(dst)) return CODEC_ERR_SHAPE;
+  for (int i = 0; i < 3; ++i)
+    if (dst_stride[i] < 0 || dst_stride[i] % 8 != 0) return CODEC_ERR_SHAPE;
+  ViewArgs a = stream_view_args(s);
+  a.out = dst_dtype;
+  a.blk0 = block_begin;
+  a.nblk = s->n_blocks - block_begin;
+  a.tok_limit = s->block;
+  a.n_copy = s->n_tail;
+  a.dst = dst;
+  a.o_sb = dst_stride[0];
+  a.o_sh = dst_stride[1];
+  a.o_st = dst_stride[2];
+  a.o_t0 = block_begin * s->block;
+  (void)hipGetLastError();
+  if (launch_view(a, stream) != 0) return CODEC_ERR_HIP;
+  return CODEC_OK;
+}
+
+int codec_crop(codec_stream *s, int64_t new_len, hipStream_t stream) {
+  int rc = check_stream(s);
+  if (rc) return rc;
+  const int64_t R = s->block;
+  if (new_len < 0 || new_len > s->n_blocks * R + s->n_tail) return CODEC_ERR_STATE;
+  const int64_t kb = new_len / R;
+  const int32_t t = (int32_t)(new_len % R);
+  if (kb < s->n_blocks && t > 0) {
+    // the boundary block's first t tokens, decoded into tail slots 0..t-1
+    ViewArgs a = stream_view_args(s);
+    a.out = s->raw_dtype;
+    a.blk0 = kb;
+    a.nblk = 1;
+    a.tok_limit = t;
+    a.n_copy = 0;
+    a.dst = s->tail;
+    a.o_sb = s->heads * R * s->head_dim;
+    a.o_sh = R * s->head_dim;
+    a.o_st = s->head_dim;
+    a.o_t0 = 0;
+    (void)hipGetLastError();
+    if (launch_view(a, stream) != 0) return CODEC_ERR_HIP;
+  }
+  if (kb < s->n_blocks) s->n_blocks = kb;
+  s->n_tail = t;
+  return CODEC_OK;
+}
+
+int codec_select_batch(const codec_stream *src, codec_stream *dst, const int64_t *idx, int64_t n,
+                       hipStream_t stream) {
+  int rc = check_stream(src);
+  if (rc) return rc;
+  if (!dst || !idx) return CODEC_ERR_NULL;
+  if (n < 1 || dst->batch != n) return CODEC_ERR_SHAPE;
+  if (dst->heads != src->heads || dst->block != src->block || dst->keep != src->keep ||
+      dst->head_dim != src->head_dim)
+    return CODEC_ERR_SHAPE;
+  if (dst->fmt != src->fmt || dst->raw_dtype != src->raw_dtype) return CODEC_ERR_FORMAT;
+  if (!dst->tail || (src->n_blocks > 0 && !dst->rows) ||
+      (src->n_blocks > 0 && src->fmt == CODEC_I8 && !dst->scales))
+    return CODEC_ERR_NULL;
+  if (dst->capacity < src->n_blocks) return CODEC_ERR_CAPACITY;
+  if (!aligned16(dst->tail) || (dst->rows && !aligned16(dst->rows)) ||
+      (dst->fmt == CODEC_I8 && dst->scales && !aligned16(dst->scales)))
+    return CODEC_ERR_SHAPE;
+  for (int64_t i = 0; i < n; ++i)
+    if (idx[i] < 0 || idx[i] >= src->batch) return CODEC_ERR_SHAPE;
+  const int64_t H = src->heads, S = src->keep, D = src->head_dim;
+  const int64_t eb = elem_bytes(src->fmt);
+  GatherArgs g;
+  memset(&g, 0, sizeof(g));
+  g.src_rows = src->rows;
+  g.dst_rows = dst->rows;
+  g.slab_bytes = src->capacity * S * D * eb;
+  g.dst_slab_bytes = dst->capacity * S * D * eb;
+  g.row_bytes = src->n_blocks * S * D * eb;
+  if (src->fmt == CODEC_I8 && src->n_blocks > 0) {
+    g.src_scales = src->scales;
+    g.dst_scales = dst->scales;
+    g.scale_slab = src->capacity * S;
+    g.dst_scale_slab = dst->capacity * S;
+    g.n_scales = src->n_blocks * S;
+  }
+  g.src_tail = src->tail;
+  g.dst_tail = dst->tail;
+  g.tail_bytes = (int64_t)src->block * D * elem_bytes(src->raw_dtype);
+  g.H = H;
+  // destination rows in chunks: at most kGatherChunk indices and 65535 (row, head) units per launch
+  int64_t chunk = kGatherChunk;
+  if (chunk * H > 65535) chunk = 65535 / H;
+  if (chunk < 1) return CODEC_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  for (int64_t i0 = 0; i0 < n; i0 += chunk) {
+    const int64_t m = n - i0 < chunk ? n - i0 : chunk;
+    g.i0 = i0;
+    for (int64_t k = 0; k < m; ++k) g.idx[k] = (int32_t)idx[i0 + k];
+    if (launch_gather(g, m * H, stream) != 0) return CODEC_ERR_HIP;
+  }
+  dst->n_blocks = src->n_blocks;
+  dst->n_tail = src->n_tail;
+  return CODEC_OK;
+}
+
 }  // extern "C"

@@ -57,6 +57,45 @@ struct AppendArgs {
 int launch_encode(int D, const EncodeLaunch &a, int64_t BH, hipStream_t stream);
 int launch_append(int D, const AppendArgs &a, int64_t BH, hipStream_t stream);
 
+// ------------------------------------------------------ view, crop, gather --
+// Decoded view: blocks blk0 .. blk0+nblk-1 of every (b, h); token i of block
+// n goes to dst token (n - blk0)*R + i + o_t0 (i < tok_limit); then, if
+// n_copy > 0, tail slots 0..n_copy-1 go to dst tokens nblk*R + o_t0 + i.
+struct ViewArgs {
+  const void *rows;       // [BH][cap][S][D] of rf
+  const float *scales;    // [BH][cap][S] (I8)
+  const void *tail;       // [BH][R][D] of raw
+  int32_t rf, raw, out;   // row, tail and view formats
+  int32_t R, S, D;
+  int64_t H, BH, cap;
+  int64_t blk0, nblk;
+  int32_t tok_limit;
+  int32_t n_copy;
+  void *dst;
+  int64_t o_sb, o_sh, o_st, o_t0;
+  float A[kMaxR * kMaxS]; // synthesis basis, A[i*S + j] = fp32(M[j][i])
+};
+
+constexpr int kGatherChunk = 256;   // destination batch rows per gather launch
+
+// Batch gather of up to kGatherChunk destination rows i0 .. i0+n-1.
+struct GatherArgs {
+  const void *src_rows;
+  void *dst_rows;
+  int64_t slab_bytes, dst_slab_bytes, row_bytes;   // per (b, h): allocated, allocated, used
+  const float *src_scales;                         // NULL unless I8
+  float *dst_scales;
+  int64_t scale_slab, dst_scale_slab, n_scales;    // floats
+  const void *src_tail;
+  void *dst_tail;
+  int64_t tail_bytes;                              // all R slots
+  int64_t H, i0;
+  int32_t idx[kGatherChunk];                       // source batch row of destination row i0 + k
+};
+
+int launch_view(const ViewArgs &a, hipStream_t stream);
+int launch_gather(const GatherArgs &g, int64_t n_units, hipStream_t stream);
+
 // ---------------------------------------------------------------- decode --
 struct DecodeArgs {
   const uint16_t *q;      // bf16 (B, Hq, 1, D)

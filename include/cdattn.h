@@ -188,6 +188,67 @@ int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
                            void *out, const int64_t out_stride[2], int32_t out_dtype,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * codec_materialise -- the decoded (materialised) view of a stream, e.g. for
+ * prefill attention.  cache.py ``_CodecStream.read`` / ``_decode_pending``:
+ * the view is the archived blocks decoded, X_hat = M^T C block by block
+ * (README "Math"), followed by the raw tail, in the stream's dtype; it is
+ * memoised and append-only (README "Causal-safety design": archived blocks
+ * never change), so a read only decodes the blocks archived since the last.
+ * This call decodes blocks block_begin .. n_blocks-1 into dst tokens
+ * block_begin*R .. n_blocks*R-1 and copies the n_tail raw tokens to dst
+ * tokens n_blocks*R .. n_blocks*R+n_tail-1; dst tokens below block_begin*R
+ * are not touched.
+ * Arithmetic (bit-exact contract): x_hat = sum over j = 0..S-1, in order,
+ * from +0.0, of fp64(A[i][j]) * c_hat[j] with separately rounded fp64
+ * products and sums (no fused multiply-add); c_hat = fp64(code) *
+ * fp64(scale) for int8 rows (exact), the stored value for float rows.
+ * Output fp32(x_hat), or bf16(fp32(x_hat)) (RNE); tail tokens converted
+ * (bf16 -> fp32 exact, fp32 -> bf16 RNE).
+ *   s            the stream (not modified).
+ *   block_begin  0 .. n_blocks (n_blocks: only the tail is written).
+ *   dst          device, (B, H, >= n_blocks*R + n_tail, D) of dst_dtype,
+ *                16-byte aligned; dst_stride = element strides of the b, h
+ *                and t axes, each a multiple of 8 (d is contiguous).
+ *   dst_dtype    CODEC_F32 | CODEC_BF16.
+ * Errors: NULL, SHAPE, FORMAT, STATE (block_begin out of range), HIP.
+ */
+int codec_materialise(const codec_stream *s, int64_t block_begin, void *dst, const int64_t dst_stride[3],
+                      int32_t dst_dtype, hipStream_t stream);
+
+/*
+ * codec_crop -- remove trailing tokens exactly (cache.py
+ * ``_CodecStream.crop``).  With kb = new_len / R and t = new_len mod R:
+ *   kb <  n_blocks: blocks kb .. leave the archive (their rows are left as
+ *                   they are); when t > 0 the first t tokens of block kb,
+ *                   decoded as in codec_materialise into the raw dtype,
+ *                   become tail slots 0..t-1; n_blocks = kb, n_tail = t.
+ *   kb == n_blocks: the cut is inside the raw tail: n_tail = t (no launch).
+ * Archived blocks below kb are never re-encoded, so repeated crops are
+ * idempotent and crops compose (crop to L1, then to L2 <= L1, equals crop
+ * to L2).
+ *   s        the stream; counters change only on success.
+ *   new_len  tokens to keep, 0 .. n_blocks*R + n_tail.
+ * Errors: NULL, SHAPE, FORMAT, STATE (new_len out of range), HIP.
+ */
+int codec_crop(codec_stream *s, int64_t new_len, hipStream_t stream);
+
+/*
+ * codec_select_batch -- gather rows of the batch axis (beam reorder; cache.py
+ * ``_CodecStream.select_batch``).  Batch row i of dst becomes batch row
+ * idx[i] of src: archived rows 0..n_blocks-1, their scales and all R tail
+ * slots; dst's n_blocks and n_tail are set to src's.
+ *   src   stream, not modified.
+ *   dst   stream with batch == n and the same heads, R, S, D, fmt and
+ *         raw_dtype, capacity >= src->n_blocks; its buffers must not
+ *         overlap src's (gathering in place needs new buffers).
+ *   idx   HOST array of n source batch rows, each in [0, src->batch).
+ * Errors: NULL, SHAPE (geometry or an index out of range), FORMAT,
+ * CAPACITY, UNSUPPORTED (more than 65535 heads), HIP.
+ */
+int codec_select_batch(const codec_stream *src, codec_stream *dst, const int64_t *idx, int64_t n,
+                       hipStream_t stream);
+
 /* codec_status_string -- static text for a status code (never NULL). */
 const char *codec_status_string(int status);
 

@@ -37,7 +37,8 @@ def declared_functions():
 def test_header_symbols_exported(lib):
     names = declared_functions()
     assert set(names) == {"codec_basis", "codec_encode_blocks", "codec_append_step",
-                          "codec_decode_workspace_bytes", "codec_decode_attention", "codec_status_string"}
+                          "codec_decode_workspace_bytes", "codec_decode_attention", "codec_status_string",
+                          "codec_materialise", "codec_crop", "codec_select_batch"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -181,3 +182,68 @@ def test_decode_validation(lib):
     assert dec(qs=bd._I64_2(2048, 100)) == SHAPE
     assert dec(vv=stream(n_blocks=16, capacity=16, keep=3)) == SHAPE
     assert dec(kk=stream(), vv=stream()) == SHAPE
+
+
+def test_materialise_validation(lib):
+    three = bd._I64_3(8192, 2048, 128)
+
+    def mat(s, b0=0, dst=FAKE, st=three, odt=bd.FMT_BF16):
+        return lib.codec_materialise(ctypes.byref(s) if s is not None else None, b0, dst, st, odt, None)
+
+    s = stream(n_blocks=4, capacity=16)
+    assert mat(None) == NULL
+    assert mat(s, dst=None) == NULL
+    assert lib.codec_materialise(ctypes.byref(s), 0, FAKE, None, bd.FMT_BF16, None) == NULL
+    assert mat(s, odt=bd.FMT_I8) == FORMAT
+    assert mat(s, b0=-1) == STATE
+    assert mat(s, b0=5) == STATE
+    assert mat(s, dst=FAKE + 8) == SHAPE
+    assert mat(s, st=bd._I64_3(8192, 2048, 130)) == SHAPE
+    assert mat(stream(fmt=9)) == FORMAT
+    assert (s.n_blocks, s.n_tail) == (4, 0)
+    # nothing to write (no new blocks, empty tail): succeeds without a launch
+    assert mat(s, b0=4) == OK
+
+
+def test_crop_validation_and_host_only_cases(lib):
+    s = stream(n_blocks=4, capacity=16, n_tail=3)       # 35 tokens
+    assert lib.codec_crop(None, 3, None) == NULL
+    assert lib.codec_crop(ctypes.byref(s), -1, None) == STATE
+    assert lib.codec_crop(ctypes.byref(s), 36, None) == STATE
+    assert (s.n_blocks, s.n_tail) == (4, 3)
+    # inside the raw tail: counters only
+    assert lib.codec_crop(ctypes.byref(s), 34, None) == OK
+    assert (s.n_blocks, s.n_tail) == (4, 2)
+    # on a block boundary: counters only (archived rows are left as they are)
+    assert lib.codec_crop(ctypes.byref(s), 16, None) == OK
+    assert (s.n_blocks, s.n_tail) == (2, 0)
+    assert lib.codec_crop(ctypes.byref(s), 16, None) == OK
+    assert (s.n_blocks, s.n_tail) == (2, 0)
+    assert lib.codec_crop(ctypes.byref(s), 0, None) == OK
+    assert (s.n_blocks, s.n_tail) == (0, 0)
+
+
+def test_select_batch_validation(lib):
+    src = stream(n_blocks=4, capacity=16)
+    idx = (ctypes.c_int64 * 3)(1, 0, 1)
+
+    def sel(dst, ix=idx, n=3, s=src):
+        return lib.codec_select_batch(ctypes.byref(s), ctypes.byref(dst) if dst is not None else None, ix, n, None)
+
+    assert sel(None) == NULL
+    assert sel(stream(batch=3), ix=None) == NULL
+    assert sel(stream(batch=2)) == SHAPE                      # dst batch != n
+    assert sel(stream(batch=3), n=0) == SHAPE
+    assert sel(stream(batch=3, heads=2)) == SHAPE
+    assert sel(stream(batch=3, keep=3)) == SHAPE
+    assert sel(stream(batch=3, fmt=bd.FMT_BF16)) == FORMAT
+    assert sel(stream(batch=3, raw_dtype=bd.FMT_F32)) == FORMAT
+    assert sel(stream(batch=3, capacity=3)) == CAPACITY
+    assert sel(stream(batch=3, rows=None)) == NULL
+    assert sel(stream(batch=3, tail=FAKE + 4)) == SHAPE
+    assert sel(stream(batch=3), ix=(ctypes.c_int64 * 3)(0, 2, 1)) == SHAPE   # index out of range
+    assert sel(stream(batch=3), ix=(ctypes.c_int64 * 3)(0, -1, 1)) == SHAPE
+    d = stream(batch=3)
+    before = (d.n_blocks, d.n_tail)
+    assert sel(d, ix=(ctypes.c_int64 * 3)(0, 5, 1)) == SHAPE
+    assert (d.n_blocks, d.n_tail) == before
