@@ -129,6 +129,58 @@ def traffic_summary(w, fetch_csv, write_csv, command):
     print(json.dumps(d, indent=1))
 
 
+def view_bytes(w, fmt, n_blocks, n_tail, out_bytes=2):
+    """Algorithmic bytes of one full materialised view of a stream: rows (+
+    scales) and tail read, every token written in the view format."""
+    per_bh = n_blocks * w.S * (w.D * EB[fmt] + (4 if fmt == "i8" else 0)) + n_tail * w.D * 2 \
+        + (n_blocks * w.R + n_tail) * w.D * out_bytes
+    return w.B * w.Hkv * per_bh
+
+
+def archive_ops(w, streams, dev, rounds=3):
+    """Timings of the structural archive operations on the workload's
+    streams (each layer's key stream, rotated so reads come from HBM):
+    the full bf16 materialised view (codec_materialise from block 0) and a
+    batch gather of every row (codec_select_batch, reversed order)."""
+    L = len(streams)
+    ks0 = streams[0][0]
+    n, t = ks0.n_blocks, ks0.n_tail
+    views = [torch.empty((w.B, w.Hkv, n * w.R + t, w.D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    for li in range(L):
+        cda.materialise(streams[li][0], views[li], block_begin=0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(rounds):
+        for li in range(L):
+            cda.materialise(streams[li][0], views[li], block_begin=0)
+    e1.record()
+    torch.cuda.synchronize()
+    v_us = e0.elapsed_time(e1) * 1e3 / (rounds * L)
+    vb = view_bytes(w, w.kfmt, n, t)
+    del views
+    # gather: every batch row, reversed, of each layer's key stream into new buffers
+    idx = list(range(w.B))[::-1]
+    gb = 2 * (w.B * w.Hkv * (n * w.S * (w.D * EB[w.kfmt] + (4 if w.kfmt == "i8" else 0)) + w.R * w.D * 2))
+    g_ms = []
+    for li in range(L):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        streams[li][0].select_batch(idx)
+        b.record()
+        torch.cuda.synchronize()
+        g_ms.append(a.elapsed_time(b))
+    g_us = float(np.median(g_ms)) * 1e3
+    return {"materialise": {"kernel": "view_kernel", "avg_us": round(v_us, 3), "bytes": vb,
+                            "GBps": round(vb / (v_us * 1e-6) / 1e9, 2),
+                            "hbm_peak_fraction": round(vb / (v_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "what": "whole bf16 view of one layer's key archive (all blocks + tail)"},
+            "select_batch": {"kernel": "gather_kernel", "avg_us_incl_alloc": round(g_us, 3), "bytes": gb,
+                             "GBps": round(gb / (g_us * 1e-6) / 1e9, 2),
+                             "what": "all batch rows of one layer's key stream, reversed, into new buffers"}}
+
+
 def cpu_baseline(w, k, v, q, budget_s=12.0):
     """The fp64 oracle on the host cores, on a bounded sample: whole-sequence
     decode attention of one kv head (with its G query heads) at a time,
@@ -279,6 +331,7 @@ def main():
     per_launch = decode_bytes(w, streams[0][0].n_blocks, streams[0][0].n_tail)
     achieved = per_launch / avg_s / 1e9
     traffic = load_traffic(w.name)
+    ops = archive_ops(w, streams, dev)
 
     res = {
         "metric": "decode-attn compressed-KV GB/s + query-heads*tokens/s at 1 GPU; % of HBM peak",
@@ -299,6 +352,7 @@ def main():
         "encode": {"avg_ms": round(float(np.mean(enc_ms[1:] or enc_ms)), 4),
                    "bytes": enc_bytes,
                    "GBps": round(enc_bytes / (float(np.mean(enc_ms[1:] or enc_ms)) * 1e-3) / 1e9, 2)},
+        **ops,
     }
     if not args.no_cpu_baseline:
         print("# timing the oracle on the host cores", file=sys.stderr, flush=True)

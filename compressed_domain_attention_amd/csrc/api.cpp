@@ -392,7 +392,9 @@ int codec_materialise(const codec_stream *s, int64_t block_begin, void *dst, con
   a.o_st = dst_stride[2];
   a.o_t0 = block_begin * s->block;
   (void)hipGetLastError();
-  if (launch_view(a, stream) != 0) return CODEC_ERR_HIP;
+  const int lr = launch_view(a, stream);
+  if (lr < 0) return CODEC_ERR_UNSUPPORTED;
+  if (lr > 0) return CODEC_ERR_HIP;
   return CODEC_OK;
 }
 
@@ -417,7 +419,9 @@ int codec_crop(codec_stream *s, int64_t new_len, hipStream_t stream) {
     a.o_st = s->head_dim;
     a.o_t0 = 0;
     (void)hipGetLastError();
-    if (launch_view(a, stream) != 0) return CODEC_ERR_HIP;
+    const int lr = launch_view(a, stream);
+    if (lr < 0) return CODEC_ERR_UNSUPPORTED;
+    if (lr > 0) return CODEC_ERR_HIP;
   }
   if (kb < s->n_blocks) s->n_blocks = kb;
   s->n_tail = t;

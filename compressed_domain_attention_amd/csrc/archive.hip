@@ -22,111 +22,147 @@
 //
 // The view is streaming work (S fp64 multiply-adds per output element, about
 // 4 flop per byte moved at S = 4): plain fp64 VALU, lanes along head_dim,
-// 4 elements per lane, one (b, h, block) per group of D/4 lanes.  Writes of
-// R tokens per block dominate the traffic.
+// 8 elements per lane (16-byte bf16 stores; 4 per lane when S > 8), one
+// (b, h, block) per group of D/8 lanes, the basis staged in LDS as fp64.
+// Writes of R tokens per block dominate the traffic.
 
 #include "internal.h"
 
 namespace cdattn {
 namespace {
 
-__device__ inline uint16_t bf16_of(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to a packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ inline uint32_t bf16_pair(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-// Four consecutive output elements, rounded to the view format and stored.
-__device__ inline void store4(void *dst, int64_t off, int out, float a, float b, float c, float d) {
+// EPL (4 or 8) consecutive output elements, rounded to the view format.
+template <int EPL>
+__device__ inline void store_out(void *dst, int64_t off, int out, const float (&v)[EPL]) {
   if (out == BF16) {
-    const uint32_t lo = (uint32_t)bf16_of(a) | ((uint32_t)bf16_of(b) << 16);
-    const uint32_t hi = (uint32_t)bf16_of(c) | ((uint32_t)bf16_of(d) << 16);
-    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(dst) + off) = make_uint2(lo, hi);
+    uint32_t w[EPL / 2];
+#pragma unroll
+    for (int k = 0; k < EPL / 2; ++k) w[k] = bf16_pair(v[2 * k], v[2 * k + 1]);
+    uint16_t *p = static_cast<uint16_t *>(dst) + off;
+    if constexpr (EPL == 8)
+      *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    else
+      *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
   } else {
-    *reinterpret_cast<float4 *>(static_cast<float *>(dst) + off) = make_float4(a, b, c, d);
+    float *p = static_cast<float *>(dst) + off;
+#pragma unroll
+    for (int k = 0; k < EPL / 4; ++k)
+      reinterpret_cast<float4 *>(p)[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
   }
 }
 
-// Four consecutive raw (bf16 / fp32) elements as floats.
-__device__ inline float4 load4_raw(const void *src, int64_t off, int raw) {
+// EPL consecutive raw (bf16 / fp32) elements as floats.
+template <int EPL>
+__device__ inline void load_raw(const void *src, int64_t off, int raw, float (&v)[EPL]) {
   if (raw == BF16) {
-    const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(src) + off);
-    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(src) + off);
+#pragma unroll
+    for (int k = 0; k < EPL / 2; ++k) {
+      const uint32_t w = p[k];
+      v[2 * k] = __uint_as_float(w << 16);
+      v[2 * k + 1] = __uint_as_float(w & 0xFFFF0000u);
+    }
+  } else {
+    const float *p = static_cast<const float *>(src) + off;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) v[k] = p[k];
   }
-  return *reinterpret_cast<const float4 *>(static_cast<const float *>(src) + off);
 }
 
-// fp64 values of four consecutive elements of one coefficient row.
-template <int RF>
-__device__ inline void load_row4(const void *rows, const float *scales, int64_t row, int D, int d0,
-                                 double (&c)[4]) {
+// fp64 values of EPL consecutive elements of one coefficient row.
+template <int RF, int EPL>
+__device__ inline void load_row(const void *rows, const float *scales, int64_t row, int D, int d0,
+                                double (&c)[EPL]) {
   const int64_t off = row * D + d0;
   if constexpr (RF == I8) {
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(static_cast<const int8_t *>(rows) + off);
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(static_cast<const int8_t *>(rows) + off);
     const double sc = (double)scales[row];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) c[e] = (double)(int)(int8_t)(w >> (8 * e)) * sc;   // exact
+    for (int k = 0; k < EPL / 4; ++k) {
+      const uint32_t w = p[k];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[4 * k + e] = (double)(int)(int8_t)(w >> (8 * e)) * sc;   // exact
+    }
   } else if constexpr (RF == BF16) {
-    const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(rows) + off);
-    c[0] = (double)__uint_as_float(w.x << 16);
-    c[1] = (double)__uint_as_float(w.x & 0xFFFF0000u);
-    c[2] = (double)__uint_as_float(w.y << 16);
-    c[3] = (double)__uint_as_float(w.y & 0xFFFF0000u);
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(rows) + off);
+#pragma unroll
+    for (int k = 0; k < EPL / 2; ++k) {
+      const uint32_t w = p[k];
+      c[2 * k] = (double)__uint_as_float(w << 16);
+      c[2 * k + 1] = (double)__uint_as_float(w & 0xFFFF0000u);
+    }
   } else {
-    const float4 w = *reinterpret_cast<const float4 *>(static_cast<const float *>(rows) + off);
-    c[0] = (double)w.x;
-    c[1] = (double)w.y;
-    c[2] = (double)w.z;
-    c[3] = (double)w.w;
+    const float *p = static_cast<const float *>(rows) + off;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) c[e] = (double)p[e];
   }
 }
 
-// Work items: BH * nblk blocks (decoded), then BH tails (copied) when
-// copy_tail is set.  A group of D/4 lanes takes one item, 4 elements each.
-template <int RF, int SP>
+// Grid: x = chunks of items, y = kv head, z = batch row.  Item k of (b, h) is
+// block blk0 + k (decoded) for k < nblk; item nblk copies the raw tail when
+// n_copy > 0.  A group of D/EPL lanes takes one item, EPL elements each.
+template <int RF, int SP, int EPL>
 __global__ __launch_bounds__(256) void view_kernel(ViewArgs a) {
-  const int lpi = a.D / 4;                       // lanes per item
-  const int64_t item = (int64_t)blockIdx.x * (256 / lpi) + threadIdx.x / lpi;
-  const int d0 = 4 * (threadIdx.x % lpi);
-  const int64_t nb_items = a.BH * a.nblk;
+  __shared__ double sA[kMaxR * SP];   // A[i][j] as fp64, zero past column S
+  for (int t = threadIdx.x; t < a.R * SP; t += 256) {
+    const int i = t / SP, j = t % SP;
+    sA[t] = j < a.S ? (double)a.A[i * a.S + j] : 0.0;
+  }
+  __syncthreads();
+  const int lpi = a.D / EPL;                     // lanes per item
+  const int64_t k = (int64_t)blockIdx.x * (256 / lpi) + threadIdx.x / lpi;
+  const int d0 = EPL * (threadIdx.x % lpi);
+  const int64_t h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = b * a.H + h;
   const int R = a.R, S = a.S;
-  if (item < nb_items) {
-    const int64_t bh = item / a.nblk, n = a.blk0 + item % a.nblk;
-    const int64_t b = bh / a.H, h = bh % a.H;
+  if (k < a.nblk) {
+    const int64_t n = a.blk0 + k;
     const int64_t row0 = (bh * a.cap + n) * S;   // first coefficient row of the block
-    double c[SP][4];
+    double c[SP][EPL];
 #pragma unroll
     for (int j = 0; j < SP; ++j) {
       if (j < S) {
-        load_row4<RF>(a.rows, a.scales, row0 + j, a.D, d0, c[j]);
+        load_row<RF, EPL>(a.rows, a.scales, row0 + j, a.D, d0, c[j]);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) c[j][e] = 0.0;
+        for (int e = 0; e < EPL; ++e) c[j][e] = 0.0;
       }
     }
-    const int64_t tbase = b * a.o_sb + h * a.o_sh + ((n - a.blk0) * R + a.o_t0) * a.o_st + d0;
+    const int64_t tbase = b * a.o_sb + h * a.o_sh + (k * R + a.o_t0) * a.o_st + d0;
+#pragma unroll 2
     for (int i = 0; i < a.tok_limit; ++i) {
 #pragma clang fp contract(off)   // products and sums rounded separately (the contract)
-      double x[4] = {0.0, 0.0, 0.0, 0.0};
+      double x[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[e] = 0.0;
+      // Columns j >= S add 0 * 0 = +0.0, which leaves x unchanged: x starts
+      // at +0.0 and round-to-nearest sums never produce -0.0 from it.
 #pragma unroll
       for (int j = 0; j < SP; ++j) {
-        if (j < S) {
-          const double Aij = (double)a.A[i * S + j];
+        const double Aij = sA[i * SP + j];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = x[e] + Aij * c[j][e];
-        }
+        for (int e = 0; e < EPL; ++e) x[e] = x[e] + Aij * c[j][e];
       }
-      store4(a.dst, tbase + i * a.o_st, a.out, (float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+      float o[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = (float)x[e];
+      store_out<EPL>(a.dst, tbase + i * a.o_st, a.out, o);
     }
-  } else if (item < nb_items + (a.n_copy > 0 ? a.BH : 0)) {
-    const int64_t bh = item - nb_items;
-    const int64_t b = bh / a.H, h = bh % a.H;
+  } else if (k == a.nblk && a.n_copy > 0) {
     const int64_t src = bh * (int64_t)R * a.D + d0;
     const int64_t dst = b * a.o_sb + h * a.o_sh + (a.nblk * R + a.o_t0) * a.o_st + d0;
     for (int i = 0; i < a.n_copy; ++i) {
-      const float4 v = load4_raw(a.tail, src + (int64_t)i * a.D, a.raw);
-      store4(a.dst, dst + i * a.o_st, a.out, v.x, v.y, v.z, v.w);
+      float v[EPL];
+      load_raw<EPL>(a.tail, src + (int64_t)i * a.D, a.raw, v);
+      store_out<EPL>(a.dst, dst + i * a.o_st, a.out, v);
     }
   }
 }
@@ -158,12 +194,12 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs g) {
 }
 
 template <int RF>
-int launch_view_rf(int SP, const ViewArgs &a, int64_t n_wg, hipStream_t stream) {
+int launch_view_rf(int SP, const ViewArgs &a, dim3 grid, hipStream_t stream) {
   switch (SP) {
-    case 2: hipLaunchKernelGGL((view_kernel<RF, 2>), dim3((unsigned)n_wg), dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((view_kernel<RF, 4>), dim3((unsigned)n_wg), dim3(256), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((view_kernel<RF, 8>), dim3((unsigned)n_wg), dim3(256), 0, stream, a); break;
-    case 16: hipLaunchKernelGGL((view_kernel<RF, 16>), dim3((unsigned)n_wg), dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((view_kernel<RF, 2, 8>), grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((view_kernel<RF, 4, 8>), grid, dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((view_kernel<RF, 8, 8>), grid, dim3(256), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((view_kernel<RF, 16, 4>), grid, dim3(256), 0, stream, a); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;
@@ -173,15 +209,18 @@ int launch_view_rf(int SP, const ViewArgs &a, int64_t n_wg, hipStream_t stream) 
 
 int launch_view(const ViewArgs &a, hipStream_t stream) {
   const int SP = a.S <= 2 ? 2 : (a.S <= 4 ? 4 : (a.S <= 8 ? 8 : 16));
-  const int64_t items = a.BH * a.nblk + (a.n_copy > 0 ? a.BH : 0);
-  const int64_t per_wg = 256 / (a.D / 4);
-  const int64_t n_wg = (items + per_wg - 1) / per_wg;
-  if (n_wg == 0) return 0;
-  if (n_wg > 0x7FFFFFFF) return -1;
+  const int EPL = SP == 16 ? 4 : 8;
+  const int64_t items = a.nblk + (a.n_copy > 0 ? 1 : 0);   // per (b, h)
+  const int64_t per_wg = 256 / (a.D / EPL);
+  const int64_t gx = (items + per_wg - 1) / per_wg;
+  const int64_t B = a.BH / a.H;
+  if (gx == 0) return 0;
+  if (gx > 0x7FFFFFFF || a.H > 65535 || B > 65535) return -1;
+  const dim3 grid((unsigned)gx, (unsigned)a.H, (unsigned)B);
   switch (a.rf) {
-    case I8: return launch_view_rf<I8>(SP, a, n_wg, stream);
-    case BF16: return launch_view_rf<BF16>(SP, a, n_wg, stream);
-    case F32: return launch_view_rf<F32>(SP, a, n_wg, stream);
+    case I8: return launch_view_rf<I8>(SP, a, grid, stream);
+    case BF16: return launch_view_rf<BF16>(SP, a, grid, stream);
+    case F32: return launch_view_rf<F32>(SP, a, grid, stream);
     default: return -1;
   }
 }
