@@ -211,7 +211,8 @@ int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
  *                16-byte aligned; dst_stride = element strides of the b, h
  *                and t axes, each a multiple of 8 (d is contiguous).
  *   dst_dtype    CODEC_F32 | CODEC_BF16.
- * Errors: NULL, SHAPE, FORMAT, STATE (block_begin out of range), HIP.
+ * Errors: NULL, SHAPE, FORMAT, STATE (block_begin out of range),
+ * UNSUPPORTED (B or H above 65535), HIP.
  */
 int codec_materialise(const codec_stream *s, int64_t block_begin, void *dst, const int64_t dst_stride[3],
                       int32_t dst_dtype, hipStream_t stream);
@@ -229,7 +230,8 @@ int codec_materialise(const codec_stream *s, int64_t block_begin, void *dst, con
  * to L2).
  *   s        the stream; counters change only on success.
  *   new_len  tokens to keep, 0 .. n_blocks*R + n_tail.
- * Errors: NULL, SHAPE, FORMAT, STATE (new_len out of range), HIP.
+ * Errors: NULL, SHAPE, FORMAT, STATE (new_len out of range), UNSUPPORTED
+ * (B or H above 65535), HIP.
  */
 int codec_crop(codec_stream *s, int64_t new_len, hipStream_t stream);
 
