@@ -47,6 +47,13 @@ Readings where the pages are silent (each also listed in the design notes)
    format like a float row (reading 4); a crop that cuts into the archive
    re-exposes the boundary block's first tokens from that view, in the
    stream's raw format.
+10. PNG mode (README "Math", PNG item; cache.py ``_archive_spec``): S = R
+    fp32 rows per block, the anchor x_0 and the deltas x_i - x_{i-1}, formed
+    by the same fixed-order fp64 projection with the difference matrix and
+    rounded to fp32 (the README keeps PNG deltas in fp32); the anchor is
+    stored in fp32 too (it holds a bf16 or fp32 token exactly).  Decoding is
+    the cumulative sum.  The Top-M pruning rule is not on the pages: only
+    keep_ratio = 1.0 (no pruning, the lossless tier) is implemented.
 """
 
 import math
@@ -56,7 +63,8 @@ import numpy as np
 F32 = "f32"
 BF16 = "bf16"
 I8 = "i8"
-FORMATS = (F32, BF16, I8)
+PNG = "png"     # PNG mode: S = R fp32 rows, anchor + first-order deltas
+FORMATS = (F32, BF16, I8, PNG)
 
 
 # ---------------------------------------------------------------------------
@@ -84,6 +92,38 @@ def dct_basis_f32(R, S):
     return dct_basis_f64(R, S).astype(np.float32)
 
 
+def png_analysis(R):
+    """PNG mode's analysis matrix (R x R): row 0 keeps the anchor x_0, row
+    i >= 1 the first-order delta x_i - x_{i-1} (README "Math", PNG item)."""
+    M = np.zeros((R, R), dtype=np.float64)
+    M[0, 0] = 1.0
+    for i in range(1, R):
+        M[i, i], M[i, i - 1] = 1.0, -1.0
+    return M
+
+
+def png_synthesis(R):
+    """PNG mode's synthesis (R x R): x_hat_i = x_0 + sum_{j=1..i} delta_j,
+    the cumulative sum of the README's rebuild (A[i, j] = 1 for j <= i)."""
+    return np.tril(np.ones((R, R), dtype=np.float64))
+
+
+def analysis(R, S, fmt):
+    """Rows x tokens matrix that encodes a block in format `fmt`."""
+    if fmt == PNG:
+        if S != R:
+            raise ValueError("PNG mode keeps S = R rows")
+        return png_analysis(R)
+    return dct_basis_f32(R, S).astype(np.float64)
+
+
+def synthesis(R, S, fmt):
+    """Tokens x rows matrix that decodes a block (A, with X_hat = A C)."""
+    if fmt == PNG:
+        return png_synthesis(R)
+    return dct_basis_f32(R, S).astype(np.float64).T
+
+
 # ---------------------------------------------------------------------------
 # rounding helpers (bit-level, so results can be compared byte for byte)
 # ---------------------------------------------------------------------------
@@ -103,21 +143,22 @@ def bf16_bits_to_f64(bits):
 # ---------------------------------------------------------------------------
 # encode
 # ---------------------------------------------------------------------------
-def project_blocks(x, R, S):
+def project_blocks(x, R, S, fmt=F32):
     """fp64 coefficients of every complete block.
 
     x: (..., T, D) real values (bf16 or fp32 values held in any float dtype).
     Returns C: (..., n, S, D) with n = T // R and
         C[..., n, j, :] = sum_{i<R} M32[j, i] * x[..., n*R + i, :]
     summed left to right from +0.0 (reading 3).  README "Math": C = M X
-    block by block along the sequence axis.
+    block by block along the sequence axis.  PNG mode uses the difference
+    matrix instead of M32 (reading 16).
     """
     x = np.asarray(x, dtype=np.float64)
     T, D = x.shape[-2], x.shape[-1]
     lead = x.shape[:-2]
     n = T // R
     xb = x[..., : n * R, :].reshape(*lead, n, R, D)
-    M = dct_basis_f32(R, S).astype(np.float64)
+    M = analysis(R, S, fmt)
     C = np.empty((*lead, n, S, D), dtype=np.float64)
     for j in range(S):
         acc = np.zeros((*lead, n, D), dtype=np.float64)
@@ -151,7 +192,7 @@ def encode_rows(C, fmt):
     Returns (rows, scales): rows float32 for F32, uint16 bf16 patterns for
     BF16, int8 codes for I8; scales float32 for I8 else None.
     """
-    if fmt == F32:
+    if fmt in (F32, PNG):
         return np.asarray(C, dtype=np.float64).astype(np.float32), None
     if fmt == BF16:
         return f32_to_bf16_bits(np.asarray(C, dtype=np.float64).astype(np.float32)), None
@@ -171,7 +212,7 @@ def encode(x, R, S, fmt):
     x = np.asarray(x, dtype=np.float64)
     T = x.shape[-2]
     n = T // R
-    rows, scales = encode_rows(project_blocks(x, R, S), fmt)
+    rows, scales = encode_rows(project_blocks(x, R, S, fmt), fmt)
     return dict(fmt=fmt, R=R, S=S, rows=rows, scales=scales,
                 tail=x[..., n * R:, :].copy(), n_blocks=n)
 
@@ -181,7 +222,7 @@ def encode(x, R, S, fmt):
 # ---------------------------------------------------------------------------
 def dequantize(rows, scales, fmt):
     """fp64 coefficient rows from their stored form (reading 6)."""
-    if fmt == F32:
+    if fmt in (F32, PNG):
         return np.asarray(rows, dtype=np.float32).astype(np.float64)
     if fmt == BF16:
         return bf16_bits_to_f64(rows)
@@ -191,26 +232,27 @@ def dequantize(rows, scales, fmt):
     raise ValueError(f"unknown format {fmt!r}")
 
 
-def reconstruct(C, R):
-    """Synthesis X_hat = M32^T C per block (README "Math": X_hat = M^T C).
+def reconstruct(C, R, fmt=F32):
+    """Synthesis X_hat = A C per block: A = M32^T for the DCT formats
+    (README "Math": X_hat = M^T C), the cumulative sum for PNG mode.
 
     C: (..., n, S, D) fp64 -> (..., n * R, D) fp64, with
-    X_hat[..., n*R + i, :] = sum_j M32[j, i] * C[..., n, j, :].
+    X_hat[..., n*R + i, :] = sum_j A[i, j] * C[..., n, j, :].
     """
     C = np.asarray(C, dtype=np.float64)
     *lead, n, S, D = C.shape
-    M = dct_basis_f32(R, S).astype(np.float64)
+    A = synthesis(R, S, fmt)
     X = np.zeros((*lead, n, R, D), dtype=np.float64)
     for i in range(R):
         for j in range(S):
-            X[..., i, :] += M[j, i] * C[..., j, :]
+            X[..., i, :] += A[i, j] * C[..., j, :]
     return X.reshape(*lead, n * R, D)
 
 
 def materialise(archive):
     """Full (..., n*R + t, D) fp64 view: reconstructed blocks then raw tail."""
     C = dequantize(archive["rows"], archive["scales"], archive["fmt"])
-    X = reconstruct(C, archive["R"])
+    X = reconstruct(C, archive["R"], archive["fmt"])
     return np.concatenate([X, np.asarray(archive["tail"], dtype=np.float64)], axis=-2)
 
 
@@ -240,7 +282,7 @@ def view(archive, out_fmt, block_begin=0):
     n = archive["n_blocks"]
     rows = archive["rows"][..., block_begin:n, :, :]
     scales = None if archive["scales"] is None else archive["scales"][..., block_begin:n, :]
-    X = reconstruct(dequantize(rows, scales, archive["fmt"]), R)
+    X = reconstruct(dequantize(rows, scales, archive["fmt"]), R, archive["fmt"])
     X = np.concatenate([X, np.asarray(archive["tail"], dtype=np.float64)], axis=-2)
     return round_to(X, out_fmt)
 
@@ -385,7 +427,8 @@ class Stream:
         buf = tokens if self.tail is None else np.concatenate([self.tail, tokens], axis=-2)
         n_full = buf.shape[-2] // self.R
         if n_full:
-            rows, scales = encode_rows(project_blocks(buf[..., : n_full * self.R, :], self.R, self.S), self.fmt)
+            rows, scales = encode_rows(project_blocks(buf[..., : n_full * self.R, :], self.R, self.S, self.fmt),
+                                       self.fmt)
             for k in range(n_full):
                 self.rows.append(rows[..., k, :, :])
                 self.scales.append(None if scales is None else scales[..., k, :])
@@ -403,7 +446,7 @@ class Stream:
             rows = np.stack(self.rows, axis=-3)
             scales = np.stack(self.scales, axis=-2) if self.fmt == I8 else None
         else:
-            dt = {F32: np.float32, BF16: np.uint16, I8: np.int8}[self.fmt]
+            dt = {F32: np.float32, BF16: np.uint16, I8: np.int8, PNG: np.float32}[self.fmt]
             rows = np.zeros((*lead, 0, self.S, D), dtype=dt)
             scales = np.zeros((*lead, 0, self.S), dtype=np.float32) if self.fmt == I8 else None
         return dict(fmt=self.fmt, R=self.R, S=self.S, rows=rows, scales=scales,
@@ -415,5 +458,5 @@ def storage_bytes(n_blocks, S, D, fmt, tail_tokens, tail_elem_bytes):
 
     cache.py ``storage_bytes``: valid archive region plus the raw tail.
     """
-    row_b = {F32: 4, BF16: 2, I8: 1}[fmt]
+    row_b = {F32: 4, BF16: 2, I8: 1, PNG: 4}[fmt]
     return n_blocks * S * (D * row_b + (4 if fmt == I8 else 0)) + tail_tokens * D * tail_elem_bytes

@@ -436,3 +436,44 @@ def test_select_batch_invariants():
     e = O.encode(x[idx], R, S, O.I8)
     for k in ("rows", "scales", "tail"):
         assert np.array_equal(g[k], e[k])
+
+
+# ------------------------------------------------------------- PNG mode ----
+def test_png_rows_by_hand():
+    # README "Math", PNG item: the anchor x_0, then deltas x_i - x_{i-1}.
+    x = np.array([1.0, 3.0, 2.0, 2.0, 5.0, 4.0, 4.5, -1.0, 7.0]).reshape(1, 1, 9, 1)
+    a = O.encode(x, 4, 4, O.PNG)
+    assert a["rows"].dtype == np.float32 and a["n_blocks"] == 2
+    assert a["rows"][0, 0, :, :, 0].tolist() == [[1, 2, -1, 0], [5, -1, 0.5, -5.5]]
+    assert a["tail"][0, 0, :, 0].tolist() == [7.0]
+    with pytest.raises(ValueError):
+        O.encode(x, 4, 2, O.PNG)
+    # the synthesis undoes the analysis exactly (cumulative sum of the deltas)
+    for R in (1, 2, 8, 16):
+        assert np.array_equal(O.png_synthesis(R) @ O.png_analysis(R), np.eye(R))
+
+
+@pytest.mark.parametrize("R", [1, 4, 8, 16])
+def test_png_is_lossless_on_bf16_tokens(R):
+    # The lossless tier: bf16 tokens come back bit for bit through the view
+    # (deltas of bf16 values of similar magnitude are exact in fp32).
+    x = syn.bf16_to_numpy(syn.ar1_sequence(2, 3, 7 * R + 3, 32, 0.95, seed=R))
+    a = O.encode(x, R, R, O.PNG)
+    v = O.view(a, O.BF16)
+    assert np.array_equal(v, O.f32_to_bf16_bits(x.astype(np.float32)))
+    # and attention over the archive is attention over the raw tokens
+    q = np.random.default_rng(R).standard_normal((2, 6, 32))
+    got = O.decode_attention(q, a, a)
+    ref = O.attention(q, x, x, 32 ** -0.5)
+    assert np.abs(got - ref).max() <= 1e-12
+
+
+def test_png_delta_variance_collapse():
+    # README "Math": autocorrelation collapses the variance of first-order
+    # deltas; for a stationary AR(1), Var(delta) / Var(x) = 2 (1 - rho).
+    rho = 0.95
+    x = syn.bf16_to_numpy(syn.ar1_sequence(1, 4, 8 * 4096, 64, rho, seed=3))
+    a = O.encode(x, 8, 8, O.PNG)
+    deltas = a["rows"][..., 1:, :].astype(np.float64)
+    ratio = deltas.var() / x.var()
+    assert abs(ratio - 2 * (1 - rho)) <= 0.01
