@@ -30,7 +30,7 @@ import compressed_domain_attention_amd as cda  # noqa: E402
 from compressed_domain_attention_amd import synthetic as syn  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-EB = {"f32": 4, "bf16": 2, "i8": 1}
+EB = {"f32": 4, "bf16": 2, "i8": 1, "png": 4}
 
 
 def decode_bytes(w, n_blocks, n_tail):

@@ -9,5 +9,5 @@ and raises if it is missing.
 from .binding import (  # noqa: F401
     CodecError, CodecStream, basis, decode_attention, decode_workspace_bytes,
     encode_blocks, append_step, materialise, crop, select_batch, library, library_path,
-    FMT_F32, FMT_BF16, FMT_I8,
+    FMT_F32, FMT_BF16, FMT_I8, FMT_PNG,
 )

@@ -13,10 +13,10 @@ import os
 
 import torch
 
-FMT_F32, FMT_BF16, FMT_I8 = 0, 1, 2
-_FMT_NAMES = {"f32": FMT_F32, "bf16": FMT_BF16, "i8": FMT_I8}
-_TORCH_DTYPE = {FMT_F32: torch.float32, FMT_BF16: torch.bfloat16, FMT_I8: torch.int8}
-_ELEM_BYTES = {FMT_F32: 4, FMT_BF16: 2, FMT_I8: 1}
+FMT_F32, FMT_BF16, FMT_I8, FMT_PNG = 0, 1, 2, 3
+_FMT_NAMES = {"f32": FMT_F32, "bf16": FMT_BF16, "i8": FMT_I8, "png": FMT_PNG}
+_TORCH_DTYPE = {FMT_F32: torch.float32, FMT_BF16: torch.bfloat16, FMT_I8: torch.int8, FMT_PNG: torch.float32}
+_ELEM_BYTES = {FMT_F32: 4, FMT_BF16: 2, FMT_I8: 1, FMT_PNG: 4}
 INITIAL_BLOCKS = 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

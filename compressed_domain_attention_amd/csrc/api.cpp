@@ -12,9 +12,11 @@ using namespace cdattn;
 
 namespace {
 
-bool fmt_ok(int f) { return f == CODEC_F32 || f == CODEC_BF16 || f == CODEC_I8; }
+bool fmt_ok(int f) { return f == CODEC_F32 || f == CODEC_BF16 || f == CODEC_I8 || f == CODEC_PNG; }
 bool raw_ok(int f) { return f == CODEC_F32 || f == CODEC_BF16; }
-int elem_bytes(int f) { return f == CODEC_F32 ? 4 : (f == CODEC_BF16 ? 2 : 1); }
+int elem_bytes(int f) { return (f == CODEC_F32 || f == CODEC_PNG) ? 4 : (f == CODEC_BF16 ? 2 : 1); }
+// Storage format of the rows as the kernels see it (PNG rows are fp32).
+int row_fmt(int f) { return f == CODEC_PNG ? CODEC_F32 : f; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Analysis basis in double, rounded to fp32 (flashcodec-kv README "Math":
@@ -32,6 +34,7 @@ int check_stream(const codec_stream *s) {
   if (s->batch < 1 || s->heads < 1) return CODEC_ERR_SHAPE;
   if (s->batch * s->heads > (int64_t)1 << 31) return CODEC_ERR_SHAPE;
   if (!fmt_ok(s->fmt) || !raw_ok(s->raw_dtype)) return CODEC_ERR_FORMAT;
+  if (s->fmt == CODEC_PNG && s->keep != s->block) return CODEC_ERR_SHAPE;   // anchor + R-1 deltas
   if (s->n_tail < 0 || s->n_tail >= s->block) return CODEC_ERR_STATE;
   if (s->n_blocks < 0) return CODEC_ERR_STATE;
   if (s->capacity < s->n_blocks) return CODEC_ERR_CAPACITY;
@@ -50,16 +53,27 @@ bool same_geometry(const codec_stream *a, const codec_stream *b) {
          a->heads == b->heads && a->n_blocks == b->n_blocks && a->n_tail == b->n_tail;
 }
 
-void fill_M(int R, int S, float *M) {
+// Analysis matrix M[j*R + i] of a stream's rows: the fp32 DCT-II basis, or
+// for PNG mode the anchor / first-order difference rows (README "Math", PNG
+// item: delta_i = x_i - x_{i-1}, x_0 kept).
+void fill_M(int fmt, int R, int S, float *M) {
   for (int j = 0; j < S; ++j)
-    for (int i = 0; i < R; ++i) M[j * R + i] = (float)basis_entry(R, j, i);
+    for (int i = 0; i < R; ++i)
+      M[j * R + i] = fmt == CODEC_PNG ? (i == j ? 1.0f : (j > 0 && i == j - 1 ? -1.0f : 0.0f))
+                                      : (float)basis_entry(R, j, i);
+}
+
+// Synthesis entry A[i][j] (token i from row j): M^T for the DCT formats, the
+// cumulative sum for PNG mode (x_hat_i = x_0 + sum_{j=1..i} delta_j).
+float synth_entry(int fmt, int R, int i, int j) {
+  return fmt == CODEC_PNG ? (j <= i ? 1.0f : 0.0f) : (float)basis_entry(R, j, i);
 }
 
 EncodeArgs stream_encode_args(const codec_stream *s) {
   EncodeArgs e;
   memset(&e, 0, sizeof(e));
   e.raw = s->raw_dtype;
-  e.fmt = s->fmt;
+  e.fmt = row_fmt(s->fmt);
   e.R = s->block;
   e.S = s->keep;
   e.H = s->heads;
@@ -93,7 +107,7 @@ Plan make_plan(const codec_stream *k, const codec_stream *v, int64_t Hq) {
   p.SP = decode_pad_keep(k->keep);
   p.pairs = k->batch * k->heads * p.NQG;
   const int64_t n = k->n_blocks;
-  const int64_t NB = decode_tile_rows(k->head_dim, k->fmt, v->fmt) / k->keep;   // blocks per tile
+  const int64_t NB = decode_tile_rows(k->head_dim, row_fmt(k->fmt), row_fmt(v->fmt)) / k->keep;   // blocks per tile
   p.ok = NB >= 1;
   if (n == 0 || !p.ok) {
     p.ns = 1;
@@ -131,6 +145,7 @@ int check_decode(const codec_stream *k, const codec_stream *v, int64_t Hq) {
   rc = check_stream(v);
   if (rc) return rc;
   if (!same_geometry(k, v)) return CODEC_ERR_SHAPE;
+  if ((k->fmt == CODEC_PNG) != (v->fmt == CODEC_PNG)) return CODEC_ERR_FORMAT;   // one synthesis for both
   if (Hq < 1 || Hq % k->heads != 0) return CODEC_ERR_SHAPE;
   if (k->n_blocks * k->block + k->n_tail == 0) return CODEC_ERR_SHAPE;
   return CODEC_OK;
@@ -221,7 +236,7 @@ int codec_encode_blocks(codec_stream *s, const void *x, const int64_t x_stride[3
   L.e.split_i = (int32_t)R;
   L.e.n_new = n_new;
   L.e.n_copy = t;
-  fill_M((int)R, s->keep, L.M);
+  fill_M(s->fmt, (int)R, s->keep, L.M);
   (void)hipGetLastError();
   if (launch_encode(s->head_dim, L, s->batch * s->heads, stream) != 0) return CODEC_ERR_HIP;
   s->n_blocks += n_new;
@@ -236,6 +251,7 @@ int codec_append_step(codec_stream *k, codec_stream *v, const void *k_new, const
   rc = check_stream(v);
   if (rc) return rc;
   if (!same_geometry(k, v)) return CODEC_ERR_SHAPE;
+  if ((k->fmt == CODEC_PNG) != (v->fmt == CODEC_PNG)) return CODEC_ERR_FORMAT;   // one analysis for both
   if (!k_new || !v_new || !kn_stride || !vn_stride) return CODEC_ERR_NULL;
   if (!aligned16(k_new) || !aligned16(v_new)) return CODEC_ERR_SHAPE;
   for (int i = 0; i < 2; ++i)
@@ -264,7 +280,7 @@ int codec_append_step(codec_stream *k, codec_stream *v, const void *k_new, const
   }
   A.t = k->n_tail;
   A.complete = complete;
-  fill_M(k->block, k->keep, A.M);
+  fill_M(k->fmt, k->block, k->keep, A.M);
   (void)hipGetLastError();
   if (launch_append(k->head_dim, A, k->batch * k->heads, stream) != 0) return CODEC_ERR_HIP;
   for (codec_stream *s : {k, v}) {
@@ -317,8 +333,9 @@ int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
   a.vtail = v->tail;
   a.k_bh_rows = k->capacity * k->keep;
   a.v_bh_rows = v->capacity * v->keep;
-  a.kf = k->fmt;
-  a.vf = v->fmt;
+  a.kf = row_fmt(k->fmt);
+  a.vf = row_fmt(v->fmt);
+  a.png = k->fmt == CODEC_PNG ? 1 : 0;
   a.kraw = k->raw_dtype;
   a.vraw = v->raw_dtype;
   a.H = (int32_t)k->heads;
@@ -340,7 +357,7 @@ int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
   a.part_ml = reinterpret_cast<float *>(ws + p.off_ml);
   a.part_acc = reinterpret_cast<float *>(ws + p.off_acc);
   (void)hipGetLastError();
-  const int lr = launch_decode(k->head_dim, p.GS, p.SP, k->fmt, v->fmt, a, p.n_wg, stream);
+  const int lr = launch_decode(k->head_dim, p.GS, p.SP, row_fmt(k->fmt), row_fmt(v->fmt), a, p.n_wg, stream);
   if (lr < 0) return CODEC_ERR_UNSUPPORTED;
   if (lr > 0) return CODEC_ERR_HIP;
   return CODEC_OK;
@@ -355,7 +372,7 @@ ViewArgs stream_view_args(const codec_stream *s) {
   a.rows = s->rows;
   a.scales = s->scales;
   a.tail = s->tail;
-  a.rf = s->fmt;
+  a.rf = row_fmt(s->fmt);
   a.raw = s->raw_dtype;
   a.R = s->block;
   a.S = s->keep;
@@ -364,7 +381,7 @@ ViewArgs stream_view_args(const codec_stream *s) {
   a.BH = s->batch * s->heads;
   a.cap = s->capacity;
   for (int i = 0; i < s->block; ++i)
-    for (int j = 0; j < s->keep; ++j) a.A[i * s->keep + j] = (float)basis_entry(s->block, j, i);
+    for (int j = 0; j < s->keep; ++j) a.A[i * s->keep + j] = synth_entry(s->fmt, s->block, i, j);
   return a;
 }
 

@@ -1048,11 +1048,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   qr.load(a, b, hq0, lane);
   // A[r][j] = c_j cos(pi (2r + 1) j / (2R)), the orthonormal DCT-II synthesis
   // (flashcodec-kv README, "Math"), entry r * SP + j per thread, zero padded.
+  // PNG mode (README "Math", PNG item): token r = anchor + deltas 1..r, A[r][j] = [j <= r].
   float a_arg = 0.0f;
   if (tid < R * SP && tid % SP < S) {
     const int r = tid / SP, j = tid % SP;
     const float cj = j == 0 ? sqrtf(1.0f / (float)R) : sqrtf(2.0f / (float)R);
-    a_arg = cj * cospif((float)((2 * r + 1) * j) / (float)(2 * R));
+    a_arg = a.png ? (j <= r ? 1.0f : 0.0f) : cj * cospif((float)((2 * r + 1) * j) / (float)(2 * R));
   }
   // NBUF register buffers per wave: the first NBUF tiles are requested at once
   TileBuf<D, GS, KF, VF> bufs[C::NBUF];

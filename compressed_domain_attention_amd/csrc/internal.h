@@ -117,6 +117,7 @@ struct DecodeArgs {
   int32_t ns;             // splits per (b, h, query group)
   int64_t chunk;          // blocks per split
   float qk_scale;         // softmax scale * log2(e)
+  int32_t png;            // 1: PNG mode synthesis (cumulative sum), else the DCT-II basis
   void *out;
   int64_t o_sb, o_sh;
   int32_t out_f32;        // 1: fp32 out, 0: bf16 out

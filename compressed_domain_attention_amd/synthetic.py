@@ -70,6 +70,10 @@ WORKLOADS = {
                              kfmt="i8", vfmt="bf16", rho=0.9, encode=True),
     "stream64": Workload("stream64", 5, B=32, Hq=32, Hkv=8, D=128, T=32760, R=8, S=2,
                          kfmt="i8", vfmt="i8", rho=0.95, steps=64),
+    # PNG mode (anchor + fp32 deltas, R = S = 8) at the shape of the README's
+    # coefficient-domain table: B=1, Hkv=8, Hq=16, D=64, 65 536 tokens.
+    "png64k": Workload("png64k", 6, B=1, Hq=16, Hkv=8, D=64, T=65536, R=8, S=8,
+                       kfmt="png", vfmt="png", rho=0.95),
 }
 
 

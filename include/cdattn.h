@@ -57,7 +57,11 @@ enum {
 enum {
   CODEC_F32 = 0,   /* IEEE binary32                                            */
   CODEC_BF16 = 1,  /* bfloat16 (upper half of binary32), round-to-nearest-even */
-  CODEC_I8 = 2     /* int8 codes in [-127, 127] + fp32 scale per (block, row)  */
+  CODEC_I8 = 2,    /* int8 codes in [-127, 127] + fp32 scale per (block, row)  */
+  CODEC_PNG = 3    /* rows only: PNG mode (README "Math", PNG item), S == R    */
+                   /* fp32 rows per block: the anchor x_0, then the deltas     */
+                   /* x_i - x_{i-1}; decoded by the cumulative sum.  Both      */
+                   /* streams of a decode or append use it, or neither.        */
 };
 
 /* Limits of this build. */
@@ -101,6 +105,11 @@ typedef struct codec_stream {
 } codec_stream;
 
 /*
+ * Rows in PNG mode (fmt == CODEC_PNG) are produced by the arithmetic of the
+ * fp32 rows with the difference matrix in place of M: row 0 = fp32(x_0), row
+ * i = fp32(x_i - x_{i-1}) (exact fp64 difference, one rounding).  The
+ * Top-M pruning of the pages is not applied (keep ratio 1: the lossless tier).
+ *
  * codec_basis -- synthesis matrix A = M^T of the kept DCT-II rows, on the host.
  * README "Math", JPEG item: M[j, i] = c_j cos(pi (2i + 1) j / (2R)),
  * c_0 = sqrt(1/R), c_j = sqrt(2/R) (the normalisation that makes the rows

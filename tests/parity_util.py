@@ -11,7 +11,7 @@ import oracle as O
 from compressed_domain_attention_amd import binding as bd
 from compressed_domain_attention_amd import synthetic as syn
 
-FMT_NAME = {bd.FMT_F32: O.F32, bd.FMT_BF16: O.BF16, bd.FMT_I8: O.I8}
+FMT_NAME = {bd.FMT_F32: O.F32, bd.FMT_BF16: O.BF16, bd.FMT_I8: O.I8, bd.FMT_PNG: O.PNG}
 TOL = 2e-3   # max over (b, hq) of ||o - o_ref||_inf / ||o_ref||_inf
 
 

@@ -247,3 +247,19 @@ def test_select_batch_validation(lib):
     before = (d.n_blocks, d.n_tail)
     assert sel(d, ix=(ctypes.c_int64 * 3)(0, 5, 1)) == SHAPE
     assert (d.n_blocks, d.n_tail) == before
+
+
+def test_png_mode_validation(lib):
+    # PNG mode keeps S = R rows; keys and values share the synthesis
+    assert encode(lib, stream(fmt=bd.FMT_PNG, keep=2, block=8)) == SHAPE
+    assert encode(lib, stream(fmt=bd.FMT_PNG, keep=16, block=16), T=0) == OK
+    assert encode(lib, stream(fmt=bd.FMT_PNG, keep=32, block=32)) == SHAPE    # beyond CODEC_MAX_KEEP
+    two = bd._I64_2(1024, 128)
+    k = stream(fmt=bd.FMT_PNG, keep=8, block=8)
+    v = stream(fmt=bd.FMT_F32, keep=8, block=8)
+    assert lib.codec_append_step(ctypes.byref(k), ctypes.byref(v), FAKE, two, FAKE, two, None) == FORMAT
+    n = ctypes.c_size_t(0)
+    k.n_blocks = v.n_blocks = 2
+    assert lib.codec_decode_workspace_bytes(ctypes.byref(k), ctypes.byref(v), 8, ctypes.byref(n)) == FORMAT
+    v.fmt = bd.FMT_PNG
+    assert lib.codec_decode_workspace_bytes(ctypes.byref(k), ctypes.byref(v), 8, ctypes.byref(n)) == OK
