@@ -932,14 +932,44 @@ __device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt
   constexpr int LK = D / 16, RK = 64 / LK, EBK = ebytes(RAWK), EBV = ebytes(RAWV);
   constexpr int LV = D / EV, RV = 64 / LV, VDW = EV * EBV / 4;
   static_assert(kMaxR % RV == 0 && kMaxR % RK == 0, "tail steps must tile the tail rows");
+  // Up to PK key and PV value load steps are requested together (rows past
+  // the tail read zeros), so the first chunk of both costs one round trip.
+  constexpr int PK = cmin(kMaxR / RK, 4), PV = cmin(kMaxR / RV, 8);
   const rsrc_t rk = make_rsrc(kt, (uint32_t)nt * D * EBK);
   const rsrc_t rv = make_rsrc(vt, (uint32_t)nt * D * EBV);
   const int rrk = lane / LK, ck = lane % LK;
-  for (int r0 = 0; r0 < nt; r0 += RK) {
-    uint4 kb[1][EBK];
+  const int rrv = lane / LV, cv = lane % LV;
+  const uint32_t offk = (uint32_t)(rrk * D + ck * 16) * EBK;
+  const uint32_t offv = (uint32_t)(rrv * D + cv * EV) * EBV;
+  uint4 kb[PK][EBK];
+  uint32_t vb[PV][VDW];
+  auto load_k = [&](int r00) {
 #pragma unroll
-    for (int k = 0; k < EBK; ++k) kb[0][k] = bload128(rk, (uint32_t)(rrk * D + ck * 16) * EBK + 16 * k, r0 * D * EBK);
-    kcompute<D, GS, SWR, RAWK, 1, EBK>(kb, nt, lane, qh, cq, sw, r0);
+    for (int s = 0; s < PK; ++s)
+#pragma unroll
+      for (int k = 0; k < EBK; ++k) kb[s][k] = bload128(rk, offk + 16 * k, (r00 + s * RK) * D * EBK);
+  };
+  auto load_v = [&](int r00) {
+#pragma unroll
+    for (int s = 0; s < PV; ++s) {
+      if constexpr (VDW % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < VDW / 4; ++k) {
+          const uint4 t = bload128(rv, offv + 16 * k, (r00 + s * RV) * D * EBV);
+          vb[s][4 * k] = t.x; vb[s][4 * k + 1] = t.y; vb[s][4 * k + 2] = t.z; vb[s][4 * k + 3] = t.w;
+        }
+      } else {
+        const uint2 t = bload64(rv, offv, (r00 + s * RV) * D * EBV);
+        vb[s][0] = t.x; vb[s][1] = t.y;
+      }
+    }
+  };
+  load_k(0);
+  load_v(0);
+  kcompute<D, GS, SWR, RAWK, PK, EBK>(kb, nt, lane, qh, cq, sw, 0);
+  for (int r00 = PK * RK; r00 < nt; r00 += PK * RK) {
+    load_k(r00);
+    kcompute<D, GS, SWR, RAWK, PK, EBK>(kb, nt, lane, qh, cq, sw, r00);
   }
   wave_lds_sync();
   Basis<SP> unit;
@@ -947,21 +977,10 @@ __device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt
   logits_any<GS, SP, SWR>(unit, sw, nt, 1, 1, lane, m_u, m_lane, l_lane, alpha);
   rescale(acc, alpha);
   wave_lds_sync();
-  const int rrv = lane / LV, cv = lane % LV;
-  const uint32_t off = (uint32_t)(rrv * D + cv * EV) * EBV;
-  for (int r0 = 0; r0 < nt; r0 += RV) {
-    uint32_t vb[1][VDW];
-    if constexpr (VDW % 4 == 0) {
-#pragma unroll
-      for (int k = 0; k < VDW / 4; ++k) {
-        const uint4 t = bload128(rv, off + 16 * k, r0 * D * EBV);
-        vb[0][4 * k] = t.x; vb[0][4 * k + 1] = t.y; vb[0][4 * k + 2] = t.z; vb[0][4 * k + 3] = t.w;
-      }
-    } else {
-      const uint2 t = bload64(rv, off, r0 * D * EBV);
-      vb[0][0] = t.x; vb[0][1] = t.y;
-    }
-    vcompute<D, GS, SWR, RAWV, 1, VDW, EV>(vb, nt, lane, sw, acc, r0);
+  vcompute<D, GS, SWR, RAWV, PV, VDW, EV>(vb, nt, lane, sw, acc, 0);
+  for (int r00 = PV * RV; r00 < nt; r00 += PV * RV) {
+    load_v(r00);
+    vcompute<D, GS, SWR, RAWV, PV, VDW, EV>(vb, nt, lane, sw, acc, r00);
   }
   wave_lds_sync();
 }
