@@ -4,8 +4,9 @@ Default workload: the 128K-context layer (B=1, Hq=32, Hkv=8, D=128,
 T=131072+5, R=16, S=4, int8 K and V rows).  A step is one decode step of a
 stack of LAYERS such layers, each with its own archive at its own address
 (8 x 69 MB exceeds the 256 MB MALL, so HBM is what is measured): per layer,
-append the new token's K/V (codec_append_step, which archives a block every
-R steps) and attend (codec_decode_attention).  Each step is captured once
+append the new token's K/V and attend (codec_decode_attention_append: the
+decode launch takes the token itself, and a separate append launch archives
+a block every R steps).  Each step is captured once
 as a HIP graph and the graphs are replayed in order.
 
 Prints one JSON line.  value = compressed-KV GB/s: algorithmic decode bytes
@@ -286,8 +287,10 @@ def main():
         nb = ntl = 0
         with torch.cuda.graph(g, stream=cap_stream):
             for li, (ks, vs) in enumerate(streams):
-                cda.append_step(ks, vs, kd[:, :, w.T + s:w.T + s + 1], vd[:, :, w.T + s:w.T + s + 1])
-                cda.decode_attention(queries[s], ks, vs, out=outs[li], workspace=ws)
+                # append the step's token and attend, in one call (one launch
+                # unless the token completes a block)
+                cda.decode_attention_append(queries[s], ks, vs, kd[:, :, w.T + s:w.T + s + 1],
+                                            vd[:, :, w.T + s:w.T + s + 1], out=outs[li], workspace=ws)
                 nb, ntl = ks.n_blocks, ks.n_tail
         graphs.append(g)
         step_bytes.append(L * decode_bytes(w, nb, ntl))
@@ -342,7 +345,7 @@ def main():
                  "fp32 softmax, scaling and accumulation", "data": "synthetic AR(1) KV drawn on the device (seeded), N(0,1) q",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "T0": w.T,
                    "R": w.R, "S": w.S, "k_rows": w.kfmt, "v_rows": w.vfmt, "layers_rotated": L,
-                   "step": "per layer: codec_append_step + codec_decode_attention, HIP graph per step"},
+                   "step": "per layer: codec_decode_attention_append (append + decode), HIP graph per step"},
         "query_head_tokens_per_s": round(qtok, 1),
         "hbm_peak_fraction": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -66,6 +66,8 @@ def _lib():
         lib.codec_decode_workspace_bytes.argtypes = [P, P, i64, ctypes.POINTER(ctypes.c_size_t)]
         lib.codec_decode_attention.argtypes = [vp, LP, i64, P, P, f32, vp, LP, i32,
                                                vp, ctypes.c_size_t, vp]
+        lib.codec_decode_attention_append.argtypes = [vp, LP, i64, P, P, vp, LP, vp, LP, f32, vp, LP, i32,
+                                                      vp, ctypes.c_size_t, vp]
         lib.codec_materialise.argtypes = [P, i64, vp, LP, i32, vp]
         lib.codec_crop.argtypes = [P, i64, vp]
         lib.codec_select_batch.argtypes = [P, P, LP, i64, vp]
@@ -73,7 +75,7 @@ def _lib():
         lib.codec_status_string.restype = ctypes.c_char_p
         for name in ("codec_basis", "codec_encode_blocks", "codec_append_step",
                      "codec_decode_workspace_bytes", "codec_decode_attention",
-                     "codec_materialise", "codec_crop", "codec_select_batch"):
+                     "codec_materialise", "codec_crop", "codec_select_batch", "codec_decode_attention_append"):
             getattr(lib, name).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -332,6 +334,52 @@ def decode_attention(q, k, v, scale=None, out=None, out_dtype=torch.float32, wor
         ctypes.c_void_p(out.data_ptr()), _I64_2(out.stride(0), out.stride(1)), odt,
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), st),
         "codec_decode_attention")
+    return out
+
+
+def decode_attention_append(q, k, v, k_new, v_new, scale=None, out=None, out_dtype=torch.float32, workspace=None,
+                            stream=None):
+    """append_step(k, v, k_new, v_new) then decode_attention(q, k, v) in one
+    call (codec_decode_attention_append: one launch unless the token
+    completes a block)."""
+    if q.dtype != torch.bfloat16 or q.dim() != 4 or q.shape[2] != 1 or q.stride(3) != 1:
+        raise ValueError("q must be (B, Hq, 1, D) bf16 with unit d stride")
+    for s, t in ((k, k_new), (v, v_new)):
+        if t.dtype != _TORCH_DTYPE[s.raw_dtype] or t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError("new token must be (B, H, 1, D) of the raw dtype with unit d stride")
+    B, Hq, _, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, 1, D), dtype=out_dtype, device=q.device)
+    odt = {torch.float32: FMT_F32, torch.bfloat16: FMT_BF16}[out.dtype]
+    if k.n_tail + 1 == k.R:
+        k._grow(k.n_blocks + 1)
+        v._grow(v.n_blocks + 1)
+    dk, dv = k._desc(), v._desc()
+    if workspace is None:
+        # sized for the streams as the append leaves them (the split plan
+        # depends on the block count only)
+        nb = k.n_blocks + (1 if k.n_tail + 1 == k.R else 0)
+        dk2, dv2 = k._desc(), v._desc()
+        dk2.n_blocks = dv2.n_blocks = nb
+        dk2.n_tail = dv2.n_tail = (k.n_tail + 1) % k.R
+        n = ctypes.c_size_t(0)
+        _check(_lib().codec_decode_workspace_bytes(ctypes.byref(dk2), ctypes.byref(dv2), int(Hq), ctypes.byref(n)),
+               "codec_decode_workspace_bytes")
+        workspace = _workspace(int(n.value), q.device)
+    st = _hip_stream(q.device) if stream is None else ctypes.c_void_p(stream)
+    _check(_lib().codec_decode_attention_append(
+        ctypes.c_void_p(q.data_ptr()), _I64_2(q.stride(0), q.stride(1)), Hq,
+        ctypes.byref(dk), ctypes.byref(dv),
+        ctypes.c_void_p(k_new.data_ptr()), _I64_2(k_new.stride(0), k_new.stride(1)),
+        ctypes.c_void_p(v_new.data_ptr()), _I64_2(v_new.stride(0), v_new.stride(1)),
+        ctypes.c_float(float(scale)),
+        ctypes.c_void_p(out.data_ptr()), _I64_2(out.stride(0), out.stride(1)), odt,
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), st),
+        "codec_decode_attention_append")
+    k._sync(dk)
+    v._sync(dv)
     return out
 
 

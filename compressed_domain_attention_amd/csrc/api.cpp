@@ -181,6 +181,146 @@ int launch_decode(int D, int GS, int SP, int kf, int vf, const DecodeArgs &a, in
 }
 }  // namespace cdattn
 
+namespace {
+
+// Validation of codec_append_step (no HIP call).
+int check_append(const codec_stream *k, const codec_stream *v, const void *k_new, const int64_t kn_stride[2],
+                 const void *v_new, const int64_t vn_stride[2]) {
+  int rc = check_stream(k);
+  if (rc) return rc;
+  rc = check_stream(v);
+  if (rc) return rc;
+  if (!same_geometry(k, v)) return CODEC_ERR_SHAPE;
+  if ((k->fmt == CODEC_PNG) != (v->fmt == CODEC_PNG)) return CODEC_ERR_FORMAT;   // one analysis for both
+  if (!k_new || !v_new || !kn_stride || !vn_stride) return CODEC_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return CODEC_ERR_SHAPE;
+  for (int i = 0; i < 2; ++i)
+    if (kn_stride[i] < 0 || kn_stride[i] % 8 != 0 || vn_stride[i] < 0 || vn_stride[i] % 8 != 0)
+      return CODEC_ERR_SHAPE;
+  const int complete = (k->n_tail + 1 == k->block) ? 1 : 0;
+  if (complete && (k->n_blocks + 1 > k->capacity || v->n_blocks + 1 > v->capacity)) return CODEC_ERR_CAPACITY;
+  return CODEC_OK;
+}
+
+// The append launch for validated arguments; advances both streams' counters.
+int launch_append_step(codec_stream *k, codec_stream *v, const void *k_new, const int64_t kn_stride[2],
+                       const void *v_new, const int64_t vn_stride[2], hipStream_t stream) {
+  const int complete = (k->n_tail + 1 == k->block) ? 1 : 0;
+  AppendArgs A;
+  memset(&A, 0, sizeof(A));
+  const codec_stream *ss[2] = {k, v};
+  const void *nw[2] = {k_new, v_new};
+  const int64_t *ns[2] = {kn_stride, vn_stride};
+  for (int i = 0; i < 2; ++i) {
+    EncodeArgs &e = A.e[i];
+    e = stream_encode_args(ss[i]);
+    const int64_t R = ss[i]->block, D = ss[i]->head_dim;
+    e.src0 = ss[i]->tail;
+    e.s0_b = ss[i]->heads * R * D;
+    e.s0_h = R * D;
+    e.s0_t = D;
+    e.src1 = nw[i];
+    e.s1_b = ns[i][0];
+    e.s1_h = ns[i][1];
+    e.split_i = (int32_t)(R - 1);
+    e.n_new = 1;
+  }
+  A.t = k->n_tail;
+  A.complete = complete;
+  fill_M(k->fmt, k->block, k->keep, A.M);
+  (void)hipGetLastError();
+  if (launch_append(k->head_dim, A, k->batch * k->heads, stream) != 0) return CODEC_ERR_HIP;
+  for (codec_stream *s : {k, v}) {
+    if (complete) {
+      s->n_blocks += 1;
+      s->n_tail = 0;
+    } else {
+      s->n_tail += 1;
+    }
+  }
+  return CODEC_OK;
+}
+
+// Validation of codec_decode_attention (no HIP call); fills the plan.
+int check_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
+                      const codec_stream *v, float scale, const void *out, const int64_t out_stride[2],
+                      int32_t out_dtype, const void *workspace, size_t workspace_bytes, Plan *p) {
+  if (!q || !q_stride || !out || !out_stride) return CODEC_ERR_NULL;
+  int rc = check_decode(k, v, Hq);
+  if (rc) return rc;
+  if (out_dtype != CODEC_F32 && out_dtype != CODEC_BF16) return CODEC_ERR_FORMAT;
+  if (!(scale > 0.0f) || !isfinite(scale)) return CODEC_ERR_SCALE;
+  if (!aligned16(q) || q_stride[0] < 0 || q_stride[1] < 0 || q_stride[0] % 8 || q_stride[1] % 8)
+    return CODEC_ERR_SHAPE;
+  if (out_stride[0] < 0 || out_stride[1] < 0) return CODEC_ERR_SHAPE;
+  *p = make_plan(k, v, Hq);
+  if (!p->ok) return CODEC_ERR_UNSUPPORTED;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < p->bytes)
+    return CODEC_ERR_WORKSPACE;
+  return CODEC_OK;
+}
+
+// The decode launch for validated arguments.  fuse_k / fuse_v (non-null)
+// bring one new token that joins the tail as slot k->n_tail.
+int launch_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
+                       const codec_stream *v, float scale, void *out, const int64_t out_stride[2],
+                       int32_t out_dtype, void *workspace, const Plan &p, const void *fuse_k,
+                       const int64_t kn_stride[2], const void *fuse_v, const int64_t vn_stride[2],
+                       hipStream_t stream) {
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t *>(q);
+  a.q_sb = q_stride[0];
+  a.q_sh = q_stride[1];
+  a.krows = k->rows;
+  a.kscales = k->scales;
+  a.ktail = k->tail;
+  a.vrows = v->rows;
+  a.vscales = v->scales;
+  a.vtail = v->tail;
+  a.k_bh_rows = k->capacity * k->keep;
+  a.v_bh_rows = v->capacity * v->keep;
+  a.kf = row_fmt(k->fmt);
+  a.vf = row_fmt(v->fmt);
+  a.png = k->fmt == CODEC_PNG ? 1 : 0;
+  a.kraw = k->raw_dtype;
+  a.vraw = v->raw_dtype;
+  a.H = (int32_t)k->heads;
+  a.G = (int32_t)(Hq / k->heads);
+  a.NQG = p.NQG;
+  a.R = k->block;
+  a.S = k->keep;
+  a.n_blocks = k->n_blocks;
+  a.n_tail = k->n_tail;
+  a.ns = p.ns;
+  a.chunk = p.chunk;
+  a.qk_scale = (float)((double)scale * 1.4426950408889634);   // log2(e)
+  if (fuse_k) {
+    a.fuse_new = 1;
+    a.knew = fuse_k;
+    a.vnew = fuse_v;
+    a.kn_sb = kn_stride[0];
+    a.kn_sh = kn_stride[1];
+    a.vn_sb = vn_stride[0];
+    a.vn_sh = vn_stride[1];
+  }
+  a.out = out;
+  a.o_sb = out_stride[0];
+  a.o_sh = out_stride[1];
+  a.out_f32 = out_dtype == CODEC_F32 ? 1 : 0;
+  char *ws = static_cast<char *>(workspace);
+  a.counters = reinterpret_cast<uint32_t *>(ws);
+  a.part_ml = reinterpret_cast<float *>(ws + p.off_ml);
+  a.part_acc = reinterpret_cast<float *>(ws + p.off_acc);
+  (void)hipGetLastError();
+  const int lr = launch_decode(k->head_dim, p.GS, p.SP, row_fmt(k->fmt), row_fmt(v->fmt), a, p.n_wg, stream);
+  if (lr < 0) return CODEC_ERR_UNSUPPORTED;
+  if (lr > 0) return CODEC_ERR_HIP;
+  return CODEC_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *codec_status_string(int status) {
@@ -246,52 +386,9 @@ int codec_encode_blocks(codec_stream *s, const void *x, const int64_t x_stride[3
 
 int codec_append_step(codec_stream *k, codec_stream *v, const void *k_new, const int64_t kn_stride[2],
                       const void *v_new, const int64_t vn_stride[2], hipStream_t stream) {
-  int rc = check_stream(k);
+  const int rc = check_append(k, v, k_new, kn_stride, v_new, vn_stride);
   if (rc) return rc;
-  rc = check_stream(v);
-  if (rc) return rc;
-  if (!same_geometry(k, v)) return CODEC_ERR_SHAPE;
-  if ((k->fmt == CODEC_PNG) != (v->fmt == CODEC_PNG)) return CODEC_ERR_FORMAT;   // one analysis for both
-  if (!k_new || !v_new || !kn_stride || !vn_stride) return CODEC_ERR_NULL;
-  if (!aligned16(k_new) || !aligned16(v_new)) return CODEC_ERR_SHAPE;
-  for (int i = 0; i < 2; ++i)
-    if (kn_stride[i] < 0 || kn_stride[i] % 8 != 0 || vn_stride[i] < 0 || vn_stride[i] % 8 != 0)
-      return CODEC_ERR_SHAPE;
-  const int complete = (k->n_tail + 1 == k->block) ? 1 : 0;
-  if (complete && (k->n_blocks + 1 > k->capacity || v->n_blocks + 1 > v->capacity)) return CODEC_ERR_CAPACITY;
-  AppendArgs A;
-  memset(&A, 0, sizeof(A));
-  const codec_stream *ss[2] = {k, v};
-  const void *nw[2] = {k_new, v_new};
-  const int64_t *ns[2] = {kn_stride, vn_stride};
-  for (int i = 0; i < 2; ++i) {
-    EncodeArgs &e = A.e[i];
-    e = stream_encode_args(ss[i]);
-    const int64_t R = ss[i]->block, D = ss[i]->head_dim;
-    e.src0 = ss[i]->tail;
-    e.s0_b = ss[i]->heads * R * D;
-    e.s0_h = R * D;
-    e.s0_t = D;
-    e.src1 = nw[i];
-    e.s1_b = ns[i][0];
-    e.s1_h = ns[i][1];
-    e.split_i = (int32_t)(R - 1);
-    e.n_new = 1;
-  }
-  A.t = k->n_tail;
-  A.complete = complete;
-  fill_M(k->fmt, k->block, k->keep, A.M);
-  (void)hipGetLastError();
-  if (launch_append(k->head_dim, A, k->batch * k->heads, stream) != 0) return CODEC_ERR_HIP;
-  for (codec_stream *s : {k, v}) {
-    if (complete) {
-      s->n_blocks += 1;
-      s->n_tail = 0;
-    } else {
-      s->n_tail += 1;
-    }
-  }
-  return CODEC_OK;
+  return launch_append_step(k, v, k_new, kn_stride, v_new, vn_stride, stream);
 }
 
 int codec_decode_workspace_bytes(const codec_stream *k, const codec_stream *v, int64_t Hq, size_t *bytes) {
@@ -307,59 +404,48 @@ int codec_decode_workspace_bytes(const codec_stream *k, const codec_stream *v, i
 int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
                            const codec_stream *v, float scale, void *out, const int64_t out_stride[2],
                            int32_t out_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !q_stride || !out || !out_stride) return CODEC_ERR_NULL;
-  int rc = check_decode(k, v, Hq);
+  Plan p;
+  const int rc = check_decode_call(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, workspace,
+                                   workspace_bytes, &p);
   if (rc) return rc;
-  if (out_dtype != CODEC_F32 && out_dtype != CODEC_BF16) return CODEC_ERR_FORMAT;
-  if (!(scale > 0.0f) || !isfinite(scale)) return CODEC_ERR_SCALE;
-  if (!aligned16(q) || q_stride[0] < 0 || q_stride[1] < 0 || q_stride[0] % 8 || q_stride[1] % 8)
-    return CODEC_ERR_SHAPE;
-  if (out_stride[0] < 0 || out_stride[1] < 0) return CODEC_ERR_SHAPE;
-  const Plan p = make_plan(k, v, Hq);
-  if (!p.ok) return CODEC_ERR_UNSUPPORTED;
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < p.bytes)
-    return CODEC_ERR_WORKSPACE;
+  return launch_decode_call(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, workspace, p, nullptr,
+                            nullptr, nullptr, nullptr, stream);
+}
 
-  DecodeArgs a;
-  memset(&a, 0, sizeof(a));
-  a.q = static_cast<const uint16_t *>(q);
-  a.q_sb = q_stride[0];
-  a.q_sh = q_stride[1];
-  a.krows = k->rows;
-  a.kscales = k->scales;
-  a.ktail = k->tail;
-  a.vrows = v->rows;
-  a.vscales = v->scales;
-  a.vtail = v->tail;
-  a.k_bh_rows = k->capacity * k->keep;
-  a.v_bh_rows = v->capacity * v->keep;
-  a.kf = row_fmt(k->fmt);
-  a.vf = row_fmt(v->fmt);
-  a.png = k->fmt == CODEC_PNG ? 1 : 0;
-  a.kraw = k->raw_dtype;
-  a.vraw = v->raw_dtype;
-  a.H = (int32_t)k->heads;
-  a.G = (int32_t)(Hq / k->heads);
-  a.NQG = p.NQG;
-  a.R = k->block;
-  a.S = k->keep;
-  a.n_blocks = k->n_blocks;
-  a.n_tail = k->n_tail;
-  a.ns = p.ns;
-  a.chunk = p.chunk;
-  a.qk_scale = (float)((double)scale * 1.4426950408889634);   // log2(e)
-  a.out = out;
-  a.o_sb = out_stride[0];
-  a.o_sh = out_stride[1];
-  a.out_f32 = out_dtype == CODEC_F32 ? 1 : 0;
-  char *ws = static_cast<char *>(workspace);
-  a.counters = reinterpret_cast<uint32_t *>(ws);
-  a.part_ml = reinterpret_cast<float *>(ws + p.off_ml);
-  a.part_acc = reinterpret_cast<float *>(ws + p.off_acc);
-  (void)hipGetLastError();
-  const int lr = launch_decode(k->head_dim, p.GS, p.SP, row_fmt(k->fmt), row_fmt(v->fmt), a, p.n_wg, stream);
-  if (lr < 0) return CODEC_ERR_UNSUPPORTED;
-  if (lr > 0) return CODEC_ERR_HIP;
+int codec_decode_attention_append(const void *q, const int64_t q_stride[2], int64_t Hq, codec_stream *k,
+                                  codec_stream *v, const void *k_new, const int64_t kn_stride[2],
+                                  const void *v_new, const int64_t vn_stride[2], float scale, void *out,
+                                  const int64_t out_stride[2], int32_t out_dtype, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_append(k, v, k_new, kn_stride, v_new, vn_stride);
+  if (rc) return rc;
+  // the decode is validated on the streams as the append leaves them
+  const bool complete = k->n_tail + 1 == k->block;
+  codec_stream k2 = *k, v2 = *v;
+  for (codec_stream *s : {&k2, &v2}) {
+    if (complete) {
+      s->n_blocks += 1;
+      s->n_tail = 0;
+    } else {
+      s->n_tail += 1;
+    }
+  }
+  Plan p;
+  rc = check_decode_call(q, q_stride, Hq, &k2, &v2, scale, out, out_stride, out_dtype, workspace,
+                         workspace_bytes, &p);
+  if (rc) return rc;
+  if (complete) {
+    // the token completes a block: archive it, then attend
+    rc = launch_append_step(k, v, k_new, kn_stride, v_new, vn_stride, stream);
+    if (rc) return rc;
+    return launch_decode_call(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, workspace, p, nullptr,
+                              nullptr, nullptr, nullptr, stream);
+  }
+  rc = launch_decode_call(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, workspace, p, k_new,
+                          kn_stride, v_new, vn_stride, stream);
+  if (rc) return rc;
+  k->n_tail += 1;
+  v->n_tail += 1;
   return CODEC_OK;
 }
 

@@ -925,22 +925,53 @@ __device__ __forceinline__ void process_lv(const TileBuf<D, GS, KF, VF> &B, int 
 // time so it needs few registers.  Every token is a block with R = S = 1.
 // acc (VALU layout) is rescaled here; alpha is returned for other
 // accumulators of the same heads.
+// A fused new token (t_new >= 0) is tail row t_new: its key and value rows
+// are read from kn / vn (rows past the old tail read zeros from the tail,
+// every other row reads zeros from the new token), and with store_new the
+// lanes holding it also write it to tail slot t_new.
 template <int D, int GS, int SP, int SWR, int RAWK, int RAWV, int EV>
-__device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt, int lane, h2 (&qh)[GS][8],
+__device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt, const void *kn, const void *vn,
+                                          int t_new, bool store_new, int lane, h2 (&qh)[GS][8],
                                           const float (&cq)[GS], float *sw, float (&m_u)[GS], float &m_lane,
                                           float &l_lane, float (&acc)[GS][EV], float (&alpha)[GS]) {
   constexpr int LK = D / 16, RK = 64 / LK, EBK = ebytes(RAWK), EBV = ebytes(RAWV);
   constexpr int LV = D / EV, RV = 64 / LV, VDW = EV * EBV / 4;
   static_assert(kMaxR % RV == 0 && kMaxR % RK == 0, "tail steps must tile the tail rows");
-  // Up to PK key and PV value load steps are requested together (rows past
-  // the tail read zeros), so the first chunk of both costs one round trip.
-  constexpr int PK = cmin(kMaxR / RK, 4), PV = cmin(kMaxR / RV, 8);
-  const rsrc_t rk = make_rsrc(kt, (uint32_t)nt * D * EBK);
-  const rsrc_t rv = make_rsrc(vt, (uint32_t)nt * D * EBV);
+  // Up to PK key and PV value load steps (about 16 registers of data each,
+  // 8 with eight heads per group) are requested together (rows past the tail
+  // read zeros), so the first chunk of both costs one round trip.
+  constexpr int BUDGET = GS >= 8 ? 8 : 16;
+  constexpr int PK = cmin(kMaxR / RK, cmax(1, BUDGET / (4 * EBK))), PV = cmin(kMaxR / RV, cmax(1, BUDGET / VDW));
+  const int t_old = t_new >= 0 ? t_new : nt;   // rows held by the tail slab
+  const rsrc_t rk = make_rsrc(kt, (uint32_t)t_old * D * EBK);
+  const rsrc_t rv = make_rsrc(vt, (uint32_t)t_old * D * EBV);
+  constexpr uint32_t kOut = 0x40000000u;        // an offset past every range: the load reads zeros
   const int rrk = lane / LK, ck = lane % LK;
   const int rrv = lane / LV, cv = lane % LV;
   const uint32_t offk = (uint32_t)(rrk * D + ck * 16) * EBK;
   const uint32_t offv = (uint32_t)(rrv * D + cv * EV) * EBV;
+  // The new token's rows, held by the lanes whose row in a step it is
+  // (zeros in every other lane), merged into its step's registers below.
+  uint4 knw[EBK];
+  uint32_t vnw[VDW];
+  {
+    const rsrc_t rkn = make_rsrc(kn, t_new >= 0 ? (uint32_t)(D * EBK) : 0u);
+    const rsrc_t rvn = make_rsrc(vn, t_new >= 0 ? (uint32_t)(D * EBV) : 0u);
+    const uint32_t onk = t_new >= 0 && rrk == t_new % RK ? (uint32_t)(ck * 16) * EBK : kOut;
+    const uint32_t onv = t_new >= 0 && rrv == t_new % RV ? (uint32_t)(cv * EV) * EBV : kOut;
+#pragma unroll
+    for (int k = 0; k < EBK; ++k) knw[k] = bload128(rkn, onk + 16 * k, 0);
+    if constexpr (VDW % 4 == 0) {
+#pragma unroll
+      for (int k = 0; k < VDW / 4; ++k) {
+        const uint4 t = bload128(rvn, onv + 16 * k, 0);
+        vnw[4 * k] = t.x; vnw[4 * k + 1] = t.y; vnw[4 * k + 2] = t.z; vnw[4 * k + 3] = t.w;
+      }
+    } else {
+      const uint2 t = bload64(rvn, onv, 0);
+      vnw[0] = t.x; vnw[1] = t.y;
+    }
+  }
   uint4 kb[PK][EBK];
   uint32_t vb[PV][VDW];
   auto load_k = [&](int r00) {
@@ -964,11 +995,49 @@ __device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt
       }
     }
   };
+  // OR the new token into the step that holds its row (its lanes read zeros from the slab)
+  auto merge_k = [&](int r00) {
+#pragma unroll
+    for (int s = 0; s < PK; ++s)
+      if (t_new >= r00 + s * RK && t_new < r00 + (s + 1) * RK) {
+#pragma unroll
+        for (int k = 0; k < EBK; ++k)
+          kb[s][k] = make_uint4(kb[s][k].x | knw[k].x, kb[s][k].y | knw[k].y, kb[s][k].z | knw[k].z,
+                                kb[s][k].w | knw[k].w);
+      }
+  };
+  auto merge_v = [&](int r00) {
+#pragma unroll
+    for (int s = 0; s < PV; ++s)
+      if (t_new >= r00 + s * RV && t_new < r00 + (s + 1) * RV) {
+#pragma unroll
+        for (int k = 0; k < VDW; ++k) vb[s][k] |= vnw[k];
+      }
+  };
+  // the new token's rows into tail slot t_new (the lanes that hold it)
+  auto store_new_rows = [&]() {
+    if (!store_new) return;
+    if (rrk == t_new % RK) {
+#pragma unroll
+      for (int k = 0; k < EBK; ++k)
+        *reinterpret_cast<uint4 *>(static_cast<char *>(const_cast<void *>(kt)) +
+                                   (size_t)(t_new * D + ck * 16) * EBK + 16 * k) = knw[k];
+    }
+    if (rrv == t_new % RV) {
+      uint32_t *dst = reinterpret_cast<uint32_t *>(static_cast<char *>(const_cast<void *>(vt)) +
+                                                   (size_t)(t_new * D + cv * EV) * EBV);
+#pragma unroll
+      for (int k = 0; k < VDW; ++k) dst[k] = vnw[k];
+    }
+  };
   load_k(0);
   load_v(0);
+  merge_k(0);
+  store_new_rows();
   kcompute<D, GS, SWR, RAWK, PK, EBK>(kb, nt, lane, qh, cq, sw, 0);
   for (int r00 = PK * RK; r00 < nt; r00 += PK * RK) {
     load_k(r00);
+    merge_k(r00);
     kcompute<D, GS, SWR, RAWK, PK, EBK>(kb, nt, lane, qh, cq, sw, r00);
   }
   wave_lds_sync();
@@ -977,9 +1046,11 @@ __device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt
   logits_any<GS, SP, SWR>(unit, sw, nt, 1, 1, lane, m_u, m_lane, l_lane, alpha);
   rescale(acc, alpha);
   wave_lds_sync();
+  merge_v(0);
   vcompute<D, GS, SWR, RAWV, PV, VDW, EV>(vb, nt, lane, sw, acc, 0);
   for (int r00 = PV * RV; r00 < nt; r00 += PV * RV) {
     load_v(r00);
+    merge_v(r00);
     vcompute<D, GS, SWR, RAWV, PV, VDW, EV>(vb, nt, lane, sw, acc, r00);
   }
   wave_lds_sync();
@@ -1105,7 +1176,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   }
 
   // ---- the raw tail: one wave of the last split, on the VALU paths
-  const bool tail_wave = a.n_tail > 0 && split == a.ns - 1 && wave == ntiles % W;
+  const bool tail_wave = a.n_tail + a.fuse_new > 0 && split == a.ns - 1 && wave == ntiles % W;
   // tail accumulator beside the MFMA layout: ET columns per lane, few registers
   constexpr int ET = C::VM ? cmax(D / 64, 16 / GS) : 1, LT = D / ET;
   float acct[C::VM ? GS : 1][ET];
@@ -1115,20 +1186,30 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     for (int e = 0; e < ET; ++e) acct[g][e] = 0.0f;
   if (tail_wave) {
     if constexpr (C::KM) setup_q_valu<D, GS>(a, b, hq0, lane, Q.qh, Q.cq);
-    const int nt = a.n_tail;
-    const char *kt = static_cast<const char *>(a.ktail) + bh * (int64_t)R * D * (a.kraw == BF16 ? 2 : 4);
-    const char *vt = static_cast<const char *>(a.vtail) + bh * (int64_t)R * D * (a.vraw == BF16 ? 2 : 4);
+    const int nt = a.n_tail + a.fuse_new;
+    const int ebk = a.kraw == BF16 ? 2 : 4, ebv = a.vraw == BF16 ? 2 : 4;
+    const char *kt = static_cast<const char *>(a.ktail) + bh * (int64_t)R * D * ebk;
+    const char *vt = static_cast<const char *>(a.vtail) + bh * (int64_t)R * D * ebv;
+    // a fused new token: row n_tail of the tail, stored to its slot by query group 0
+    const int t_new = a.fuse_new ? a.n_tail : -1;
+    const bool store_new = a.fuse_new && qg == 0;
+    const char *kn = a.fuse_new ? static_cast<const char *>(a.knew) + (b * a.kn_sb + (int64_t)h * a.kn_sh) * ebk : kt;
+    const char *vn = a.fuse_new ? static_cast<const char *>(a.vnew) + (b * a.vn_sb + (int64_t)h * a.vn_sh) * ebv : vt;
     float alpha[GS];
     auto run = [&](auto &tacc) {
       constexpr int E = sizeof(tacc[0]) / sizeof(float);
       if (a.kraw == BF16 && a.vraw == BF16)
-        tail_pass<D, GS, SP, SWR, BF16, BF16, E>(kt, vt, nt, lane, Q.qh, Q.cq, L.sw, m_u, m_lane, l_lane, tacc, alpha);
+        tail_pass<D, GS, SP, SWR, BF16, BF16, E>(kt, vt, nt, kn, vn, t_new, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
+                                                 m_lane, l_lane, tacc, alpha);
       else if (a.kraw == F32 && a.vraw == F32)
-        tail_pass<D, GS, SP, SWR, F32, F32, E>(kt, vt, nt, lane, Q.qh, Q.cq, L.sw, m_u, m_lane, l_lane, tacc, alpha);
+        tail_pass<D, GS, SP, SWR, F32, F32, E>(kt, vt, nt, kn, vn, t_new, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
+                                               m_lane, l_lane, tacc, alpha);
       else if (a.kraw == BF16)
-        tail_pass<D, GS, SP, SWR, BF16, F32, E>(kt, vt, nt, lane, Q.qh, Q.cq, L.sw, m_u, m_lane, l_lane, tacc, alpha);
+        tail_pass<D, GS, SP, SWR, BF16, F32, E>(kt, vt, nt, kn, vn, t_new, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
+                                                m_lane, l_lane, tacc, alpha);
       else
-        tail_pass<D, GS, SP, SWR, F32, BF16, E>(kt, vt, nt, lane, Q.qh, Q.cq, L.sw, m_u, m_lane, l_lane, tacc, alpha);
+        tail_pass<D, GS, SP, SWR, F32, BF16, E>(kt, vt, nt, kn, vn, t_new, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
+                                                m_lane, l_lane, tacc, alpha);
     };
     if constexpr (C::VM) {
       run(acct);

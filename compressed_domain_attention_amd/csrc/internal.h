@@ -118,6 +118,13 @@ struct DecodeArgs {
   int64_t chunk;          // blocks per split
   float qk_scale;         // softmax scale * log2(e)
   int32_t png;            // 1: PNG mode synthesis (cumulative sum), else the DCT-II basis
+  // Fused append (fuse_new = 1): one new key / value token per (b, h) joins
+  // the raw tail as slot n_tail (it does not complete a block); the tail
+  // pass reads it from knew / vnew and query group 0 stores it to the slot.
+  int32_t fuse_new;
+  const void *knew;
+  const void *vnew;
+  int64_t kn_sb, kn_sh, vn_sb, vn_sh;
   void *out;
   int64_t o_sb, o_sh;
   int32_t out_f32;        // 1: fp32 out, 0: bf16 out

@@ -198,6 +198,26 @@ int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * codec_decode_attention_append -- one decode step of a layer in one call:
+ * codec_append_step(k, v, k_new, .., v_new, ..) followed by
+ * codec_decode_attention(q, .., k, v, ..), with identical results, stream
+ * state and output.  The pages attend to the new token as part of the
+ * cache (cache.py ``append`` then triton_attention.py); when the token does
+ * not complete a block, the decode launch itself reads it as tail row
+ * n_tail and stores it to that tail slot (one launch instead of two); a
+ * token that completes a block is archived by the append launch first.
+ * Arguments as in the two calls; the workspace must satisfy
+ * codec_decode_workspace_bytes for the streams as the append leaves them.
+ * Errors: those of both calls, all checked before any launch; counters
+ * change only on success.
+ */
+int codec_decode_attention_append(const void *q, const int64_t q_stride[2], int64_t Hq, codec_stream *k,
+                                  codec_stream *v, const void *k_new, const int64_t kn_stride[2],
+                                  const void *v_new, const int64_t vn_stride[2], float scale, void *out,
+                                  const int64_t out_stride[2], int32_t out_dtype, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
  * codec_materialise -- the decoded (materialised) view of a stream, e.g. for
  * prefill attention.  cache.py ``_CodecStream.read`` / ``_decode_pending``:
  * the view is the archived blocks decoded, X_hat = M^T C block by block

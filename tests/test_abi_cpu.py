@@ -38,7 +38,7 @@ def test_header_symbols_exported(lib):
     names = declared_functions()
     assert set(names) == {"codec_basis", "codec_encode_blocks", "codec_append_step",
                           "codec_decode_workspace_bytes", "codec_decode_attention", "codec_status_string",
-                          "codec_materialise", "codec_crop", "codec_select_batch"}
+                          "codec_materialise", "codec_crop", "codec_select_batch", "codec_decode_attention_append"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -263,3 +263,29 @@ def test_png_mode_validation(lib):
     assert lib.codec_decode_workspace_bytes(ctypes.byref(k), ctypes.byref(v), 8, ctypes.byref(n)) == FORMAT
     v.fmt = bd.FMT_PNG
     assert lib.codec_decode_workspace_bytes(ctypes.byref(k), ctypes.byref(v), 8, ctypes.byref(n)) == OK
+
+
+def test_decode_append_validation(lib):
+    k = stream(n_blocks=16, capacity=16, n_tail=3)
+    v = stream(n_blocks=16, capacity=16, n_tail=3)
+    two, qs = bd._I64_2(1024, 128), bd._I64_2(2048, 128)
+    n = ctypes.c_size_t(0)
+    k2, v2 = stream(n_blocks=16, capacity=16, n_tail=4), stream(n_blocks=16, capacity=16, n_tail=4)
+    assert lib.codec_decode_workspace_bytes(ctypes.byref(k2), ctypes.byref(v2), 16, ctypes.byref(n)) == OK
+
+    def call(kk=k, vv=v, kn=FAKE, ks=two, scale=0.1, ws=FAKE, wsb=n.value, Hq=16):
+        return lib.codec_decode_attention_append(FAKE, qs, Hq, ctypes.byref(kk), ctypes.byref(vv), kn, ks, FAKE, two,
+                                                 ctypes.c_float(scale), FAKE, qs, bd.FMT_F32, ws, wsb, None)
+
+    assert call(kn=None) == NULL
+    assert call(ks=bd._I64_2(1024, 130)) == SHAPE
+    assert call(vv=stream(n_blocks=16, capacity=16, n_tail=2)) == SHAPE
+    assert call(scale=-1.0) == SCALE
+    assert call(Hq=6) == SHAPE
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=n.value - 1) == WORKSPACE
+    # a token that completes a block needs archive capacity
+    kf, vf = stream(n_blocks=16, capacity=16, n_tail=7), stream(n_blocks=16, capacity=16, n_tail=7)
+    assert call(kk=kf, vv=vf) == CAPACITY
+    for s in (k, v, kf, vf):
+        assert s.n_blocks == 16 and s.n_tail in (3, 7)
