@@ -74,10 +74,33 @@ __device__ inline void store_raw(void *base, int64_t elem_off, int raw, const fl
   }
 }
 
+// Wave maximum of non-negative doubles.  Their bit patterns order like
+// unsigned 64-bit integers, so both halves move through DPP / gfx950
+// half-wave swaps (no LDS) and the larger pattern wins.
+template <int CTRL>
+__device__ inline uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ inline uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ inline double wave_max_f64(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
-  return v;
+  uint64_t u = __builtin_bit_cast(uint64_t, v);
+  u = umax64(u, dpp64<0xB1>(u));    // quad_perm [1,0,3,2]
+  u = umax64(u, dpp64<0x4E>(u));    // quad_perm [2,3,0,1]
+  u = umax64(u, dpp64<0x141>(u));   // row_half_mirror
+  u = umax64(u, dpp64<0x140>(u));   // row_mirror
+  {
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    u = umax64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);
+  }
+  {
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    u = umax64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);
+  }
+  return __builtin_bit_cast(double, u);
 }
 
 __device__ inline int8_t quantise(double c, float s32, double inv) {
@@ -103,11 +126,11 @@ __device__ void encode_block(const EncodeArgs &a, const float *__restrict__ M, i
 #pragma unroll
     for (int e = 0; e < EPL; ++e) c[j][e] = 0.0;  // +0.0
 
-  // PIPE (a lone block, latency-bound): tokens are loaded eight at a time, all
+  // PIPE (a lone block, latency-bound): tokens are loaded sixteen at a time, all
   // requests in flight together.  Otherwise (many blocks in flight, register
   // bound) one token at a time.  Products are added in token order either way
   // (the contract's summation order).
-  constexpr int U = PIPE ? 8 : 1;
+  constexpr int U = PIPE ? 16 : 1;
   for (int i0 = 0; i0 < R; i0 += U) {
     float x[U][EPL];
 #pragma unroll
