@@ -1066,7 +1066,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   static_assert(!C::KM || C::RG * 16 <= SWR, "key MFMA rows exceed scratch");
   static_assert(!C::VM || (C::CH * 32 == SWR && C::VQ * 1024 <= SWR * D), "value tile exceeds scratch");
   constexpr int MERGE_BYTES = (W * GS * D + W * GS * 2) * 4;
-  constexpr int LDS_BYTES = cmax(W * WL::BYTES, MERGE_BYTES);
+  constexpr int COMBINE_BYTES = (4 * NT + kMaxSplits * GS + GS) * 4;
+  constexpr int LDS_BYTES = cmax(W * WL::BYTES, cmax(MERGE_BYTES, COMBINE_BYTES));
   __shared__ __attribute__((aligned(16))) char lds_raw[LDS_BYTES];
   __shared__ __attribute__((aligned(16))) float sA[kMaxR * SP];
   __shared__ int last_flag;
@@ -1339,47 +1340,91 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   __syncthreads();
   if (!last_flag) return;
 
-  // ---- last arrival: every (head, column) loads the (max, sum) and the
-  // partial of up to CB splits per round of device-scope loads (one round
-  // for CB or fewer splits) and folds them into a running (max, sum, acc).
-  // The partial accumulators are read with system-scope (sc0 sc1) buffer
-  // loads: coherent across the XCDs like device-scope ones, and measured
-  // faster for this just-written data; the (max, sum) pairs, the same
-  // address across a wave, with device-scope loads.
-  constexpr int CB = 32, kSysScope = 1 | 16;
+  // ---- last arrival: fold the ns partials of every (head, column).  Wave
+  // g < GS turns head g's (max, sum) pairs into split weights exp2(m - M)
+  // (zero for empty splits) and the total sum; every thread sums the weighted
+  // partials of one float4 column over every NG-th split (its loads issued
+  // before the weights are known), and the NG shares are added in a fixed
+  // order.  Partials and pairs are read with system-scope (sc0 sc1) buffer
+  // loads, coherent across the XCDs; out-of-range splits read zeros.
+  constexpr int kSysScope = 1 | 16;
+  constexpr int NC = GS * D / 4, NG = NT / NC, CP = 8, KS = kMaxSplits / 64;
+  static_assert(NG >= 1 && NG * NC == NT, "float4 columns tile the workgroup");
   const int ns = a.ns;
   const rsrc_t racc = make_rsrc(a.part_acc + pairq * ns * GS * D, (uint32_t)ns * GS * D * 4);
-  const float *Pml = a.part_ml + pairq * ns * GS * 2;
-  for (int idx = tid; idx < GS * D; idx += NT) {
-    const int g = idx / D, d = idx % D;
-    float M = -INFINITY, Lsum = 0.0f, sacc = 0.0f;
-    for (int sp0 = 0; sp0 < ns; sp0 += CB) {
-      float m[CB], l[CB], p[CB];
+  const rsrc_t rml = make_rsrc(a.part_ml + pairq * ns * GS * 2, (uint32_t)ns * GS * 2 * 4);
+  float4 *red = reinterpret_cast<float4 *>(lds);   // [NG][NC] shares
+  float *fw = lds + 4 * NT;                        // [kMaxSplits][GS] split weights
+  float *ltot = fw + kMaxSplits * GS;              // [GS] total sums
+  const int c = tid % NC, gi = tid / NC, g = c / (D / 4);
+  const int gw = wave % GS;
+  float2 ml[KS];
 #pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        const int sp = sp0 + u < ns ? sp0 + u : ns - 1;   // in range; duplicates are masked below
-        m[u] = __hip_atomic_load(Pml + 2 * (sp * GS + g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        l[u] = __hip_atomic_load(Pml + 2 * (sp * GS + g) + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        p[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(racc, 4 * (sp * GS * D + idx), 0, kSysScope));
-      }
-      float Mn = M;
+  for (int k = 0; k < KS; ++k)
+    ml[k] = __builtin_bit_cast(
+        float2, __builtin_amdgcn_raw_buffer_load_b64(rml, 8 * ((lane + 64 * k) * GS + gw), 0, kSysScope));
+  auto load_round = [&](int s0, float4 (&p)[CP]) {
 #pragma unroll
-      for (int u = 0; u < CB; ++u)
-        if (sp0 + u < ns && l[u] > 0.0f) Mn = fmaxf(Mn, m[u]);
-      const float fo = Mn == M ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
-      Lsum *= fo;
-      sacc *= fo;
-      M = Mn;
+    for (int u = 0; u < CP; ++u)
+      p[u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            racc, 4 * ((s0 + u * NG) * GS * D + 4 * c), 0, kSysScope));
+  };
+  float4 p[CP];
+  load_round(gi, p);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    float M = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        if (sp0 + u < ns && l[u] > 0.0f) {
-          const float f = __builtin_amdgcn_exp2f(m[u] - M);
-          Lsum = fmaf(l[u], f, Lsum);
-          sacc = fmaf(p[u], f, sacc);
-        }
+    for (int k = 0; k < KS; ++k)
+      if (ml[k].y > 0.0f) M = fmaxf(M, ml[k].x);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, xshfl(M, o));
+    float Ls = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const float f = ml[k].y > 0.0f ? __builtin_amdgcn_exp2f(ml[k].x - M) : 0.0f;
+      Ls = fmaf(ml[k].y, f, Ls);
+      if (wave < GS && lane + 64 * k < ns) fw[(lane + 64 * k) * GS + gw] = f;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) Ls += xshfl(Ls, o);
+    if (wave < GS && lane == 0) ltot[gw] = Ls;
+  }
+  __syncthreads();
+  float4 s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = gi;;) {
+#pragma unroll
+    for (int u = 0; u < CP; ++u) {
+      const int sp = s0 + u * NG;
+      const float f = sp < ns ? fw[sp * GS + g] : 0.0f;
+      if (f != 0.0f) {
+        s4.x = fmaf(f, p[u].x, s4.x);
+        s4.y = fmaf(f, p[u].y, s4.y);
+        s4.z = fmaf(f, p[u].z, s4.z);
+        s4.w = fmaf(f, p[u].w, s4.w);
       }
     }
-    store_out(g, d, sacc / Lsum);
+    s0 += CP * NG;
+    if (s0 >= ns) break;
+    load_round(s0, p);
+  }
+  red[gi * NC + c] = s4;
+  __syncthreads();
+  if (gi == 0) {
+    float4 t = red[c];
+    for (int j = 1; j < NG; ++j) {
+      const float4 r = red[j * NC + c];
+      t.x += r.x;
+      t.y += r.y;
+      t.z += r.z;
+      t.w += r.w;
+    }
+    const float Lg = ltot[g];
+    const int d0 = 4 * (c % (D / 4));
+    store_out(g, d0, t.x / Lg);
+    store_out(g, d0 + 1, t.y / Lg);
+    store_out(g, d0 + 2, t.z / Lg);
+    store_out(g, d0 + 3, t.w / Lg);
   }
   if (tid == 0) __hip_atomic_store(a.counters + pairq * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
