@@ -50,6 +50,16 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def arith_note(w):
+    """How each contraction of the workload's row formats is computed."""
+    k = ("keys: int8 x int8 MFMA (query as int8 digits), products summed exactly in int32"
+         if w.kfmt == "i8" else "keys: fp32 VALU FMAs")
+    v = {"i8": "values: int8 x int8 MFMA (weights as int8 digits), products summed exactly in int32",
+         "bf16": "values: bf16 MFMA (weights as three bf16 terms), products exact in fp32",
+         }.get(w.vfmt, "values: fp32 VALU FMAs")
+    return f"{k}; {v}; fp32 softmax, scaling and accumulation"
+
+
 def load_traffic(workload):
     """HBM traffic per decode launch from the committed counter summary, if it
     was taken on the current kernel source; else None."""
@@ -341,8 +351,7 @@ def main():
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(elapsed_ms / K, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32",
-        "arith": "int8 x int8 MFMA products summed exactly in int32 (int8 rows, query and weights as int8 digits); "
-                 "fp32 softmax, scaling and accumulation", "data": "synthetic AR(1) KV drawn on the device (seeded), N(0,1) q",
+        "arith": arith_note(w), "data": "synthetic AR(1) KV drawn on the device (seeded), N(0,1) q",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "T0": w.T,
                    "R": w.R, "S": w.S, "k_rows": w.kfmt, "v_rows": w.vfmt, "layers_rotated": L,
                    "step": "per layer: codec_decode_attention_append (append + decode), HIP graph per step"},

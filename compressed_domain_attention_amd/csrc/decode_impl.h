@@ -145,7 +145,8 @@ struct Cfg {
   static constexpr int TR = decode_tile_rows(D, KF, VF);   // rows per tile (K+V ~ 8 KB)
   static constexpr int SWR = cmax(cdiv(TR, 32) * 32, kMaxR);   // rows of the per-head scratch
   static constexpr bool KM = KF == I8;                  // key rows through int8 MFMA
-  static constexpr bool VM = VF == I8;                  // value rows through int8 MFMA
+  static constexpr bool VM = VF == I8 || VF == BF16;   // value rows through MFMA (int8 or bf16)
+  static constexpr int RBV = D * EBV;                   // bytes of a value row
   // VALU key path: lane = 16 consecutive elements of one row
   static constexpr int LK = D / 16, RK = 64 / LK, KSTEPS = cdiv(TR, RK), KQ = EBK;
   // MFMA key path: 16-row groups x 64-element k steps; N blocks of 4 heads x 4 limb slots
@@ -224,7 +225,7 @@ __device__ __forceinline__ void issue_v(TileBuf<D, GS, KF, VF> &B, const TileRef
   if constexpr (C::VM) {
 #pragma unroll
     for (int c = 0; c < C::VQ; ++c) B.v.v[c] = bload128(rv, 16 * lane, 1024 * c);
-    B.v.vs = bloadf(make_rsrc(T.vs, (uint32_t)T.nrows * 4), 4 * lane, 0);
+    if constexpr (VF == I8) B.v.vs = bloadf(make_rsrc(T.vs, (uint32_t)T.nrows * 4), 4 * lane, 0);
   } else {
     const int rrv = lane / C::LV, cv = lane % C::LV;
     const uint32_t vv = (uint32_t)(rrv * D + cv * C::EV) * C::EBV;
@@ -362,12 +363,88 @@ __device__ __forceinline__ void kcompute_mfma(const KBuf<D, GS, KF, VF, true> &k
 }
 
 // ------------------------------------------------------ V phase (MFMA) --
-// The tile's int8 value rows go to LDS row-major with 16-byte chunks XOR
-// swizzled by row, so the transpose reads below hit distinct banks.
-template <int D>
+// The tile's value rows (RB bytes each) go to LDS row-major with 16-byte
+// chunks XOR swizzled by row, so the transpose reads below hit distinct banks.
+template <int RB>
 __device__ __forceinline__ int vlds_off(int row, int chunk16) {
-  constexpr int NC = D / 16, SW = NC < 8 ? NC : 8;
-  return row * D + ((chunk16 ^ (row % SW)) * 16);
+  constexpr int NC = RB / 16, SW = NC < 8 ? NC : 8;
+  return row * RB + ((chunk16 ^ (row % SW)) * 16);
+}
+
+// (x, y) rounded to bf16 (ties to even, v_cvt_pk_bf16_f32), x in the low half.
+__device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){x, y}, b2v));
+}
+
+// bf16 value rows (no scales): acc[mb][nb] += sum over the tile's rows of
+// w[g][row] * v[row][col] on v_mfma_f32_16x16x32_bf16.  Each weight is split
+// into three bf16 terms hi + mid + lo (each the rounded remainder of the one
+// before, together the fp32 weight to its last bits); A row m = 4 * head +
+// term (term 3 is zero), so one MFMA forms the three partial sums of a head,
+// each product exact in fp32, and the lane adds them.  The values come from
+// LDS through ds_read_b64_tr_b16, which hands lane i of a 16-lane group
+// element (i % 4) of the 8 bytes addressed by lane 4j + i/4, j = 0..3: with
+// lane k pointing at row r + k/4, columns 4*(k%4) .. of the block, lane i
+// receives column i of rows r .. r+3; two reads give the 8 rows of the B
+// operand.  Rows past the staged tile are zero (cleared once), rows past
+// nrows have zero weight.
+template <int D, int GS, int SWR, int KF, int VF>
+__device__ __forceinline__ void vcompute_mfma_bf16(int nrows, int lane, const float *sw, const char *vl,
+                                                   float (&acc)[cdiv(GS, 4)][D / 16]) {
+  using C = Cfg<D, GS, KF, VF>;
+  typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  const int m = lane % 16, G = lane / 16, k = lane % 16;
+  const int term = m % 4;
+#pragma unroll
+  for (int ch = 0; ch < C::CH; ++ch) {
+    const int r0 = 32 * ch + 8 * G;
+    v8bf A[C::MB];
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      const int g = 4 * mb + m / 4;
+      const float *wp = sw + (g < GS ? g : 0) * SWR + r0;
+      const float4 wa = *reinterpret_cast<const float4 *>(wp);
+      const float4 wb = *reinterpret_cast<const float4 *>(wp + 4);
+      const float wr[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+      // pairs of weights: three packed roundings (hi, mid, lo), each of the
+      // remainder left by the ones before; the lane keeps its term (term 3: zero)
+      uint32_t a[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float w0 = (g < GS && r0 + 2 * p < nrows) ? wr[2 * p] : 0.0f;
+        const float w1 = (g < GS && r0 + 2 * p + 1 < nrows) ? wr[2 * p + 1] : 0.0f;
+        const uint32_t t0 = pk_bf16(w0, w1);
+        const float x0 = w0 - __uint_as_float(t0 << 16), x1 = w1 - __uint_as_float(t0 & 0xFFFF0000u);
+        const uint32_t t1 = pk_bf16(x0, x1);
+        const float y0 = x0 - __uint_as_float(t1 << 16), y1 = x1 - __uint_as_float(t1 & 0xFFFF0000u);
+        const uint32_t t2 = pk_bf16(y0, y1);
+        a[p] = term == 0 ? t0 : (term == 1 ? t1 : (term == 2 ? t2 : 0u));
+      }
+      A[mb] = __builtin_bit_cast(v8bf, a);
+    }
+    const int trow = r0 + k / 4;
+#pragma unroll
+    for (int nb = 0; nb < C::NBV; ++nb) {
+      const int cb = 2 * nb + (k % 4) / 2;   // 16-byte chunk of columns 16 nb + 4 (k % 4) ..
+      const v4s b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s *)(vl + vlds_off<C::RBV>(trow, cb) + 8 * (k % 2)));
+      const v4s b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s *)(vl + vlds_off<C::RBV>(trow + 4, cb) + 8 * (k % 2)));
+      const v8s bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      const v8bf B = __builtin_bit_cast(v8bf, bb);
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        const f4v z = {0.0f, 0.0f, 0.0f, 0.0f};
+        const f4v c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], B, z, 0, 0, 0);
+        acc[mb][nb] += (c[0] + c[1]) + c[2];
+      }
+    }
+  }
 }
 
 // acc[mb][nb] (lane: head 4*mb + lane/16, column 16*nb + lane%16) +=
@@ -387,13 +464,18 @@ __device__ __forceinline__ void vcompute_mfma(const VBuf<D, GS, KF, VF, true> &v
 #pragma unroll
   for (int c = 0; c < C::VQ; ++c) {
     const int q = lane + 64 * c;            // 16-byte chunk of the tile
-    const int row = q / (D / 16), ch16 = q % (D / 16);
-    if (row < SWR) *reinterpret_cast<uint4 *>(vl + vlds_off<D>(row, ch16)) = vb.v[c];
+    const int row = q / (C::RBV / 16), ch16 = q % (C::RBV / 16);
+    if (row < SWR) *reinterpret_cast<uint4 *>(vl + vlds_off<C::RBV>(row, ch16)) = vb.v[c];
   }
-  svs[lane] = vb.vs;
+  if constexpr (VF == I8) svs[lane] = vb.vs;
   wave_lds_sync();
   const int m = lane % 16, G = lane / 16;
   const int which = m % 4;
+  if constexpr (VF == BF16) {
+    vcompute_mfma_bf16<D, GS, SWR, KF, VF>(nrows, lane, sw, vl, acc);
+    wave_lds_sync();
+    return;
+  }
 #pragma unroll
   for (int ch = 0; ch < C::CH; ++ch) {
     const float4 vs0 = *reinterpret_cast<const float4 *>(svs + 32 * ch + 8 * G);
@@ -437,7 +519,7 @@ __device__ __forceinline__ void vcompute_mfma(const VBuf<D, GS, KF, VF, true> &v
       for (int nb = 0; nb < C::NBV; ++nb) {
         typedef int v2i __attribute__((ext_vector_type(2)));
         const v2i bt = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i *)(vl + vlds_off<D>(trow, nb) + 8 * (k % 2)));
+            (__attribute__((address_space(3))) v2i *)(vl + vlds_off<C::RBV>(trow, nb) + 8 * (k % 2)));
         v4i z = {0, 0, 0, 0};
         const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, __builtin_bit_cast(long, bt), z, 0, 0, 0);
         acc[mb][nb] = fmaf(dn, ((float)c[0] + 256.0f * (float)c[1]) + 65536.0f * (float)c[2], acc[mb][nb]);
@@ -874,7 +956,7 @@ struct WaveLds {
   using C = Cfg<D, GS, KF, VF>;
   static constexpr int SW_BYTES = C::SWR * GS * 4 + 64 * 4;
   static constexpr int SC_BYTES = 64 * 4;
-  static constexpr int VT_BYTES = C::VM ? C::SWR * D : 0;
+  static constexpr int VT_BYTES = C::VM ? C::SWR * C::RBV : 0;
   static constexpr int BYTES = SW_BYTES + SC_BYTES + VT_BYTES;
   float *sw;
   float *svs;
@@ -1064,7 +1146,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   static_assert(C::TR <= 64, "one scale per lane and tile");
   static_assert(C::TR <= SWR && C::KSTEPS * C::RK <= SWR && C::VSTEPS * C::RV <= SWR, "tile exceeds scratch");
   static_assert(!C::KM || C::RG * 16 <= SWR, "key MFMA rows exceed scratch");
-  static_assert(!C::VM || (C::CH * 32 == SWR && C::VQ * 1024 <= SWR * D), "value tile exceeds scratch");
+  static_assert(!C::VM || (C::CH * 32 == SWR && C::VQ * 1024 <= SWR * C::RBV), "value tile exceeds scratch");
   constexpr int MERGE_BYTES = (W * GS * D + W * GS * 2) * 4;
   constexpr int COMBINE_BYTES = (4 * NT + kMaxSplits * GS + GS) * 4;
   constexpr int LDS_BYTES = cmax(W * WL::BYTES, cmax(MERGE_BYTES, COMBINE_BYTES));
@@ -1153,6 +1235,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   if (tid < kMaxR * SP) sA[tid] = a_arg;
   // weights of rows past a tile's end multiply zero data: keep them finite
   for (int i = lane; i < SWR * GS; i += 64) L.sw[i] = 0.0f;
+  // bf16 value rows past the staged tile meet zero weights: keep them zero (not NaN)
+  if constexpr (C::VM && VF == BF16)
+    for (int i = lane; i < SWR * C::RBV / 16; i += 64) reinterpret_cast<uint4 *>(L.vl)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
   bas.load(sA, R, S, lane);
   if constexpr (C::KM)

@@ -84,6 +84,12 @@ DECODE_CASES = [
     (1, 4, 2, 128, 8, 2, "i8", "i8", 7, "bf16"),               # tail only
     (1, 4, 2, 128, 8, 2, "i8", "i8", 1, "bf16"),               # one token
     (3, 24, 3, 64, 4, 1, "i8", "i8", 4 * 333 + 2, "bf16"),     # S = 1
+    # bf16 value rows on the MFMA path: G = 4, 2, 1 (absent heads in an M
+    # block), D = 64 (two 32-row chunks per tile), fp32 tokens, R = 32
+    (1, 8, 2, 64, 8, 2, "i8", "bf16", 8 * 50 + 3, "bf16"),
+    (2, 4, 2, 128, 16, 4, "bf16", "bf16", 16 * 30 + 7, "f32"),
+    (1, 2, 2, 128, 8, 3, "f32", "bf16", 8 * 33, "bf16"),
+    (1, 8, 2, 128, 32, 16, "i8", "bf16", 32 * 12 + 17, "bf16"),
 ]
 
 
