@@ -1219,6 +1219,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   using QR = typename std::conditional<C::KM, QRegMfma<D, GS>, QRegValu<D, GS>>::type;
   QR qr;
   qr.load(a, b, hq0, lane);
+  // NBUF register buffers per wave: the first NBUF tiles are requested at once
+  TileBuf<D, GS, KF, VF> bufs[C::NBUF];
+#pragma unroll
+  for (int i = 0; i < C::NBUF; ++i) issue(bufs[i], tile_ref(wave + i * W), lane);
   // A[r][j] = c_j cos(pi (2r + 1) j / (2R)), the orthonormal DCT-II synthesis
   // (flashcodec-kv README, "Math"), entry r * SP + j per thread, zero padded.
   // PNG mode (README "Math", PNG item): token r = anchor + deltas 1..r, A[r][j] = [j <= r].
@@ -1228,10 +1232,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     const float cj = j == 0 ? sqrtf(1.0f / (float)R) : sqrtf(2.0f / (float)R);
     a_arg = a.png ? (j <= r ? 1.0f : 0.0f) : cj * cospif((float)((2 * r + 1) * j) / (float)(2 * R));
   }
-  // NBUF register buffers per wave: the first NBUF tiles are requested at once
-  TileBuf<D, GS, KF, VF> bufs[C::NBUF];
-#pragma unroll
-  for (int i = 0; i < C::NBUF; ++i) issue(bufs[i], tile_ref(wave + i * W), lane);
   if (tid < kMaxR * SP) sA[tid] = a_arg;
   // weights of rows past a tile's end multiply zero data: keep them finite
   for (int i = lane; i < SWR * GS; i += 64) L.sw[i] = 0.0f;
