@@ -98,30 +98,32 @@ int launch_gather(const GatherArgs &g, int64_t n_units, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode --
 struct DecodeArgs {
-  const uint16_t *q;      // bf16 (B, Hq, 1, D)
-  int64_t q_sb, q_sh;
+  // The first 64 bytes hold what the first tile requests need, the next 64
+  // the shape and the query, so a workgroup starts on two scalar loads.
   const void *krows;
-  const float *kscales;
-  const void *ktail;
   const void *vrows;
+  const float *kscales;
   const float *vscales;
-  const void *vtail;
   int64_t k_bh_rows;      // coefficient rows per (b, h) in the key archive
   int64_t v_bh_rows;
-  int32_t kf, vf;         // row formats
-  int32_t kraw, vraw;     // tail formats
+  int64_t n_blocks;
+  int64_t chunk;          // blocks per split
   int32_t H, G, NQG;      // kv heads, group size, query groups per kv head
   int32_t R, S;
-  int64_t n_blocks;
   int32_t n_tail;
   int32_t ns;             // splits per (b, h, query group)
-  int64_t chunk;          // blocks per split
   float qk_scale;         // softmax scale * log2(e)
+  const uint16_t *q;      // bf16 (B, Hq, 1, D)
+  int64_t q_sb, q_sh;
+  int32_t kf, vf;         // row formats
+  int32_t kraw, vraw;     // tail formats
   int32_t png;            // 1: PNG mode synthesis (cumulative sum), else the DCT-II basis
   // Fused append (fuse_new = 1): one new key / value token per (b, h) joins
   // the raw tail as slot n_tail (it does not complete a block); the tail
   // pass reads it from knew / vnew and query group 0 stores it to the slot.
   int32_t fuse_new;
+  const void *ktail;
+  const void *vtail;
   const void *knew;
   const void *vnew;
   int64_t kn_sb, kn_sh, vn_sb, vn_sh;
@@ -132,6 +134,7 @@ struct DecodeArgs {
   float *part_ml;         // [pairs][ns][GS][2]
   float *part_acc;        // [pairs][ns][GS][D]
 };
+static_assert(offsetof(DecodeArgs, H) == 64 && offsetof(DecodeArgs, q_sh) == 112, "kernel argument lines");
 
 // Heads of one query group handled per workgroup, and padded kept rows.
 int decode_group_size(int G);
