@@ -19,8 +19,11 @@ ARCH = "gfx950"
 SOURCES = ["api.cpp", "encode.hip", "archive.hip"] + [f"decode_{k}_{v}.hip" for k in ("i8", "bf16", "f32") for v in ("i8", "bf16", "f32")]
 
 # Packed fp32 VALU ops are disabled for all device code.
+# Leading scalar kernel arguments are preloaded into SGPRs at wave launch
+# (the compiler keeps a loading entry for firmware without the feature).
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-kernarg-preload-count=16",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wno-unused-command-line-argument"]
 
 

@@ -130,6 +130,9 @@ Plan make_plan(const codec_stream *k, const codec_stream *v, int64_t Hq) {
   // call's partials where they expect a zero counter.  More than one split
   // only happens below kTargetWorkgroups pairs, which bounds the region.
   if (p.ns > 1 && p.pairs > kTargetWorkgroups) p.ok = false;
+  // the launch: grid z = batch rows x kv heads, row counts per (b, h) in 32 bits
+  if (k->batch * k->heads > 65535 || k->capacity * k->keep > INT32_MAX || v->capacity * v->keep > INT32_MAX)
+    p.ok = false;
   const size_t counters = (size_t)kTargetWorkgroups * kCounterStride * 4;
   const size_t ml = align256((size_t)p.pairs * p.ns * p.GS * 2 * 4);
   const size_t acc = (size_t)p.pairs * p.ns * p.GS * k->head_dim * 4;

@@ -1138,8 +1138,15 @@ __device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt
   wave_lds_sync();
 }
 
+// The first tiles' addresses come as separate leading arguments (row counts
+// in 32 bits) so that they can be preloaded into scalar registers at wave
+// launch; everything else is in `a`.
 template <int D, int GS, int SP, int KF, int VF>
-__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *krows, const char *vrows,
+                                                                   const float *kscales, const float *vscales,
+                                                                   int32_t k_bh_rows, int32_t v_bh_rows,
+                                                                   int32_t chunk_rows, int32_t n_rows,
+                                                                   int32_t tile_rows, DecodeArgs a) {
   using C = Cfg<D, GS, KF, VF>;
   using WL = WaveLds<D, GS, KF, VF>;
   constexpr int W = C::W, EV = C::EV, SWR = C::SWR, NT = 64 * W;
@@ -1158,12 +1165,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile addresses live in SGPRs
-  // grid: x = split, y = kv head * query groups + query group, z = batch row
+  // grid: x = split, y = query group, z = batch row * kv heads + kv head
   const int split = blockIdx.x;
-  const int qg = (int)(blockIdx.y % (unsigned)a.NQG);
-  const int h = (int)(blockIdx.y / (unsigned)a.NQG);
-  const int b = blockIdx.z;
-  const int64_t bh = (int64_t)b * a.H + h;
+  const int qg = blockIdx.y;
+  const int64_t bh = blockIdx.z;
+  const int h = (int)(blockIdx.z % (unsigned)a.H);
+  const int b = (int)(blockIdx.z / (unsigned)a.H);
   const int64_t pairq = bh * a.NQG + qg;
   const int hq0 = h * a.G + qg * GS;
   const int R = a.R, S = a.S;
@@ -1188,28 +1195,26 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   }
   float m_lane = -INFINITY, l_lane = 0.0f;   // running max and sum of this lane's head, (lane % 16) % GS
 
-  // ---- this wave's tiles: t = wave, wave + W, ... of the split
-  const int NB = C::TR / S;
-  const int64_t blk0 = (int64_t)split * a.chunk;
-  const int64_t blk1 = (blk0 + a.chunk < a.n_blocks) ? blk0 + a.chunk : a.n_blocks;
-  const int nblk = blk1 > blk0 ? (int)(blk1 - blk0) : 0;   // a split holds < 2^31 blocks
-  const int ntiles = (nblk + NB - 1) / NB;
-  const int64_t k_bh = bh * a.k_bh_rows, v_bh = bh * a.v_bh_rows;
+  // ---- this wave's tiles: t = wave, wave + W, ... of the split; a tile is
+  // tile_rows = (TR / S) * S rows (whole blocks), a split chunk_rows rows
+  const int64_t r0s = (int64_t)split * chunk_rows;
+  const int64_t r1s = r0s + chunk_rows < n_rows ? r0s + chunk_rows : n_rows;
+  const int nrs = r1s > r0s ? (int)(r1s - r0s) : 0;
+  const int ntiles = (nrs + tile_rows - 1) / tile_rows;
+  const int64_t k_bh = bh * k_bh_rows, v_bh = bh * v_bh_rows;
   // Tiles past the split's end are empty (zero rows): their loads are out of
   // range and return zeros without touching memory, so every buffer is
   // re-requested unconditionally and the number of loads in flight is the
   // same on every path (the compiler's wait counts stay exact).
   auto tile_ref = [&](int t) {
     TileRef T;
-    const int64_t tb0 = blk0 + (int64_t)t * NB;
-    const int64_t left = blk1 - tb0;
-    const int nb = (int)(left < 0 ? 0 : (left < NB ? left : NB));
-    const int64_t row0 = tb0 * S;
-    T.k = static_cast<const char *>(a.krows) + (k_bh + row0) * D * C::EBK;
-    T.v = static_cast<const char *>(a.vrows) + (v_bh + row0) * D * C::EBV;
-    T.ks = KF == I8 ? a.kscales + k_bh + row0 : nullptr;
-    T.vs = VF == I8 ? a.vscales + v_bh + row0 : nullptr;
-    T.nrows = nb * S;
+    const int64_t row0 = r0s + (int64_t)t * tile_rows;
+    const int64_t left = r1s - row0;
+    T.k = krows + (k_bh + row0) * D * C::EBK;
+    T.v = vrows + (v_bh + row0) * D * C::EBV;
+    T.ks = KF == I8 ? kscales + k_bh + row0 : nullptr;
+    T.vs = VF == I8 ? vscales + v_bh + row0 : nullptr;
+    T.nrows = (int)(left < 0 ? 0 : (left < tile_rows ? left : tile_rows));
     return T;
   };
 
@@ -1516,10 +1521,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
 
 template <int D, int GS, int SP, int KF, int VF>
 int launch_one(const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
-  const unsigned gy = (unsigned)(a.H * a.NQG);
-  const unsigned gz = (unsigned)(n_wg / ((int64_t)a.ns * gy));
-  hipLaunchKernelGGL((decode_kernel<D, GS, SP, KF, VF>), dim3((unsigned)a.ns, gy, gz), dim3(64 * kDecodeWaves), 0,
-                     stream, a);
+  using C = Cfg<D, GS, KF, VF>;
+  const unsigned gy = (unsigned)a.NQG;
+  const int64_t gz = n_wg / ((int64_t)a.ns * gy);   // batch rows x kv heads
+  const int64_t tile_rows = (int64_t)(C::TR / a.S) * a.S;
+  const int64_t chunk_rows = a.chunk * a.S, n_rows = a.n_blocks * a.S;
+  if (gz > 65535 || a.k_bh_rows > INT32_MAX || a.v_bh_rows > INT32_MAX || chunk_rows > INT32_MAX ||
+      n_rows > INT32_MAX)
+    return -1;
+  hipLaunchKernelGGL((decode_kernel<D, GS, SP, KF, VF>), dim3((unsigned)a.ns, gy, (unsigned)gz),
+                     dim3(64 * kDecodeWaves), 0, stream, static_cast<const char *>(a.krows),
+                     static_cast<const char *>(a.vrows), a.kscales, a.vscales, (int32_t)a.k_bh_rows,
+                     (int32_t)a.v_bh_rows, (int32_t)chunk_rows, (int32_t)n_rows, (int32_t)tile_rows, a);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

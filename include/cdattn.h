@@ -190,7 +190,8 @@ int codec_decode_workspace_bytes(const codec_stream *k, const codec_stream *v,
  *   workspace    device, >= codec_decode_workspace_bytes, 256-byte aligned,
  *                zero-filled before its first use (see above).
  * Errors: NULL, SHAPE (includes an empty sequence), FORMAT, SCALE,
- * WORKSPACE, UNSUPPORTED, HIP.
+ * WORKSPACE, UNSUPPORTED (no kernel for the shape, B * H above 65535, or
+ * 2^31 or more coefficient rows per (b, h) in a stream's capacity), HIP.
  */
 int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
                            const codec_stream *k, const codec_stream *v, float scale,
