@@ -154,6 +154,13 @@ def test_workspace_plan(lib):
     big = stream(n_blocks=8192, capacity=8192)
     assert ws_bytes(lib, big, big, 16) == ws_bytes(lib, big, big, 16)
     assert ws_bytes(lib, big, big, 16)[1] >= n
+    # launch limits: batch rows x kv heads on one grid axis, rows per (b, h) in 32 bits
+    wide = stream(n_blocks=16, capacity=16, batch=16383, heads=4)
+    assert ws_bytes(lib, wide, wide, 16)[0] == OK
+    wide = stream(n_blocks=16, capacity=16, batch=16384, heads=4)
+    assert ws_bytes(lib, wide, wide, 16)[0] == UNSUPPORTED
+    deep = stream(n_blocks=16, capacity=(1 << 30), keep=2)
+    assert ws_bytes(lib, deep, deep, 16)[0] == UNSUPPORTED
 
 
 def test_decode_validation(lib):
