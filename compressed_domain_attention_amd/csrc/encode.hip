@@ -61,6 +61,32 @@ __device__ inline void load_raw(const void *base, int64_t elem_off, int raw, flo
   }
 }
 
+// The same with the raw format fixed at compile time (no branch, so the
+// loads of several tokens stay in flight together).
+template <int EPL, int RAW>
+__device__ inline void load_raw_t(const void *base, int64_t elem_off, float (&x)[EPL]) {
+  if constexpr (RAW == BF16) {
+    const uint16_t *p = static_cast<const uint16_t *>(base) + elem_off;
+    if constexpr (EPL == 1) {
+      x[0] = __uint_as_float((uint32_t)p[0] << 16);
+    } else if constexpr (EPL == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t *>(p);
+      x[0] = __uint_as_float(w << 16);
+      x[1] = __uint_as_float(w & 0xFFFF0000u);
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2 *>(p);
+      x[0] = __uint_as_float(w.x << 16);
+      x[1] = __uint_as_float(w.x & 0xFFFF0000u);
+      x[2] = __uint_as_float(w.y << 16);
+      x[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    }
+  } else {
+    const float *p = static_cast<const float *>(base) + elem_off;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = p[e];
+  }
+}
+
 template <int EPL>
 __device__ inline void store_raw(void *base, int64_t elem_off, int raw, const float (&x)[EPL]) {
   if (raw == BF16) {
@@ -114,34 +140,33 @@ __device__ inline int8_t quantise(double c, float s32, double inv) {
 
 // Encode block `n` (call-relative) of stream row (b, h) into archive slot
 // a.n0 + n.  One wave; lane owns head_dim elements [lane*EPL, lane*EPL+EPL).
-template <int EPL, int SP, bool PIPE>
-__device__ void encode_block(const EncodeArgs &a, const float *__restrict__ M, int64_t b, int64_t h,
-                             int64_t n, int lane) {
-  constexpr int D = EPL * 64;
+// The basis is copied from Mfill (the kernel arguments) into the wave's own
+// LDS slice M after the first round's loads are issued, so both are in
+// flight together.
+template <int EPL, int SP, int U, int RAW>
+__device__ void encode_sums(const EncodeArgs &a, float *M, const float *Mfill, int64_t b, int64_t h, int64_t n,
+                            int lane, double (&c)[SP][EPL]) {
   const int d0 = lane * EPL;
   const int R = a.R, S = a.S;
-  double c[SP][EPL];
-#pragma unroll
-  for (int j = 0; j < SP; ++j)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) c[j][e] = 0.0;  // +0.0
-
-  // PIPE (a lone block, latency-bound): tokens are loaded sixteen at a time, all
-  // requests in flight together.  Otherwise (many blocks in flight, register
-  // bound) one token at a time.  Products are added in token order either way
-  // (the contract's summation order).
-  constexpr int U = PIPE ? 16 : 1;
+  // U tokens per round, their loads all in flight together (token i comes
+  // from src0 below split_i, else from src1; indices past R repeat token R-1
+  // and are not used).  Products are added in token order (the contract's
+  // summation order).
   for (int i0 = 0; i0 < R; i0 += U) {
     float x[U][EPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = i0 + u;
-      if (i < R) {
-        if (i < a.split_i)
-          load_raw<EPL>(a.src0, b * a.s0_b + h * a.s0_h + (n * R + i) * a.s0_t + d0, a.raw, x[u]);
-        else
-          load_raw<EPL>(a.src1, b * a.s1_b + h * a.s1_h + d0, a.raw, x[u]);
-      }
+      const int i = i0 + u < R ? i0 + u : R - 1;
+      const bool f0 = i < a.split_i;
+      const void *src = f0 ? a.src0 : a.src1;
+      const int64_t off = f0 ? b * a.s0_b + h * a.s0_h + (n * R + i) * a.s0_t + d0 : b * a.s1_b + h * a.s1_h + d0;
+      load_raw_t<EPL, RAW>(src, off, x[u]);
+    }
+    if (i0 == 0) {
+      for (int k = lane; k < S * R; k += 64) M[k] = Mfill[k];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -158,6 +183,26 @@ __device__ void encode_block(const EncodeArgs &a, const float *__restrict__ M, i
       }
     }
   }
+}
+
+// U tokens' loads in flight per round: sixteen for a lone block (latency
+// bound), eight when many blocks are in flight.
+template <int EPL, int SP, bool PIPE>
+__device__ void encode_block(const EncodeArgs &a, float *M, const float *Mfill, int64_t b, int64_t h,
+                             int64_t n, int lane) {
+  constexpr int D = EPL * 64;
+  const int d0 = lane * EPL;
+  const int S = a.S;
+  double c[SP][EPL];
+#pragma unroll
+  for (int j = 0; j < SP; ++j)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) c[j][e] = 0.0;  // +0.0
+  constexpr int U = PIPE ? 16 : 8;
+  if (a.raw == BF16)
+    encode_sums<EPL, SP, U, BF16>(a, M, Mfill, b, h, n, lane, c);
+  else
+    encode_sums<EPL, SP, U, F32>(a, M, Mfill, b, h, n, lane, c);
 
   const int64_t slot = (b * a.H + h) * a.cap + a.n0 + n;
 #pragma unroll
@@ -187,29 +232,42 @@ __device__ void encode_block(const EncodeArgs &a, const float *__restrict__ M, i
   }
 }
 
+// The raw remainder of an encode call into tail slots 0 .. n_copy-1, eight
+// tokens' loads in flight per round.
+template <int EPL, int RAW>
+__device__ void copy_tail(const EncodeArgs &a, int64_t b, int64_t h, int64_t bh, int lane) {
+  const int d0 = lane * EPL;
+  for (int i0 = 0; i0 < a.n_copy; i0 += 8) {
+    float x[8][EPL];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u < a.n_copy ? i0 + u : a.n_copy - 1;
+      load_raw_t<EPL, RAW>(a.src0, b * a.s0_b + h * a.s0_h + (a.n_new * a.R + i) * a.s0_t + d0, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + u < a.n_copy) store_raw<EPL>(a.tail, ((bh * a.R) + i0 + u) * (EPL * 64) + d0, RAW, x[u]);
+  }
+}
+
 // Grid: x = (b, h) * per_bh + wave-group; each wave one block (or the tail copy).
 template <int EPL, int SP>
 __global__ __launch_bounds__(64 * kEncodeWaves) void encode_kernel(EncodeLaunch L, int64_t per_bh) {
   const EncodeArgs &a = L.e;
-  // kernel arguments may live in host-coherent memory: read the basis once
-  __shared__ float sM[kMaxS * kMaxR];
-  for (int i = threadIdx.x; i < a.S * a.R; i += 64 * kEncodeWaves) sM[i] = L.M[i];
-  __syncthreads();
+  __shared__ float sM[kEncodeWaves][kMaxS * kMaxR];   // one basis copy per wave
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t bh = blockIdx.x / per_bh;
   const int64_t n = (blockIdx.x % per_bh) * kEncodeWaves + wave;
   const int64_t b = bh / a.H, h = bh % a.H;
   if (n < a.n_new) {
-    encode_block<EPL, SP, false>(a, sM, b, h, n, lane);
+    encode_block<EPL, SP, false>(a, sM[wave], L.M, b, h, n, lane);
   } else if (n == a.n_new && a.n_copy > 0) {
     // raw remainder -> tail slots 0 .. n_copy-1, verbatim
-    const int d0 = lane * EPL;
-    for (int i = 0; i < a.n_copy; ++i) {
-      float x[EPL];
-      load_raw<EPL>(a.src0, b * a.s0_b + h * a.s0_h + (a.n_new * a.R + i) * a.s0_t + d0, a.raw, x);
-      store_raw<EPL>(a.tail, ((bh * a.R) + i) * (EPL * 64) + d0, a.raw, x);
-    }
+    if (a.raw == BF16)
+      copy_tail<EPL, BF16>(a, b, h, bh, lane);
+    else
+      copy_tail<EPL, F32>(a, b, h, bh, lane);
   }
 }
 
@@ -224,9 +282,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs A) {
     // tail slots 0..R-2 plus the new token form the block; slot R-1 of the
     // tail is not written since the tail empties.
     __shared__ float sM[kMaxS * kMaxR];
-    for (int i = lane; i < a.S * a.R; i += 64) sM[i] = A.M[i];
-    __syncthreads();
-    encode_block<EPL, SP, true>(a, sM, b, h, 0, lane);
+    encode_block<EPL, SP, true>(a, sM, A.M, b, h, 0, lane);
   } else {
     const int d0 = lane * EPL;
     float x[EPL];
