@@ -77,34 +77,40 @@ __device__ inline void load_raw(const void *src, int64_t off, int raw, float (&v
   }
 }
 
-// fp64 values of EPL consecutive elements of one coefficient row.
+// One coefficient row's EPL consecutive elements as raw 32-bit words (and
+// its scale for int8 rows), then their fp64 values: all rows of a block are
+// requested before any is converted, so their loads are in flight together.
 template <int RF, int EPL>
-__device__ inline void load_row(const void *rows, const float *scales, int64_t row, int D, int d0,
-                                double (&c)[EPL]) {
-  const int64_t off = row * D + d0;
-  if constexpr (RF == I8) {
-    const uint32_t *p = reinterpret_cast<const uint32_t *>(static_cast<const int8_t *>(rows) + off);
-    const double sc = (double)scales[row];
+struct RowWords {
+  static constexpr int NW = RF == I8 ? EPL / 4 : (RF == BF16 ? EPL / 2 : EPL);
+  uint32_t w[NW];
+  float sc;
+  __device__ inline void load(const void *rows, const float *scales, int64_t row, int D, int d0) {
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(static_cast<const char *>(rows) +
+                                                           (row * D + d0) * (RF == I8 ? 1 : (RF == BF16 ? 2 : 4)));
 #pragma unroll
-    for (int k = 0; k < EPL / 4; ++k) {
-      const uint32_t w = p[k];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) c[4 * k + e] = (double)(int)(int8_t)(w >> (8 * e)) * sc;   // exact
-    }
-  } else if constexpr (RF == BF16) {
-    const uint32_t *p = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(rows) + off);
-#pragma unroll
-    for (int k = 0; k < EPL / 2; ++k) {
-      const uint32_t w = p[k];
-      c[2 * k] = (double)__uint_as_float(w << 16);
-      c[2 * k + 1] = (double)__uint_as_float(w & 0xFFFF0000u);
-    }
-  } else {
-    const float *p = static_cast<const float *>(rows) + off;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) c[e] = (double)p[e];
+    for (int k = 0; k < NW; ++k) w[k] = p[k];
+    sc = RF == I8 ? scales[row] : 1.0f;
   }
-}
+  __device__ inline void values(double (&c)[EPL]) const {
+    if constexpr (RF == I8) {
+      const double s = (double)sc;
+#pragma unroll
+      for (int k = 0; k < NW; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[4 * k + e] = (double)(int)(int8_t)(w[k] >> (8 * e)) * s;   // exact
+    } else if constexpr (RF == BF16) {
+#pragma unroll
+      for (int k = 0; k < NW; ++k) {
+        c[2 * k] = (double)__uint_as_float(w[k] << 16);
+        c[2 * k + 1] = (double)__uint_as_float(w[k] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) c[e] = (double)__uint_as_float(w[e]);
+    }
+  }
+};
 
 // Grid: x = chunks of items, y = kv head, z = batch row.  Item k of (b, h) is
 // block blk0 + k (decoded) for k < nblk; item nblk copies the raw tail when
@@ -112,26 +118,41 @@ __device__ inline void load_row(const void *rows, const float *scales, int64_t r
 template <int RF, int SP, int EPL>
 __global__ __launch_bounds__(256) void view_kernel(ViewArgs a) {
   __shared__ double sA[kMaxR * SP];   // A[i][j] as fp64, zero past column S
-  for (int t = threadIdx.x; t < a.R * SP; t += 256) {
-    const int i = t / SP, j = t % SP;
-    sA[t] = j < a.S ? (double)a.A[i * a.S + j] : 0.0;
-  }
-  __syncthreads();
   const int lpi = a.D / EPL;                     // lanes per item
   const int64_t k = (int64_t)blockIdx.x * (256 / lpi) + threadIdx.x / lpi;
   const int d0 = EPL * (threadIdx.x % lpi);
   const int64_t h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = b * a.H + h;
   const int R = a.R, S = a.S;
+  // The basis entries (two per thread cover R * SP <= 512) and the block's
+  // coefficient rows are requested together (rows past S repeat row S-1, in
+  // range, and are zeroed below); the basis is staged once its words land.
+  const int nA = R * SP;
+  float av[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = (int)threadIdx.x + 256 * u, tc = t < nA ? t : nA - 1;
+    const int j = tc % SP;
+    av[u] = a.A[(tc / SP) * S + (j < S ? j : 0)];
+  }
+  RowWords<RF, EPL> rw[SP];
   if (k < a.nblk) {
-    const int64_t n = a.blk0 + k;
-    const int64_t row0 = (bh * a.cap + n) * S;   // first coefficient row of the block
+    const int64_t row0 = (bh * a.cap + a.blk0 + k) * S;   // first coefficient row of the block
+#pragma unroll
+    for (int j = 0; j < SP; ++j) rw[j].load(a.rows, a.scales, row0 + (j < S ? j : S - 1), a.D, d0);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = (int)threadIdx.x + 256 * u;
+    if (t < nA) sA[t] = t % SP < S ? (double)av[u] : 0.0;
+  }
+  __syncthreads();
+  if (k < a.nblk) {
     double c[SP][EPL];
 #pragma unroll
     for (int j = 0; j < SP; ++j) {
-      if (j < S) {
-        load_row<RF, EPL>(a.rows, a.scales, row0 + j, a.D, d0, c[j]);
-      } else {
+      rw[j].values(c[j]);
+      if (j >= S) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) c[j][e] = 0.0;
       }
