@@ -549,36 +549,8 @@ __device__ __forceinline__ void rescale_mfma(float (&acc)[MBK][NBK], const float
 
 // ------------------------------------------------------- VALU query setup --
 // fp16 pairs of the lane's 16 key elements (lane % (D/16) picks them),
-// pre-scaled per head by a power of two into fp16 range.
-template <int D, int GS>
-__device__ __forceinline__ void setup_q_valu(const DecodeArgs &a, int64_t b, int hq0, int lane, h2 (&qh)[GS][8],
-                                             float (&cq)[GS]) {
-  constexpr int LK = D / 16;
-  const int d0 = (lane % LK) * 16;
-#pragma unroll
-  for (int g = 0; g < GS; ++g) {
-    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + b * a.q_sb + (int64_t)(hq0 + g) * a.q_sh + d0);
-    const uint4 q0 = qp[0], q1 = qp[1];
-    const uint32_t wv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-    float qf[16];
-    float amax = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      qf[2 * t] = bf16lo(wv[t]);
-      qf[2 * t + 1] = bf16hi(wv[t]);
-      amax = fmaxf(amax, fmaxf(fabsf(qf[2 * t]), fabsf(qf[2 * t + 1])));
-    }
-    amax = group_red<LK, true>(amax);
-    int E = 0;
-    if (amax > 0.0f) frexpf(amax, &E);
-    const float up = ldexpf(1.0f, 15 - E);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) qh[g][t] = h2{(_Float16)(qf[2 * t] * up), (_Float16)(qf[2 * t + 1] * up)};
-    cq[g] = a.qk_scale * ldexpf(1.0f, E - 15);
-  }
-}
-
-// The same, loads issued ahead of the tiles and converted afterwards.
+// pre-scaled per head by a power of two into fp16 range; loads issued first,
+// converted once other loads are in flight.
 template <int D, int GS>
 struct QRegValu {
   static constexpr int LK = D / 16;
@@ -1011,11 +983,11 @@ __device__ __forceinline__ void process_lv(const TileBuf<D, GS, KF, VF> &B, int 
 // are read from kn / vn (rows past the old tail read zeros from the tail,
 // every other row reads zeros from the new token), and with store_new the
 // lanes holding it also write it to tail slot t_new.
-template <int D, int GS, int SP, int SWR, int RAWK, int RAWV, int EV>
+template <int D, int GS, int SP, int SWR, int RAWK, int RAWV, int EV, typename Prep>
 __device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt, const void *kn, const void *vn,
                                           int t_new, bool store_new, int lane, h2 (&qh)[GS][8],
                                           const float (&cq)[GS], float *sw, float (&m_u)[GS], float &m_lane,
-                                          float &l_lane, float (&acc)[GS][EV], float (&alpha)[GS]) {
+                                          float &l_lane, float (&acc)[GS][EV], float (&alpha)[GS], Prep &&prep) {
   constexpr int LK = D / 16, RK = 64 / LK, EBK = ebytes(RAWK), EBV = ebytes(RAWV);
   constexpr int LV = D / EV, RV = 64 / LV, VDW = EV * EBV / 4;
   static_assert(kMaxR % RV == 0 && kMaxR % RK == 0, "tail steps must tile the tail rows");
@@ -1116,6 +1088,7 @@ __device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt
   load_v(0);
   merge_k(0);
   store_new_rows();
+  prep();   // the query in the VALU layout, its loads issued before the tail's
   kcompute<D, GS, SWR, RAWK, PK, EBK>(kb, nt, lane, qh, cq, sw, 0);
   for (int r00 = PK * RK; r00 < nt; r00 += PK * RK) {
     load_k(r00);
@@ -1276,7 +1249,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
 #pragma unroll
     for (int e = 0; e < ET; ++e) acct[g][e] = 0.0f;
   if (tail_wave) {
-    if constexpr (C::KM) setup_q_valu<D, GS>(a, b, hq0, lane, Q.qh, Q.cq);
+    // MFMA key path: the VALU-layout query is loaded here and converted once
+    // the tail's own loads are in flight
+    QRegValu<D, GS> qv;
+    if constexpr (C::KM) qv.load(a, b, hq0, lane);
+    auto prep = [&]() {
+      if constexpr (C::KM) qv.convert(a, lane, Q.qh, Q.cq);
+    };
     const int nt = a.n_tail + a.fuse_new;
     const int ebk = a.kraw == BF16 ? 2 : 4, ebv = a.vraw == BF16 ? 2 : 4;
     const char *kt = static_cast<const char *>(a.ktail) + bh * (int64_t)R * D * ebk;
@@ -1291,16 +1270,16 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
       constexpr int E = sizeof(tacc[0]) / sizeof(float);
       if (a.kraw == BF16 && a.vraw == BF16)
         tail_pass<D, GS, SP, SWR, BF16, BF16, E>(kt, vt, nt, kn, vn, t_new, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
-                                                 m_lane, l_lane, tacc, alpha);
+                                                 m_lane, l_lane, tacc, alpha, prep);
       else if (a.kraw == F32 && a.vraw == F32)
         tail_pass<D, GS, SP, SWR, F32, F32, E>(kt, vt, nt, kn, vn, t_new, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
-                                               m_lane, l_lane, tacc, alpha);
+                                               m_lane, l_lane, tacc, alpha, prep);
       else if (a.kraw == BF16)
         tail_pass<D, GS, SP, SWR, BF16, F32, E>(kt, vt, nt, kn, vn, t_new, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
-                                                m_lane, l_lane, tacc, alpha);
+                                                m_lane, l_lane, tacc, alpha, prep);
       else
         tail_pass<D, GS, SP, SWR, F32, BF16, E>(kt, vt, nt, kn, vn, t_new, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
-                                                m_lane, l_lane, tacc, alpha);
+                                                m_lane, l_lane, tacc, alpha, prep);
     };
     if constexpr (C::VM) {
       run(acct);
