@@ -958,9 +958,10 @@ __device__ __forceinline__ void process_lv(const TileBuf<D, GS, KF, VF> &B, int 
                                            float &m_lane, float &l_lane, Acc<D, GS, KF, VF> &acc) {
   using C = Cfg<D, GS, KF, VF>;
   float alpha[GS];
-  // groups of 16 (block, head) items in a tile: the fewest kept rows a
-  // padded keep count SP allows is SP / 2 + 1 (S = 1 when SP = 2)
-  constexpr int kSmin = SP == 2 ? 1 : SP / 2 + 1;
+  // groups of 16 (block, head) items in a tile, bounded by the fewest kept
+  // rows a padded keep count SP allows: SP / 2 + 1, and 2 for SP = 2 (a
+  // tile with S = 1 has more groups and takes logits_any)
+  constexpr int kSmin = SP == 2 ? 2 : SP / 2 + 1;
   constexpr int NG = cmax(1, cdiv((C::TR / kSmin) * GS, 16));
   logits<GS, SP, C::SWR, NG>(bas, L.sw, nrows / S, R, S, lane, m_u, m_lane, l_lane, alpha);
   if constexpr (C::VM)
