@@ -51,7 +51,20 @@ __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float xshfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
+// op(v[l], v[l ^ 16]) and op(v[l], v[l ^ 32]) through the gfx950 row-pair
+// and half-wave swaps (no LDS): with both operands v, the swap returns the
+// lane's own value and its partner's, in an order that depends on the lane,
+// so op must be commutative (it is: max, or an fp32 sum of two terms).
+template <typename Op>
+__device__ __forceinline__ float xop16(float v, Op op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <typename Op>
+__device__ __forceinline__ float xop32(float v, Op op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // Sum / max over aligned groups of L consecutive lanes (every lane gets it).
 template <int L, bool MAX>
@@ -61,8 +74,8 @@ __device__ __forceinline__ float group_red(float v) {
   if constexpr (L >= 4) v = op(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
   if constexpr (L >= 8) v = op(v, dpp<0x141>(v));   // row_half_mirror
   if constexpr (L >= 16) v = op(v, dpp<0x140>(v));  // row_mirror
-  if constexpr (L >= 32) v = op(v, xshfl(v, 16));
-  if constexpr (L >= 64) v = op(v, xshfl(v, 32));
+  if constexpr (L >= 32) v = xop16(v, op);
+  if constexpr (L >= 64) v = xop32(v, op);
   return v;
 }
 
@@ -74,8 +87,8 @@ __device__ __forceinline__ float strided(float v) {
   if constexpr (L <= 2) v = op(v, dpp<0x122>(v));   // row_ror:2
   if constexpr (L <= 4) v = op(v, dpp<0x124>(v));   // row_ror:4
   if constexpr (L <= 8) v = op(v, dpp<0x128>(v));   // row_ror:8
-  if constexpr (L <= 16) v = op(v, xshfl(v, 16));
-  if constexpr (L <= 32) v = op(v, xshfl(v, 32));
+  if constexpr (L <= 16) v = xop16(v, op);
+  if constexpr (L <= 32) v = xop32(v, op);
   return v;
 }
 
@@ -316,8 +329,8 @@ struct QRegMfma {
           amax = fmaxf(amax, fmaxf(fabsf(qf[kk][2 * t]), fabsf(qf[kk][2 * t + 1])));
         }
       }
-      amax = fmaxf(amax, xshfl(amax, 16));
-      amax = fmaxf(amax, xshfl(amax, 32));
+      amax = xop16(amax, [](float x, float y) { return fmaxf(x, y); });
+      amax = xop32(amax, [](float x, float y) { return fmaxf(x, y); });
       int E = 0;
       if (amax > 0.0f) frexpf(amax, &E);
       const float up = ldexpf(1.0f, 22 - E);
@@ -1447,8 +1460,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
 #pragma unroll
     for (int k = 0; k < KS; ++k)
       if (ml[k].y > 0.0f) M = fmaxf(M, ml[k].x);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, xshfl(M, o));
+    M = group_red<64, true>(M);
     float Ls = 0.0f;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
@@ -1456,8 +1468,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
       Ls = fmaf(ml[k].y, f, Ls);
       if (wave < GS && lane + 64 * k < ns) fw[(lane + 64 * k) * GS + gw] = f;
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) Ls += xshfl(Ls, o);
+    Ls = group_red<64, false>(Ls);
     if (wave < GS && lane == 0) ltot[gw] = Ls;
   }
   __syncthreads();
