@@ -495,6 +495,18 @@ __device__ __forceinline__ void vcompute_mfma(const VBuf<D, GS, KF, VF, true> &v
     const float4 vs1 = *reinterpret_cast<const float4 *>(svs + 32 * ch + 8 * G + 4);
     const float vsj[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
     const int r0 = 32 * ch + 8 * G;
+    // the B operands of every N block first: their LDS reads overlap the
+    // weight conversion, and the MFMAs below then issue back to back
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    v2i bt[C::NBV];
+    {
+      const int k = lane % 16;
+      const int trow = 32 * ch + 8 * G + k / 2;
+#pragma unroll
+      for (int nb = 0; nb < C::NBV; ++nb)
+        bt[nb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i *)(vl + vlds_off<C::RBV>(trow, nb) + 8 * (k % 2)));
+    }
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
       const int g = 4 * mb + m / 4;
@@ -526,17 +538,15 @@ __device__ __forceinline__ void vcompute_mfma(const VBuf<D, GS, KF, VF, true> &v
       const float down = ldexpf(1.0f, E - 22);
       const float d0 = readlane(down, 0), d1 = readlane(down, 4), d2 = readlane(down, 8), d3 = readlane(down, 12);
       const float dn = G == 0 ? d0 : (G == 1 ? d1 : (G == 2 ? d2 : d3));
-      const int k = lane % 16;
-      const int trow = 32 * ch + 8 * G + k / 2;
+      v4i c[C::NBV];
 #pragma unroll
       for (int nb = 0; nb < C::NBV; ++nb) {
-        typedef int v2i __attribute__((ext_vector_type(2)));
-        const v2i bt = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i *)(vl + vlds_off<C::RBV>(trow, nb) + 8 * (k % 2)));
-        v4i z = {0, 0, 0, 0};
-        const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, __builtin_bit_cast(long, bt), z, 0, 0, 0);
-        acc[mb][nb] = fmaf(dn, ((float)c[0] + 256.0f * (float)c[1]) + 65536.0f * (float)c[2], acc[mb][nb]);
+        const v4i z = {0, 0, 0, 0};
+        c[nb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, __builtin_bit_cast(long, bt[nb]), z, 0, 0, 0);
       }
+#pragma unroll
+      for (int nb = 0; nb < C::NBV; ++nb)
+        acc[mb][nb] = fmaf(dn, ((float)c[nb][0] + 256.0f * (float)c[nb][1]) + 65536.0f * (float)c[nb][2], acc[mb][nb]);
     }
   }
   wave_lds_sync();
