@@ -717,9 +717,23 @@ struct Basis {
   float az[2][SK];   // A operand of z, token tile rt: A[16 rt + l%16][4 kk + l/16]
   float bw[2][4];    // B operand of w, token tile rt: A[16 rt + 4 (l/16) + kk][l%16]
   int rt_n;          // token tiles of 16: 1 if R <= 16 else 2
+  // SP = 2 with R <= 8: two items per MFMA column (item half h = rows 8h ..
+  // of z, coefficients 2h .. of its B operand, columns S h .. of w):
+  // A operand of z, A'[l%16][l/16]; B operand of w, B'[l/16][l%16] per step
+  float azp;
+  float bwp[4];
   __device__ __forceinline__ void load(const float *sA, int R, int S, int lane) {
     const int lo = lane % 16, hi = lane / 16;
     rt_n = R > 16 ? 2 : 1;
+    if constexpr (SP == 2) {
+      const int h = lo / 8, t = lo % 8, j = hi - 2 * h;
+      azp = (hi / 2 == h && t < R && j >= 0 && j < S) ? sA[t * SP + j] : 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int hb = hi / 2, tb = 4 * (hi % 2) + kk, jb = lo - S * hb;
+        bwp[kk] = (tb < R && jb >= 0 && jb < S) ? sA[tb * SP + jb] : 0.0f;
+      }
+    }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
@@ -913,6 +927,87 @@ __device__ __forceinline__ void logits(const Basis<SP> &A, float *sw, int nb, in
   l_lane = l_lane * a_lane + lsum;
 }
 
+// Tile version for SP = 2 and R <= 8: two (block, head) items per MFMA
+// column, so a group holds 32 items and both products run on half as many
+// groups.  Column n of group ig holds items ig*32 + n and ig*32 + 16 + n (the
+// same head); lane (hi, col) gives coefficient hi % 2 of item half hi / 2 and
+// receives z rows 4 hi .. 4 hi + 3, tokens 4 (hi % 2) .. of that item half;
+// w comes out with item half h in columns S h .. S h + S - 1.  Other shapes
+// (S = 1 tiles with more groups, R > 8) take logits / logits_any.
+template <int GS, int SWR, int NGP>
+__device__ __forceinline__ bool logits_packed(const Basis<2> &A, float *sw, int nb, int R, int S, int lane,
+                                              float (&m_u)[GS], float &m_lane, float &l_lane, float (&alpha)[GS]) {
+  const int items = nb * GS;
+  const int ngroups = (items + 31) / 32;
+  if (R > 8 || ngroups > NGP) return false;
+  const int col = lane % 16, hi = lane / 16;
+  const int g = col % GS, hh = hi / 2, jb = hi % 2;
+  constexpr float kSlack = 8.0f;
+  v4f z[NGP];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int ig = 0; ig < NGP; ++ig) {
+    if (ig < ngroups) {
+      const int it = ig * 32 + 16 * hh + col;
+      const bool live = it < items && jb < S;
+      const float sv = sw[live ? g * SWR + (it / GS) * S + jb : 0];
+      v4f zz = {0.0f, 0.0f, 0.0f, 0.0f};
+      zz = __builtin_amdgcn_mfma_f32_16x16x4f32(A.azp, live ? sv : 0.0f, zz, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool v = it < items && 4 * jb + i < R;
+        zz[i] = v ? zz[i] : -INFINITY;
+        mx = fmaxf(mx, zz[i]);
+      }
+      z[ig] = zz;
+    }
+  }
+  float m_new = m_lane, a_lane = 1.0f;
+  if (__builtin_amdgcn_ballot_w64(mx > m_lane + kSlack) != 0) {
+    mx = strided<GS, true>(mx);
+    m_new = fmaxf(m_lane, mx);
+    a_lane = m_new == m_lane ? 1.0f : __builtin_amdgcn_exp2f(m_lane - m_new);
+#pragma unroll
+    for (int gg = 0; gg < GS; ++gg) {
+      m_u[gg] = readlane(m_new, gg);
+      alpha[gg] = readlane(a_lane, gg);
+    }
+  } else {
+#pragma unroll
+    for (int gg = 0; gg < GS; ++gg) alpha[gg] = 1.0f;
+  }
+  m_lane = m_new;
+  float lsum = 0.0f;
+  // output column col: item half hs = col / S (col < 2 S), coefficient col - S hs
+  const int hs = col < S ? 0 : 1, jo = col - S * hs;
+#pragma unroll
+  for (int ig = 0; ig < NGP; ++ig) {
+    if (ig < ngroups) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(z[ig][i] - m_new);   // masked tokens: exp2(-inf) = 0
+        lsum += p[i];
+      }
+      v4f w0 = {0.0f, 0.0f, 0.0f, 0.0f}, w1 = w0, w2 = w0, w3 = w0;
+      w0 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[0], A.bwp[0], w0, 0, 0, 0);
+      w1 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[1], A.bwp[1], w1, 0, 0, 0);
+      w2 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[2], A.bwp[2], w2, 0, 0, 0);
+      w3 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[3], A.bwp[3], w3, 0, 0, 0);
+      // lane (hi, col) holds w of item columns 4 hi + i, slot col; lanes
+      // without a live (item, coefficient) store to the junk slots
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int it = ig * 32 + 16 * hs + 4 * hi + i;
+        const bool ok = col < 2 * S && it < items;
+        sw[ok ? (it % GS) * SWR + (it / GS) * S + jo : GS * SWR + lane] = (w0[i] + w1[i]) + (w2[i] + w3[i]);
+      }
+    }
+  }
+  l_lane = l_lane * a_lane + lsum;
+  return true;
+}
+
 // acc *= alpha, skipped when no head's running max moved (the common case).
 template <int GS, int EV>
 __device__ __forceinline__ void rescale(float (&acc)[GS][EV], const float (&alpha)[GS]) {
@@ -986,7 +1081,10 @@ __device__ __forceinline__ void process_lv(const TileBuf<D, GS, KF, VF> &B, int 
   // tile with S = 1 has more groups and takes logits_any)
   constexpr int kSmin = SP == 2 ? 2 : SP / 2 + 1;
   constexpr int NG = cmax(1, cdiv((C::TR / kSmin) * GS, 16));
-  logits<GS, SP, C::SWR, NG>(bas, L.sw, nrows / S, R, S, lane, m_u, m_lane, l_lane, alpha);
+  bool done = false;
+  if constexpr (SP == 2 && GS <= 4)   // (eight-head groups keep the registers for the plain path)
+    done = logits_packed<GS, C::SWR, cdiv(NG, 2)>(bas, L.sw, nrows / S, R, S, lane, m_u, m_lane, l_lane, alpha);
+  if (!done) logits<GS, SP, C::SWR, NG>(bas, L.sw, nrows / S, R, S, lane, m_u, m_lane, l_lane, alpha);
   if constexpr (C::VM)
     rescale_mfma<GS>(acc.m, alpha, lane);
   else

@@ -90,6 +90,10 @@ DECODE_CASES = [
     (2, 4, 2, 128, 16, 4, "bf16", "bf16", 16 * 30 + 7, "f32"),
     (1, 2, 2, 128, 8, 3, "f32", "bf16", 8 * 33, "bf16"),
     (1, 8, 2, 128, 32, 16, "i8", "bf16", 32 * 12 + 17, "bf16"),
+    # S <= 2: two items per logit MFMA column when R <= 8 (R = 6, 8), the
+    # plain path when R > 8
+    (1, 8, 2, 128, 6, 2, "i8", "i8", 6 * 201 + 5, "bf16"),
+    (3, 8, 2, 128, 16, 2, "i8", "i8", 16 * 64 + 3, "bf16"),
 ]
 
 
