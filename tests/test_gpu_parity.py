@@ -94,6 +94,10 @@ DECODE_CASES = [
     # plain path when R > 8
     (1, 8, 2, 128, 6, 2, "i8", "i8", 6 * 201 + 5, "bf16"),
     (3, 8, 2, 128, 16, 2, "i8", "i8", 16 * 64 + 3, "bf16"),
+    # eight-head groups with S = 2 (plain logit path), bf16 values at D = 256 and D = 64
+    (1, 16, 2, 128, 8, 2, "i8", "i8", 8 * 150 + 3, "bf16"),
+    (1, 8, 2, 256, 8, 3, "i8", "bf16", 8 * 60 + 5, "bf16"),
+    (2, 16, 2, 64, 8, 2, "i8", "bf16", 8 * 70 + 1, "bf16"),
 ]
 
 
