@@ -271,6 +271,125 @@ __global__ __launch_bounds__(64 * kEncodeWaves) void encode_kernel(EncodeLaunch 
   }
 }
 
+// Maximum of non-negative doubles over aligned groups of LPB lanes (8, 16
+// or 32), the same bit-pattern ordering as wave_max_f64.
+template <int LPB>
+__device__ inline double group_max_f64(double v) {
+  uint64_t u = __builtin_bit_cast(uint64_t, v);
+  u = umax64(u, dpp64<0xB1>(u));    // quad_perm [1,0,3,2]
+  u = umax64(u, dpp64<0x4E>(u));    // quad_perm [2,3,0,1]
+  u = umax64(u, dpp64<0x141>(u));   // row_half_mirror: eight lanes
+  if constexpr (LPB >= 16) u = umax64(u, dpp64<0x140>(u));   // row_mirror: sixteen
+  if constexpr (LPB >= 32) {
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    u = umax64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);
+  }
+  return __builtin_bit_cast(double, u);
+}
+
+// Bulk encode with wide lanes: a lane owns eight consecutive head_dim
+// elements of one block (16-byte token loads), LPB = D/8 lanes per block and
+// 64/LPB blocks per wave, blocks numbered across (b, h) rows.  EXACT: R ==
+// RP, so no token is conditional.  All RP (>= R) token loads are in flight together; the S coefficient rows are then formed
+// one after another from the registers, each element by the same fp64 FMA
+// chain in token order as encode_block, so the rows, codes and scales are
+// identical.  Waves past the block waves copy the raw remainder of one
+// (b, h) row each.  The basis comes from the kernel arguments through scalar
+// loads (its index is uniform).
+template <int LPB, int RP, int RAW, bool EXACT>
+__global__ __launch_bounds__(64 * kEncodeWaves) void encode_wide_kernel(EncodeLaunch L, int64_t BH,
+                                                                         int64_t block_waves) {
+  const EncodeArgs &a = L.e;
+  constexpr int D = LPB * 8, BPW = 64 / LPB, EPL = D / 64;
+  constexpr int WPT = RAW == BF16 ? 1 : 2;   // 16-byte words per token and lane
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * kEncodeWaves + (threadIdx.x >> 6);
+  const int R = a.R, S = a.S;
+  if (gw >= block_waves) {
+    const int64_t bh = gw - block_waves;
+    if (bh < BH && a.n_copy > 0) copy_tail<EPL, RAW>(a, bh / a.H, bh % a.H, bh, lane);
+    return;
+  }
+  const int64_t total = BH * a.n_new;
+  const int64_t gb = gw * BPW + lane / LPB;
+  const bool live = gb < total;
+  const int64_t gbc = live ? gb : total - 1;
+  const int64_t bh = gbc / a.n_new, n = gbc % a.n_new;
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const int d0 = (lane % LPB) * 8;
+  const char *src = static_cast<const char *>(a.src0) +
+                    (b * a.s0_b + h * a.s0_h + n * R * a.s0_t + d0) * (RAW == BF16 ? 2 : 4);
+  const int64_t tstride = a.s0_t * (RAW == BF16 ? 2 : 4);
+  uint4 x[RP][WPT];
+#pragma unroll
+  for (int u = 0; u < RP; ++u) {
+    const int i = u < R ? u : R - 1;
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) x[u][w] = *reinterpret_cast<const uint4 *>(src + i * tstride + 16 * w);
+  }
+  auto elem = [&](int u, int e) -> double {
+    if constexpr (RAW == BF16) {
+      const uint32_t wd = (&x[u][0].x)[e / 2];
+      return (double)__uint_as_float(e % 2 ? wd & 0xFFFF0000u : wd << 16);
+    } else {
+      return (double)__uint_as_float((&x[u][e / 4].x)[e % 4]);
+    }
+  };
+  const int64_t slot = (b * a.H + h) * a.cap + a.n0 + n;
+  for (int j = 0; j < S; ++j) {
+    // the row's basis entries, requested together (j*R + u < kMaxS*kMaxR
+    // for every u < RP, so the entries past R are in bounds and unused)
+    double m[RP];
+#pragma unroll
+    for (int u = 0; u < RP; ++u) m[u] = (double)L.M[j * R + u];
+    double c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = 0.0;   // +0.0
+#pragma unroll
+    for (int u = 0; u < RP; ++u) {
+      if (EXACT || u < R) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[e] = fma(m[u], elem(u, e), c[e]);
+      }
+    }
+    const int64_t row = (slot * S + j) * D + d0;
+    if (a.fmt == F32) {
+      if (live) {
+        float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(a.rows) + row);
+        p[0] = make_float4((float)c[0], (float)c[1], (float)c[2], (float)c[3]);
+        p[1] = make_float4((float)c[4], (float)c[5], (float)c[6], (float)c[7]);
+      }
+    } else if (a.fmt == BF16) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = (uint32_t)bf16_rne((float)c[2 * k]) | ((uint32_t)bf16_rne((float)c[2 * k + 1]) << 16);
+      if (live) *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.rows) + row) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      double amax = 0.0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmax(amax, fabs(c[e]));
+      amax = group_max_f64<LPB>(amax);
+      const float s32 = (float)(amax / 127.0);
+      const double inv = s32 != 0.0f ? 1.0 / (double)s32 : 0.0;
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e / 4] |= (uint32_t)(uint8_t)quantise(c[e], s32, inv) << (8 * (e % 4));
+      if (live) {
+        *reinterpret_cast<uint2 *>(static_cast<int8_t *>(a.rows) + row) = make_uint2(w[0], w[1]);
+        if (lane % LPB == 0) a.scales[slot * S + j] = s32;
+      }
+    }
+    // The token words count as changed here, so their conversions stay
+    // inside the row loop instead of being hoisted as RP x 8 doubles.
+#pragma unroll
+    for (int u = 0; u < RP; ++u)
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) asm volatile("" : "+v"(x[u][w].x), "+v"(x[u][w].y), "+v"(x[u][w].z), "+v"(x[u][w].w));
+  }
+}
+
 // Grid: x = (b, h), y = stream (0 keys, 1 values); one wave each.
 template <int EPL, int SP>
 __global__ __launch_bounds__(64) void append_kernel(AppendArgs A) {
@@ -322,8 +441,49 @@ int launch_append_epl(int SP, const AppendArgs &A, int64_t BH, hipStream_t strea
 
 }  // namespace
 
+template <int LPB, int RP>
+int launch_encode_wide(const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
+  constexpr int BPW = 64 / LPB;
+  const int64_t block_waves = (BH * L.e.n_new + BPW - 1) / BPW;
+  const int64_t waves = block_waves + (L.e.n_copy > 0 ? BH : 0);
+  if (waves == 0) return 0;
+  const dim3 grid((unsigned)((waves + kEncodeWaves - 1) / kEncodeWaves)), block(64 * kEncodeWaves);
+  const bool exact = L.e.R == RP;
+  if (L.e.raw == BF16) {
+    if (exact)
+      hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, BF16, true>), grid, block, 0, stream, L, BH, block_waves);
+    else
+      hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, BF16, false>), grid, block, 0, stream, L, BH, block_waves);
+  } else {
+    if (exact)
+      hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, F32, true>), grid, block, 0, stream, L, BH, block_waves);
+    else
+      hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, F32, false>), grid, block, 0, stream, L, BH, block_waves);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+template <int LPB>
+int launch_encode_wide_r(const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
+  return L.e.R <= 8 ? launch_encode_wide<LPB, 8>(L, BH, stream) : launch_encode_wide<LPB, 16>(L, BH, stream);
+}
+
 // Returns 0 on success, 1 on a HIP launch error, -1 if no kernel exists.
+// Blocks of up to 16 tokens from one source with 16-byte aligned rows take
+// the wide-lane kernel; the rest one wave per block.
 int launch_encode(int D, const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
+  const EncodeArgs &e = L.e;
+  const bool wide = e.split_i == e.R && e.R <= 16 && (e.raw == BF16 || e.raw == F32) &&
+                    ((uintptr_t)e.src0 | (uintptr_t)e.rows) % 16 == 0 && e.s0_b % 8 == 0 && e.s0_h % 8 == 0 &&
+                    e.s0_t % 8 == 0;
+  if (wide) {
+    switch (D) {
+      case 64: return launch_encode_wide_r<8>(L, BH, stream);
+      case 128: return launch_encode_wide_r<16>(L, BH, stream);
+      case 256: return launch_encode_wide_r<32>(L, BH, stream);
+      default: return -1;
+    }
+  }
   const int SP = decode_pad_keep(L.e.S);
   switch (D) {
     case 64: return launch_encode_epl<1>(SP, L, BH, stream);
