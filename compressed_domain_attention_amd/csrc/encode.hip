@@ -288,21 +288,38 @@ __device__ inline double group_max_f64(double v) {
   return __builtin_bit_cast(double, u);
 }
 
+// quantise() with the clamp taken on the integer (the same code: |rint(y)|
+// stays far inside the int range), as a byte.
+__device__ inline uint32_t quantise_byte(double c, float s32, double inv) {
+  if (s32 == 0.0f) return 0u;
+  const double y = c * inv;
+  double r = rint(y);
+  if (fabs(y - floor(y) - 0.5) < 1e-9) r = rint(c / (double)s32);
+  const int q = min(max((int)r, -127), 127);
+  return (uint32_t)q & 0xFFu;
+}
+
 // Bulk encode with wide lanes: a lane owns eight consecutive head_dim
 // elements of one block (16-byte token loads), LPB = D/8 lanes per block and
-// 64/LPB blocks per wave, blocks numbered across (b, h) rows.  EXACT: R ==
-// RP, so no token is conditional.  All RP (>= R) token loads are in flight together; the S coefficient rows are then formed
-// one after another from the registers, each element by the same fp64 FMA
-// chain in token order as encode_block, so the rows, codes and scales are
-// identical.  Waves past the block waves copy the raw remainder of one
-// (b, h) row each.  The basis comes from the kernel arguments through scalar
-// loads (its index is uniform).
-template <int LPB, int RP, int RAW, bool EXACT>
-__global__ __launch_bounds__(64 * kEncodeWaves) void encode_wide_kernel(EncodeLaunch L, int64_t BH,
+// 64/LPB blocks per wave, blocks numbered across (b, h) rows.  All RP (>= R)
+// token loads are in flight together.  The S coefficient rows are then
+// formed JC at a time: each token is widened to fp64 once per pass and
+// feeds the JC rows' sums, each element by the same fp64 FMA chain in token
+// order as encode_block, so rows, codes and scales are identical.  A pass
+// past row S - 1 computes unused sums (its basis reads stay inside
+// EncodeLaunch::M).  Each token's sums sit behind its own (uniform) u < R
+// test even when R == RP: the branch keeps the scheduler from widening every
+// token at once, which would take twice the registers.  Waves past the
+// block waves copy the raw remainder of one (b, h) row each.  The basis comes
+// from the kernel arguments through scalar loads (its index is uniform).
+template <int LPB, int RP, int JC, int RAW>
+__global__ __launch_bounds__(64 * kEncodeWaves) __attribute__((amdgpu_waves_per_eu(
+    RAW == BF16 ? (RP == 8 ? 4 : 3) : (RP == 8 ? 3 : 2)))) void encode_wide_kernel(EncodeLaunch L, int64_t BH,
                                                                          int64_t block_waves) {
   const EncodeArgs &a = L.e;
   constexpr int D = LPB * 8, BPW = 64 / LPB, EPL = D / 64;
   constexpr int WPT = RAW == BF16 ? 1 : 2;   // 16-byte words per token and lane
+  static_assert((kMaxS + JC - 1) * 16 + RP <= kMaxS * kMaxR, "basis reads stay inside M");
   const int lane = threadIdx.x & 63;
   const int64_t gw = (int64_t)blockIdx.x * kEncodeWaves + (threadIdx.x >> 6);
   const int R = a.R, S = a.S;
@@ -337,52 +354,62 @@ __global__ __launch_bounds__(64 * kEncodeWaves) void encode_wide_kernel(EncodeLa
     }
   };
   const int64_t slot = (b * a.H + h) * a.cap + a.n0 + n;
-  for (int j = 0; j < S; ++j) {
-    // the row's basis entries, requested together (j*R + u < kMaxS*kMaxR
-    // for every u < RP, so the entries past R are in bounds and unused)
-    double m[RP];
+  for (int j0 = 0; j0 < S; j0 += JC) {
+    double c[JC][8];
 #pragma unroll
-    for (int u = 0; u < RP; ++u) m[u] = (double)L.M[j * R + u];
-    double c[8];
+    for (int jj = 0; jj < JC; ++jj)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = 0.0;   // +0.0
+      for (int e = 0; e < 8; ++e) c[jj][e] = 0.0;   // +0.0
 #pragma unroll
     for (int u = 0; u < RP; ++u) {
-      if (EXACT || u < R) {
+      if (u < R) {
+        double xd[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) c[e] = fma(m[u], elem(u, e), c[e]);
+        for (int e = 0; e < 8; ++e) xd[e] = elem(u, e);
+#pragma unroll
+        for (int jj = 0; jj < JC; ++jj) {
+          const double m = (double)L.M[(j0 + jj) * R + u];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) c[jj][e] = fma(m, xd[e], c[jj][e]);
+        }
       }
     }
-    const int64_t row = (slot * S + j) * D + d0;
-    if (a.fmt == F32) {
-      if (live) {
-        float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(a.rows) + row);
-        p[0] = make_float4((float)c[0], (float)c[1], (float)c[2], (float)c[3]);
-        p[1] = make_float4((float)c[4], (float)c[5], (float)c[6], (float)c[7]);
-      }
-    } else if (a.fmt == BF16) {
-      uint32_t w[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        w[k] = (uint32_t)bf16_rne((float)c[2 * k]) | ((uint32_t)bf16_rne((float)c[2 * k + 1]) << 16);
-      if (live) *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.rows) + row) = make_uint4(w[0], w[1], w[2], w[3]);
-    } else {
-      double amax = 0.0;
+    for (int jj = 0; jj < JC; ++jj) {
+      const int j = j0 + jj;
+      if (j >= S) break;
+      const int64_t row = (slot * S + j) * D + d0;
+      if (a.fmt == F32) {
+        if (live) {
+          float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(a.rows) + row);
+          p[0] = make_float4((float)c[jj][0], (float)c[jj][1], (float)c[jj][2], (float)c[jj][3]);
+          p[1] = make_float4((float)c[jj][4], (float)c[jj][5], (float)c[jj][6], (float)c[jj][7]);
+        }
+      } else if (a.fmt == BF16) {
+        uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmax(amax, fabs(c[e]));
-      amax = group_max_f64<LPB>(amax);
-      const float s32 = (float)(amax / 127.0);
-      const double inv = s32 != 0.0f ? 1.0 / (double)s32 : 0.0;
-      uint32_t w[2] = {0u, 0u};
+        for (int k = 0; k < 4; ++k)
+          w[k] = (uint32_t)bf16_rne((float)c[jj][2 * k]) | ((uint32_t)bf16_rne((float)c[jj][2 * k + 1]) << 16);
+        if (live)
+          *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.rows) + row) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        double amax = 0.0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e / 4] |= (uint32_t)(uint8_t)quantise(c[e], s32, inv) << (8 * (e % 4));
-      if (live) {
-        *reinterpret_cast<uint2 *>(static_cast<int8_t *>(a.rows) + row) = make_uint2(w[0], w[1]);
-        if (lane % LPB == 0) a.scales[slot * S + j] = s32;
+        for (int e = 0; e < 8; ++e) amax = fmax(amax, fabs(c[jj][e]));
+        amax = group_max_f64<LPB>(amax);
+        const float s32 = (float)(amax / 127.0);
+        const double inv = s32 != 0.0f ? 1.0 / (double)s32 : 0.0;
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e / 4] |= quantise_byte(c[jj][e], s32, inv) << (8 * (e % 4));
+        if (live) {
+          *reinterpret_cast<uint2 *>(static_cast<int8_t *>(a.rows) + row) = make_uint2(w[0], w[1]);
+          if (lane % LPB == 0) a.scales[slot * S + j] = s32;
+        }
       }
     }
-    // The token words count as changed here, so their conversions stay
-    // inside the row loop instead of being hoisted as RP x 8 doubles.
+    // The token words count as changed here, so a second pass widens them
+    // again instead of the first pass hoisting RP x 8 doubles.
 #pragma unroll
     for (int u = 0; u < RP; ++u)
 #pragma unroll
@@ -441,31 +468,34 @@ int launch_append_epl(int SP, const AppendArgs &A, int64_t BH, hipStream_t strea
 
 }  // namespace
 
-template <int LPB, int RP>
+template <int LPB, int RP, int JC>
 int launch_encode_wide(const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
   constexpr int BPW = 64 / LPB;
   const int64_t block_waves = (BH * L.e.n_new + BPW - 1) / BPW;
   const int64_t waves = block_waves + (L.e.n_copy > 0 ? BH : 0);
   if (waves == 0) return 0;
   const dim3 grid((unsigned)((waves + kEncodeWaves - 1) / kEncodeWaves)), block(64 * kEncodeWaves);
-  const bool exact = L.e.R == RP;
-  if (L.e.raw == BF16) {
-    if (exact)
-      hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, BF16, true>), grid, block, 0, stream, L, BH, block_waves);
-    else
-      hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, BF16, false>), grid, block, 0, stream, L, BH, block_waves);
-  } else {
-    if (exact)
-      hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, F32, true>), grid, block, 0, stream, L, BH, block_waves);
-    else
-      hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, F32, false>), grid, block, 0, stream, L, BH, block_waves);
-  }
+  if (L.e.raw == BF16)
+    hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, JC, BF16>), grid, block, 0, stream, L, BH, block_waves);
+  else
+    hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, JC, F32>), grid, block, 0, stream, L, BH, block_waves);
   return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// Rows per pass: S itself up to 4 (no unused sums), else passes of 4.
+template <int LPB, int RP>
+int launch_encode_wide_j(const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
+  switch (L.e.S) {
+    case 1:
+    case 2: return launch_encode_wide<LPB, RP, 2>(L, BH, stream);
+    case 3: return launch_encode_wide<LPB, RP, 3>(L, BH, stream);
+    default: return launch_encode_wide<LPB, RP, 4>(L, BH, stream);
+  }
 }
 
 template <int LPB>
 int launch_encode_wide_r(const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
-  return L.e.R <= 8 ? launch_encode_wide<LPB, 8>(L, BH, stream) : launch_encode_wide<LPB, 16>(L, BH, stream);
+  return L.e.R <= 8 ? launch_encode_wide_j<LPB, 8>(L, BH, stream) : launch_encode_wide_j<LPB, 16>(L, BH, stream);
 }
 
 // Returns 0 on success, 1 on a HIP launch error, -1 if no kernel exists.
