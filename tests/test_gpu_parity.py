@@ -34,6 +34,8 @@ ENCODE_CASES = [
     (128, 5, 3, "i8", "bf16", 1, 1, 5 * 11 + 2),
     (64, 8, 8, "f32", "bf16", 1, 1, 8 * 6),
     (128, 8, 2, "i8", "bf16", 1, 1, 5),        # tail only
+    (128, 16, 16, "i8", "bf16", 1, 2, 16 * 9 + 3),   # four passes of four rows
+    (256, 16, 5, "bf16", "bf16", 2, 1, 16 * 7),      # a second pass with one row
 ]
 
 
@@ -46,6 +48,22 @@ def test_encode_bitexact(D, R, S, fmt, raw, B, H, T):
     st.encode(k.to(DEV))
     torch.cuda.synchronize()
     assert (st.n_blocks, st.n_tail) == (T // R, T % R)
+    assert_archive_equal(gpu_archive(st), O.encode(syn.bf16_to_numpy(k), R, S, fmt))
+
+
+@pytest.mark.parametrize("D,R,S,fmt,T1,T2", [(128, 8, 3, "i8", 8 * 21, 8 * 13 + 6), (64, 16, 4, "bf16", 16 * 5, 16 * 2)])
+def test_encode_two_calls(D, R, S, fmt, T1, T2):
+    # the second call archives into slots after the first call's blocks, from
+    # a view that starts T1 tokens into the tensor
+    note("encode two calls", D, R, S, fmt, T1, T2)
+    B, H = 2, 3
+    k, _, _ = syn.small_case(B, H, H, D, T1 + T2, seed=D + R + S, dtype=torch.bfloat16, offset_var=2.0)
+    kd = k.to(DEV)
+    st = bd.CodecStream(B, H, D, R, S, fmt=fmt, device=DEV)
+    st.encode(kd[:, :, :T1])
+    st.encode(kd[:, :, T1:])
+    torch.cuda.synchronize()
+    assert (st.n_blocks, st.n_tail) == ((T1 + T2) // R, (T1 + T2) % R)
     assert_archive_equal(gpu_archive(st), O.encode(syn.bf16_to_numpy(k), R, S, fmt))
 
 
