@@ -381,7 +381,9 @@ int codec_encode_blocks(codec_stream *s, const void *x, const int64_t x_stride[3
   L.e.n_copy = t;
   fill_M(s->fmt, (int)R, s->keep, L.M);
   (void)hipGetLastError();
-  if (launch_encode(s->head_dim, L, s->batch * s->heads, stream) != 0) return CODEC_ERR_HIP;
+  rc = launch_encode(s->head_dim, L, s->batch * s->heads, stream);
+  if (rc < 0) return CODEC_ERR_UNSUPPORTED;   // grid beyond 2^31 - 1 workgroups
+  if (rc > 0) return CODEC_ERR_HIP;
   s->n_blocks += n_new;
   s->n_tail = t;
   return CODEC_OK;

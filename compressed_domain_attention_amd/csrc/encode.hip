@@ -442,6 +442,7 @@ int launch_encode_epl(int SP, const EncodeLaunch &L, int64_t BH, hipStream_t str
   const int64_t units = L.e.n_new + (L.e.n_copy > 0 ? 1 : 0);
   if (units == 0) return 0;
   const int64_t per_bh = (units + kEncodeWaves - 1) / kEncodeWaves;
+  if (per_bh * BH > 0x7FFFFFFF) return -1;
   const dim3 grid((unsigned)(per_bh * BH)), block(64 * kEncodeWaves);
   switch (SP) {
     case 2: hipLaunchKernelGGL((encode_kernel<EPL, 2>), grid, block, 0, stream, L, per_bh); break;
@@ -474,6 +475,7 @@ int launch_encode_wide(const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
   const int64_t block_waves = (BH * L.e.n_new + BPW - 1) / BPW;
   const int64_t waves = block_waves + (L.e.n_copy > 0 ? BH : 0);
   if (waves == 0) return 0;
+  if ((waves + kEncodeWaves - 1) / kEncodeWaves > 0x7FFFFFFF) return -1;
   const dim3 grid((unsigned)((waves + kEncodeWaves - 1) / kEncodeWaves)), block(64 * kEncodeWaves);
   if (L.e.raw == BF16)
     hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, JC, BF16>), grid, block, 0, stream, L, BH, block_waves);

@@ -136,7 +136,9 @@ int codec_basis(int32_t R, int32_t S, float *A_host);
  *   x        device, (B, H, T, D) elements of s->raw_dtype.
  *   x_stride element strides of the b, h and t axes (d stride is 1).
  *   T        tokens, >= 0 (T == 0 is a no-op).
- * Errors: NULL, SHAPE, FORMAT, STATE (tail not empty), CAPACITY, HIP.
+ * Errors: NULL, SHAPE, FORMAT, STATE (tail not empty), CAPACITY,
+ * UNSUPPORTED (a launch of more than 2^31 - 1 workgroups: about 2^33 blocks
+ * over all (b, h)), HIP.
  */
 int codec_encode_blocks(codec_stream *s, const void *x, const int64_t x_stride[3],
                         int64_t T, hipStream_t stream);
