@@ -55,7 +55,7 @@ def _lib():
         path = library_path()
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build the HIP library first "
-                               "(python -c 'import __graft_entry__ as g; g.build()')")
+                               "(python -m compressed_domain_attention_amd.build)")
         lib = ctypes.CDLL(path)
         P = ctypes.POINTER(_Stream)
         vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
