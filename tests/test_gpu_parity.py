@@ -36,6 +36,8 @@ ENCODE_CASES = [
     (128, 8, 2, "i8", "bf16", 1, 1, 5),        # tail only
     (128, 16, 16, "i8", "bf16", 1, 2, 16 * 9 + 3),   # four passes of four rows
     (256, 16, 5, "bf16", "bf16", 2, 1, 16 * 7),      # a second pass with one row
+    (128, 16, 4, "i8", "f32", 1, 2, 16 * 7 + 9),      # fp32 tokens, sixteen-token blocks
+    (256, 12, 3, "bf16", "f32", 1, 1, 12 * 5 + 1),    # fp32 tokens, R = 12, three rows per pass
 ]
 
 
