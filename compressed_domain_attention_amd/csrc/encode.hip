@@ -134,8 +134,11 @@ __device__ inline int8_t quantise(double c, float s32, double inv) {
   double y = c * inv;
   double r = rint(y);
   if (fabs(y - floor(y) - 0.5) < 1e-9) r = rint(c / (double)s32);
-  r = fmin(fmax(r, -127.0), 127.0);
-  return (int8_t)(int)r;
+  // clamp to [-127, 127]: the lower bound in fp64 (a NaN becomes -127), after
+  // which r is finite and at most 128 (|c| <= 127 scale up to rounding), so
+  // the upper bound is taken on the integer
+  r = fmax(r, -127.0);
+  return (int8_t)min((int)r, 127);
 }
 
 // Encode block `n` (call-relative) of stream row (b, h) into archive slot
@@ -288,17 +291,6 @@ __device__ inline double group_max_f64(double v) {
   return __builtin_bit_cast(double, u);
 }
 
-// quantise() with the clamp taken on the integer (the same code: |rint(y)|
-// stays far inside the int range), as a byte.
-__device__ inline uint32_t quantise_byte(double c, float s32, double inv) {
-  if (s32 == 0.0f) return 0u;
-  const double y = c * inv;
-  double r = rint(y);
-  if (fabs(y - floor(y) - 0.5) < 1e-9) r = rint(c / (double)s32);
-  const int q = min(max((int)r, -127), 127);
-  return (uint32_t)q & 0xFFu;
-}
-
 // Bulk encode with wide lanes: a lane owns eight consecutive head_dim
 // elements of one block (16-byte token loads), LPB = D/8 lanes per block and
 // 64/LPB blocks per wave, blocks numbered across (b, h) rows.  All RP (>= R)
@@ -401,7 +393,7 @@ __global__ __launch_bounds__(64 * kEncodeWaves) __attribute__((amdgpu_waves_per_
         const double inv = s32 != 0.0f ? 1.0 / (double)s32 : 0.0;
         uint32_t w[2] = {0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e / 4] |= quantise_byte(c[jj][e], s32, inv) << (8 * (e % 4));
+        for (int e = 0; e < 8; ++e) w[e / 4] |= (uint32_t)(uint8_t)quantise(c[jj][e], s32, inv) << (8 * (e % 4));
         if (live) {
           *reinterpret_cast<uint2 *>(static_cast<int8_t *>(a.rows) + row) = make_uint2(w[0], w[1]);
           if (lane % LPB == 0) a.scales[slot * S + j] = s32;
