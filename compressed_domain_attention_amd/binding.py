@@ -298,13 +298,29 @@ def decode_workspace_bytes(k, v, Hq):
 _WS_CACHE = {}
 
 
-def _workspace(nbytes, device):
-    """A zero-filled workspace per device, grown on demand and then reused
-    (the kernels leave its counters at zero after every call)."""
-    key = (device.type, device.index)
+def _torch_stream(device, stream):
+    """The torch stream object for a raw HIP stream handle (None: the
+    current stream of `device`)."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _workspace(nbytes, device, ts):
+    """A zero-filled decode workspace for one (device, HIP stream), grown on
+    demand and then reused: the kernels leave its arrival counters at zero
+    after every call, so calls in order on one stream can share it.  The
+    zero fill is enqueued on that stream, ahead of the kernel that first
+    uses it, and the buffer belongs to that stream in torch's allocator, so a
+    replaced buffer is not handed out again before the stream has passed
+    the work already enqueued on it.  Calls on different streams get
+    different workspaces (overlapping calls must not share arrival
+    counters)."""
+    key = (device.type, device.index, ts.cuda_stream)
     ws = _WS_CACHE.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(ts):
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS_CACHE[key] = ws
     return ws
 
@@ -325,9 +341,10 @@ def decode_attention(q, k, v, scale=None, out=None, out_dtype=torch.float32, wor
     odt = {torch.float32: FMT_F32, torch.bfloat16: FMT_BF16}[out.dtype]
     dk, dv = k._desc(), v._desc()
     need = decode_workspace_bytes(k, v, Hq)
+    ts = _torch_stream(q.device, stream)
     if workspace is None:
-        workspace = _workspace(need, q.device)
-    st = _hip_stream(q.device) if stream is None else ctypes.c_void_p(stream)
+        workspace = _workspace(need, q.device, ts)
+    st = ctypes.c_void_p(ts.cuda_stream)
     _check(_lib().codec_decode_attention(
         ctypes.c_void_p(q.data_ptr()), _I64_2(q.stride(0), q.stride(1)), Hq,
         ctypes.byref(dk), ctypes.byref(dv), ctypes.c_float(float(scale)),
@@ -357,6 +374,7 @@ def decode_attention_append(q, k, v, k_new, v_new, scale=None, out=None, out_dty
         k._grow(k.n_blocks + 1)
         v._grow(v.n_blocks + 1)
     dk, dv = k._desc(), v._desc()
+    ts = _torch_stream(q.device, stream)
     if workspace is None:
         # sized for the streams as the append leaves them (the split plan
         # depends on the block count only)
@@ -367,8 +385,8 @@ def decode_attention_append(q, k, v, k_new, v_new, scale=None, out=None, out_dty
         n = ctypes.c_size_t(0)
         _check(_lib().codec_decode_workspace_bytes(ctypes.byref(dk2), ctypes.byref(dv2), int(Hq), ctypes.byref(n)),
                "codec_decode_workspace_bytes")
-        workspace = _workspace(int(n.value), q.device)
-    st = _hip_stream(q.device) if stream is None else ctypes.c_void_p(stream)
+        workspace = _workspace(int(n.value), q.device, ts)
+    st = ctypes.c_void_p(ts.cuda_stream)
     _check(_lib().codec_decode_attention_append(
         ctypes.c_void_p(q.data_ptr()), _I64_2(q.stride(0), q.stride(1)), Hq,
         ctypes.byref(dk), ctypes.byref(dv),

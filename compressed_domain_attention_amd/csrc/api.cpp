@@ -440,11 +440,21 @@ int codec_decode_attention_append(const void *q, const int64_t q_stride[2], int6
                          workspace_bytes, &p);
   if (rc) return rc;
   if (complete) {
-    // the token completes a block: archive it, then attend
+    // the token completes a block: archive it, then attend.  If the decode
+    // launch fails, the counters go back to their values before the call:
+    // the archive launch wrote only slot n_blocks (spare capacity under the
+    // restored counters) and left tail slots 0..R-2 as they were, so the
+    // restored stream is the one the caller passed in.
+    const codec_stream k0 = *k, v0 = *v;
     rc = launch_append_step(k, v, k_new, kn_stride, v_new, vn_stride, stream);
     if (rc) return rc;
-    return launch_decode_call(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, workspace, p, nullptr,
-                              nullptr, nullptr, nullptr, stream);
+    rc = launch_decode_call(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, workspace, p, nullptr,
+                            nullptr, nullptr, nullptr, stream);
+    if (rc) {
+      *k = k0;
+      *v = v0;
+    }
+    return rc;
   }
   rc = launch_decode_call(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, workspace, p, k_new,
                           kn_stride, v_new, vn_stride, stream);

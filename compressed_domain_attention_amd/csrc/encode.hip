@@ -19,7 +19,8 @@
 // The quotient c / scale is evaluated as c * (1 / scale); within 1e-9 of a
 // half-integer it is recomputed with an IEEE fp64 division.  The product
 // differs from the correctly rounded quotient by < 6e-14 for |c/scale| <=
-// 128, so both round to the same integer everywhere outside that band.
+// 192 (the largest quotient, reached when a / 127 rounds to an fp32
+// subnormal), so both round to the same integer everywhere outside that band.
 //
 // The encode is streaming work (S fp64 FMAs per input element): plain fp64
 // VALU, one wave per block, lanes along head_dim.  MFMA is not used because
@@ -134,9 +135,12 @@ __device__ inline int8_t quantise(double c, float s32, double inv) {
   double y = c * inv;
   double r = rint(y);
   if (fabs(y - floor(y) - 0.5) < 1e-9) r = rint(c / (double)s32);
-  // clamp to [-127, 127]: the lower bound in fp64 (a NaN becomes -127), after
-  // which r is finite and at most 128 (|c| <= 127 scale up to rounding), so
-  // the upper bound is taken on the integer
+  // clamp to [-127, 127]: the lower bound in fp64, the upper bound on the
+  // integer.  For finite c, |c / scale| is at most 127 up to the rounding of
+  // the scale, i.e. about 127 * 1.5 ~ 190 when a / 127 is an fp32 subnormal,
+  // which fits an int.  Non-finite input has no defined codes (the contract
+  // covers finite tokens): fmax keeps r from being NaN so the conversion
+  // stays defined.
   r = fmax(r, -127.0);
   return (int8_t)min((int)r, 127);
 }

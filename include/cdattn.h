@@ -212,7 +212,11 @@ int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
  * Arguments as in the two calls; the workspace must satisfy
  * codec_decode_workspace_bytes for the streams as the append leaves them.
  * Errors: those of both calls, all checked before any launch; counters
- * change only on success.
+ * change only on success.  One exception to "an error enqueues nothing":
+ * when the token completes a block and the decode launch itself fails
+ * (CODEC_ERR_HIP) after the archive launch was enqueued, that launch has
+ * written archive slot n_blocks; the counters are restored, so the slot is
+ * spare capacity again and the stream holds what it held before the call.
  */
 int codec_decode_attention_append(const void *q, const int64_t q_stride[2], int64_t Hq, codec_stream *k,
                                   codec_stream *v, const void *k_new, const int64_t kn_stride[2],

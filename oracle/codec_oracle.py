@@ -151,7 +151,7 @@ def project_blocks(x, R, S, fmt=F32):
         C[..., n, j, :] = sum_{i<R} M32[j, i] * x[..., n*R + i, :]
     summed left to right from +0.0 (reading 3).  README "Math": C = M X
     block by block along the sequence axis.  PNG mode uses the difference
-    matrix instead of M32 (reading 16).
+    matrix instead of M32 (reading 10).
     """
     x = np.asarray(x, dtype=np.float64)
     T, D = x.shape[-2], x.shape[-1]
@@ -402,6 +402,81 @@ def _head(archive, b, h):
     out["rows"] = archive["rows"][b, h]
     out["scales"] = None if archive["scales"] is None else archive["scales"][b, h]
     out["tail"] = archive["tail"][b, h]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# the pages' coefficient-domain algorithm, split over block ranges
+# ---------------------------------------------------------------------------
+def decode_attention_split(q, k_archive, v_archive, scale=None, ns=1):
+    """Decode attention computed the way the pages compute it, in fp64.
+
+    README "Materialization-free decode attention" and triton_attention.py:
+    the blocks of each (b, kv head) are cut into ns consecutive ranges of
+    chunk = ceil(n / ns) blocks (the split kernel's grid); within a range,
+    block by block, s = rows . q (rows dequantised, reading 6), the R
+    logits z = scale * A s (A = the synthesis matrix), an online-softmax
+    update of the running (max m, sum l, accumulator acc) with
+    alpha = exp(m_old - m_new), the weights w = p A and acc += w . rows;
+    the last range also takes the raw tail tokens one by one.  A combine then
+    merges the ranges (the combine kernel): M = max m_i over ranges with
+    l_i > 0, L = sum l_i exp(m_i - M), out = sum acc_i exp(m_i - M) / L.
+    Ranges left empty (ns > n) contribute nothing.  Nothing is ever
+    reconstructed, so agreement with ``decode_attention`` (which
+    materialises) is the identity the README states.
+    q: (B, Hq, D) or (B, Hq, 1, D).  Returns (B, Hq, D).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    if q.ndim == 4:
+        q = q[:, :, 0, :]
+    B, Hq, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    R, fmt = k_archive["R"], k_archive["fmt"]
+    S = k_archive["S"]
+    A = synthesis(R, S, fmt)                                   # R x S
+    Kc = dequantize(k_archive["rows"], k_archive["scales"], k_archive["fmt"])
+    Vc = dequantize(v_archive["rows"], v_archive["scales"], v_archive["fmt"])
+    Kt = np.asarray(k_archive["tail"], dtype=np.float64)
+    Vt = np.asarray(v_archive["tail"], dtype=np.float64)
+    Hkv = Kc.shape[1]
+    G = Hq // Hkv
+    n = k_archive["n_blocks"]
+    if n + Kt.shape[-2] == 0:
+        raise ValueError("nothing to attend: T = 0")
+    chunk = -(-n // ns) if n else 0
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // G
+            qv = q[b, hq]
+            parts = []
+            for sid in range(ns):
+                m, l, acc = -np.inf, 0.0, np.zeros(D)
+
+                def update(z, w_of_p, rows):
+                    nonlocal m, l, acc
+                    m_new = max(m, float(z.max()))
+                    alpha = math.exp(m - m_new) if m > -np.inf else 0.0
+                    p = np.exp(z - m_new)
+                    l = l * alpha + p.sum()
+                    acc = acc * alpha + w_of_p(p) @ rows
+                    m = m_new
+
+                lo, hi = sid * chunk, min((sid + 1) * chunk, n)
+                for blk in range(lo, hi):
+                    sj = Kc[b, h, blk] @ qv                      # (S,)
+                    z = scale * (A @ sj)                         # (R,)
+                    update(z, lambda p: p @ A, Vc[b, h, blk])    # w = p A (S,)
+                if sid == ns - 1:
+                    for t in range(Kt.shape[-2]):
+                        z = np.array([scale * (Kt[b, h, t] @ qv)])
+                        update(z, lambda p: p, Vt[b, h, t:t + 1])
+                parts.append((m, l, acc))
+            live = [(m, l, a) for (m, l, a) in parts if l > 0.0]
+            M = max(m for (m, _, _) in live)
+            L = sum(l * math.exp(m - M) for (m, l, _) in live)
+            out[b, hq] = sum(a * math.exp(m - M) for (m, _, a) in live) / L
     return out
 
 

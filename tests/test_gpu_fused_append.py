@@ -24,6 +24,9 @@ DEV = "cuda"
     ("f32", "f32", 4, 2, 1, 4, 1, 256, 4 * 9 + 1),
     ("png", "bf16", 8, 8, 1, 8, 2, 128, 8 * 11 + 5),
     ("i8", "bf16", 8, 2, 1, 4, 1, 128, 3),               # tail only at start
+    # the benchmark's 128K-context constants (GQA 4, R = 16, S = 4, int8 keys
+    # and values, five tail tokens at the start) on a shorter sequence
+    ("i8", "bf16", 16, 4, 1, 32, 8, 128, 16 * 600 + 5),
 ])
 def test_fused_equals_two_calls(fmt, raw, R, S, B, Hq, H, D, T0):
     note("fused append", fmt, raw, R, S, B, Hq, H, D, T0)

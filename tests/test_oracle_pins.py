@@ -44,6 +44,73 @@ def test_basis_closed_forms():
         np.testing.assert_allclose(O.dct_basis_f64(R, 1)[0], np.full(R, 1 / math.sqrt(R)), rtol=0, atol=2.3e-16)
 
 
+def _f32_rne_bits(x):
+    """fp32 bit pattern of a positive exact value (decimal.Decimal), rounded
+    to nearest with ties to even, by integer arithmetic on the scaled value."""
+    from decimal import Decimal
+    e = 0
+    while x >= 2:
+        x, e = x / 2, e + 1
+    while x < 1:
+        x, e = x * 2, e - 1
+    scaled = x * (Decimal(2) ** 23)
+    fl = int(scaled)
+    frac = scaled - fl
+    mant = fl + (1 if frac > Decimal("0.5") or (frac == Decimal("0.5") and fl % 2) else 0)
+    if mant == 1 << 24:
+        mant, e = mant >> 1, e + 1
+    return ((e + 127) << 23) | (mant - (1 << 23))
+
+
+def test_basis_f32_rounding_by_hand():
+    # Reading 2: the codec's basis is the fp64 basis rounded to nearest fp32.
+    # At R = 4, frequency 1, the exact entries are sqrt(1/2) cos(pi/8) =
+    # sqrt((2 + sqrt 2) / 8) = 0.6532814824381882639... and sqrt(1/2)
+    # cos(3 pi/8) = sqrt((2 - sqrt 2) / 8) = 0.2705980500730984921...; their
+    # nearest fp32 values are 0x3f273d75 and 0x3e8a8bd4, while truncation
+    # gives 0x3f273d74 and 0x3e8a8bd3, so a chopped or otherwise misrounded
+    # basis fails here (R = 2's 1/sqrt 2 rounds the same both ways).
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    r2 = Decimal(2).sqrt()
+    exact = [((2 + r2) / 8).sqrt(), ((2 - r2) / 8).sqrt()]
+    assert [_f32_rne_bits(x) for x in exact] == [0x3F273D75, 0x3E8A8BD4]
+    got = O.dct_basis_f32(4, 2)[1].view(np.uint32).tolist()
+    assert got == [0x3F273D75, 0x3E8A8BD4, 0xBE8A8BD4, 0xBF273D75]
+    # every entry of the R = 8 and R = 16 bases against the exact value from
+    # fifty-digit arithmetic, rounded by hand (cos from its Taylor series)
+    def cos_dec(xn, xd):
+        # cos(pi * xn / xd) in Decimal: pi from Machin's formula
+        def arctan_inv(k):
+            t, s, n, sign = Decimal(1) / k, Decimal(0), 1, 1
+            pw = Decimal(1) / k
+            while True:
+                term = pw / n
+                if term < Decimal(10) ** -58:
+                    return s + sign * term
+                s += sign * term
+                pw /= k * k
+                n += 2
+                sign = -sign
+        pi = 16 * arctan_inv(5) - 4 * arctan_inv(239)
+        x = pi * xn / xd
+        tot, term, k = Decimal(1), Decimal(1), 0
+        while abs(term) > Decimal(10) ** -58:
+            term = -term * x * x / ((2 * k + 1) * (2 * k + 2))
+            tot += term
+            k += 1
+        return tot
+    for R in (8, 16):
+        M = O.dct_basis_f32(R, R)
+        for j in range(R):
+            cj = (Decimal(1) / R).sqrt() if j == 0 else (Decimal(2) / R).sqrt()
+            for i in range(R):
+                v = cj * cos_dec((2 * i + 1) * j, 2 * R)
+                bits = _f32_rne_bits(abs(v)) if v != 0 else 0
+                want = bits | (0x80000000 if v < 0 else 0)
+                assert int(M[j, i].view(np.uint32)) == want, (R, j, i)
+
+
 @pytest.mark.parametrize("R,S", [(2, 1), (3, 2), (8, 2), (8, 8), (12, 5), (16, 4)])
 def test_projection_equals_scipy_dct(R, S):
     # The lowest S outputs of the orthonormal DCT-II of each block.
@@ -142,6 +209,77 @@ def test_quantiser_invariants():
     assert (err <= s.astype(np.float64)[..., None] / 2 * (1 + 2.0 ** -40)).all()
 
 
+def test_dequantize_int8_within_half_a_step():
+    # Reading 6 through O.dequantize: each code times ITS OWN row's scale is
+    # within half a quantisation step of the coefficient.  Rows of one block
+    # and of neighbouring blocks differ in magnitude by up to 10^6, so a scale
+    # taken from the wrong row, block or axis misses by orders of magnitude.
+    rng = np.random.default_rng(8)
+    mag = 10.0 ** rng.uniform(-3, 3, size=(2, 3, 9, 5, 1))
+    C = rng.standard_normal((2, 3, 9, 5, 48)) * mag
+    codes, s = O.quantize_rows(C)
+    got = O.dequantize(codes, s, O.I8)
+    assert got.shape == C.shape
+    half = s.astype(np.float64)[..., None] / 2
+    assert (np.abs(got - C) <= half * (1 + 2.0 ** -40)).all()
+    # and the steps really are per row: every row's error is at most its
+    # own half step although the steps differ by up to 10^6 between rows
+    assert s.max() / s.min() > 1e3
+
+
+def _int8_token_error_bound(X, R):
+    """Bound on |x_hat - x| per token for an int8 archive keeping all S = R
+    frequencies, from scipy's orthonormal DCT (independent of the oracle):
+    x_hat - x = M32^T e + (M32^T M32 - I) x with |e_j| <= s_j / 2, s_j the
+    row scale max_d |c_j| / 127 (fp32 rounding: the factor 1 + 2^-20);
+    the second term is below 8 R 2^-24 max |x| of the block.  Tail tokens
+    are exact.  Returns (..., T) bounds."""
+    T, D = X.shape[-2], X.shape[-1]
+    n = T // R
+    blocks = X[..., :n * R, :].reshape(*X.shape[:-2], n, R, D)
+    C = scipy.fft.dct(blocks, type=2, norm="ortho", axis=-2)
+    s = np.abs(C).max(axis=-1) / 127 * (1 + 2.0 ** -20)
+    Mabs = np.abs(scipy.fft.dct(np.eye(R), type=2, norm="ortho", axis=0))   # |M[j, i]|
+    b = np.einsum("ji,...nj->...ni", Mabs, s / 2) + 8 * R * 2.0 ** -24 * np.abs(blocks).max(axis=(-1, -2))[..., None]
+    return np.concatenate([b.reshape(*X.shape[:-2], n * R), np.zeros((*X.shape[:-2], T - n * R))], axis=-1)
+
+
+@pytest.mark.parametrize("R", [4, 8, 16])
+def test_int8_all_frequencies_reconstruction_bound(R):
+    # README "Math" (K = r is lossless) with int8 rows: the reconstruction
+    # differs from the tokens only by the quantisation, within the bound above.
+    k, _, _ = syn.small_case(2, 2, 2, 24, 12 * R + 3, seed=R + 60)
+    K = syn.bf16_to_numpy(k)
+    got = O.materialise(O.encode(K, R, R, O.I8))
+    bound = _int8_token_error_bound(K, R)
+    assert (np.abs(got - K) <= bound[..., None]).all()
+    assert np.abs(got - K).max() > 0       # the bound is not vacuous: quantisation is visible
+
+
+@pytest.mark.parametrize("R,D", [(8, 16), (4, 16), (16, 16)])
+def test_int8_all_frequencies_attention_bound(R, D):
+    # An int8 archive with all frequencies against textbook attention on the
+    # raw tokens (torch SDPA, fp64).  Per token, |dk|, |dv| are bounded as in
+    # the previous pin; then |dz_t| <= scale sum_d |q_d| |dk_t| <= delta, the
+    # softmax weights move by a factor within exp(+-2 delta), so
+    #   |out' - out|_inf <= max_t |dv_t| + (exp(2 delta) - 1) * max_d (max_t v - min_t v) / 2
+    # (the weights of both sums total 1, so v may be centred).  The softmax
+    # scale 0.02 keeps delta small enough for the bound to be tight.
+    scale = 0.02
+    k, v, q = syn.small_case(1, 2, 1, D, 12 * R + 3, seed=77)
+    K, V, qn = (syn.bf16_to_numpy(t) for t in (k, v, q))
+    got = O.decode_attention(qn, O.encode(K, R, R, O.I8), O.encode(V, R, R, O.I8), scale)
+    ref = _sdpa_ref(qn[:, :, 0], K, V, scale)
+    bK, bV = _int8_token_error_bound(K, R), _int8_token_error_bound(V, R)
+    for hq in range(2):
+        delta = (scale * np.abs(qn[0, hq, 0]).sum() * bK[0, 0]).max()
+        centre = ((V[0, 0].max(axis=0) - V[0, 0].min(axis=0)) / 2).max()
+        bound = bV[0, 0].max() + (math.exp(2 * delta) - 1) * centre
+        err = np.abs(got[0, hq] - ref[0, hq]).max()
+        assert err <= bound, (hq, err, bound)
+        assert bound < 0.1 * np.abs(V).max()
+
+
 def test_bf16_rounding_matches_torch():
     rng = np.random.default_rng(6)
     v = (rng.standard_normal(10000) * 10.0 ** rng.uniform(-30, 30, 10000)).astype(np.float32)
@@ -232,6 +370,42 @@ def test_coefficient_domain_identity():
         out[0, hq] = acc / p.sum()
     got = O.decode_attention(qn, ka, va, scale)
     np.testing.assert_allclose(got, out, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kfmt,vfmt,T", [(O.I8, O.I8, 8 * 9 + 5), (O.I8, O.BF16, 8 * 12), (O.F32, O.I8, 8 * 3 + 7),
+                                         (O.PNG, O.PNG, 8 * 5 + 2)])
+def test_split_combine_equals_materialised(kfmt, vfmt, T):
+    # README "Materialization-free decode attention": attending in the
+    # coefficient domain (never building K or V) equals attending to the
+    # reconstruction; triton_attention.py's split over block ranges and its
+    # (max, sum, acc) combine leave the result unchanged for any split count,
+    # including splits that hold no block (ns > n) and the raw tail.
+    R = 8
+    S = R if kfmt == O.PNG else 3
+    k, v, q = syn.small_case(2, 6, 2, 16, T, seed=T)
+    K, V, qn = (syn.bf16_to_numpy(t) for t in (k, v, q))
+    ka, va = O.encode(K, R, S, kfmt), O.encode(V, R, S, vfmt)
+    ref = O.decode_attention(qn, ka, va, 0.3)
+    n = T // R
+    for ns in (1, 2, 3, n, n + 4):
+        np.testing.assert_allclose(O.decode_attention_split(qn, ka, va, 0.3, ns), ref, rtol=0, atol=1e-12)
+
+
+def test_split_combine_tail_only_and_by_hand():
+    # no complete block: the last (only non-empty) split holds the tail
+    k, v, q = syn.small_case(1, 2, 1, 16, 5, seed=3)
+    K, V, qn = (syn.bf16_to_numpy(t) for t in (k, v, q))
+    ka, va = O.encode(K, 8, 2, O.I8), O.encode(V, 8, 2, O.I8)
+    for ns in (1, 4):
+        np.testing.assert_allclose(O.decode_attention_split(qn, ka, va, None, ns), _sdpa_ref(qn[:, :, 0], K, V, 0.25),
+                                   rtol=0, atol=1e-12)
+    # R = S = 1 identity codec, three tokens, two splits of one block and a
+    # tail: logits 0, 1, 2 (q = 1, keys 0, 1, 2), values 1, 0, 0 -> 1 / (1 + e + e^2)
+    e = math.e
+    arch = lambda x: dict(fmt=O.F32, R=1, S=1, rows=np.array(x[:2], dtype=np.float32).reshape(1, 1, 2, 1, 1),
+                          scales=None, tail=np.array(x[2:], dtype=np.float64).reshape(1, 1, 1, 1), n_blocks=2)
+    got = O.decode_attention_split(np.ones((1, 1, 1)), arch([0.0, 1.0, 2.0]), arch([1.0, 0.0, 0.0]), 1.0, 2)
+    assert abs(got[0, 0, 0] - 1 / (1 + e + e * e)) <= 1e-15
 
 
 def test_identity_codec_equals_plain_attention():
