@@ -68,6 +68,7 @@ def _lib():
                                                vp, ctypes.c_size_t, vp]
         lib.codec_decode_attention_append.argtypes = [vp, LP, i64, P, P, vp, LP, vp, LP, f32, vp, LP, i32,
                                                       vp, ctypes.c_size_t, vp]
+        lib.codec_decode_attention_noalloc.argtypes = [vp, LP, i64, P, P, f32, vp, LP, i32, vp]
         lib.codec_materialise.argtypes = [P, i64, vp, LP, i32, vp]
         lib.codec_crop.argtypes = [P, i64, vp]
         lib.codec_select_batch.argtypes = [P, P, LP, i64, vp]
@@ -75,7 +76,8 @@ def _lib():
         lib.codec_status_string.restype = ctypes.c_char_p
         for name in ("codec_basis", "codec_encode_blocks", "codec_append_step",
                      "codec_decode_workspace_bytes", "codec_decode_attention",
-                     "codec_materialise", "codec_crop", "codec_select_batch", "codec_decode_attention_append"):
+                     "codec_materialise", "codec_crop", "codec_select_batch", "codec_decode_attention_append",
+                     "codec_decode_attention_noalloc"):
             getattr(lib, name).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -351,6 +353,29 @@ def decode_attention(q, k, v, scale=None, out=None, out_dtype=torch.float32, wor
         ctypes.c_void_p(out.data_ptr()), _I64_2(out.stride(0), out.stride(1)), odt,
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), st),
         "codec_decode_attention")
+    return out
+
+
+def decode_attention_noalloc(q, k, v, scale=None, out=None, out_dtype=torch.float32, stream=None):
+    """decode_attention without a workspace (codec_decode_attention_noalloc):
+    the split partials live in the library's own per-GPU scratch array, so
+    the call allocates nothing when `out` is given.  Calls that overlap on one
+    GPU race on that array."""
+    if q.dtype != torch.bfloat16 or q.dim() != 4 or q.shape[2] != 1 or q.stride(3) != 1:
+        raise ValueError("q must be (B, Hq, 1, D) bf16 with unit d stride")
+    B, Hq, _, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, 1, D), dtype=out_dtype, device=q.device)
+    odt = {torch.float32: FMT_F32, torch.bfloat16: FMT_BF16}[out.dtype]
+    dk, dv = k._desc(), v._desc()
+    st = ctypes.c_void_p(_torch_stream(q.device, stream).cuda_stream)
+    _check(_lib().codec_decode_attention_noalloc(
+        ctypes.c_void_p(q.data_ptr()), _I64_2(q.stride(0), q.stride(1)), Hq,
+        ctypes.byref(dk), ctypes.byref(dv), ctypes.c_float(float(scale)),
+        ctypes.c_void_p(out.data_ptr()), _I64_2(out.stride(0), out.stride(1)), odt, st),
+        "codec_decode_attention_noalloc")
     return out
 
 

@@ -85,22 +85,13 @@ EncodeArgs stream_encode_args(const codec_stream *s) {
   return e;
 }
 
-// Split plan of the decode: splits per (b, kv head, query group), blocks per
-// split, workgroups.  A pure function of the shapes.
-struct Plan {
-  bool ok;
-  int GS, NQG, SP, ns;
-  int64_t pairs, chunk, n_wg;
-  size_t off_ml, off_acc, bytes;
-};
-
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workgroups that fill MI355X once: 256 CUs x 1 resident 8-wave workgroup.
 constexpr int64_t kTargetWorkgroups = 256;
 
-Plan make_plan(const codec_stream *k, const codec_stream *v, int64_t Hq) {
-  Plan p;
+DecodePlan make_plan(const codec_stream *k, const codec_stream *v, int64_t Hq) {
+  DecodePlan p;
   const int64_t G = Hq / k->heads;
   p.GS = decode_group_size((int)G);
   p.NQG = (int)(G / p.GS);
@@ -244,10 +235,14 @@ int launch_append_step(codec_stream *k, codec_stream *v, const void *k_new, cons
   return CODEC_OK;
 }
 
-// Validation of codec_decode_attention (no HIP call); fills the plan.
-int check_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
+}  // namespace
+
+namespace cdattn {
+// Validation of a decode call apart from its workspace (no HIP call); fills
+// the plan.
+int decode_check_args(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
                       const codec_stream *v, float scale, const void *out, const int64_t out_stride[2],
-                      int32_t out_dtype, const void *workspace, size_t workspace_bytes, Plan *p) {
+                      int32_t out_dtype, DecodePlan *p) {
   if (!q || !q_stride || !out || !out_stride) return CODEC_ERR_NULL;
   int rc = check_decode(k, v, Hq);
   if (rc) return rc;
@@ -258,16 +253,29 @@ int check_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, cons
   if (out_stride[0] < 0 || out_stride[1] < 0) return CODEC_ERR_SHAPE;
   *p = make_plan(k, v, Hq);
   if (!p->ok) return CODEC_ERR_UNSUPPORTED;
+  return CODEC_OK;
+}
+}  // namespace cdattn
+
+namespace {
+// Validation of codec_decode_attention (no HIP call); fills the plan.
+int check_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
+                      const codec_stream *v, float scale, const void *out, const int64_t out_stride[2],
+                      int32_t out_dtype, const void *workspace, size_t workspace_bytes, DecodePlan *p) {
+  const int rc = decode_check_args(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, p);
+  if (rc) return rc;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < p->bytes)
     return CODEC_ERR_WORKSPACE;
   return CODEC_OK;
 }
+}  // namespace
 
+namespace cdattn {
 // The decode launch for validated arguments.  fuse_k / fuse_v (non-null)
 // bring one new token that joins the tail as slot k->n_tail.
 int launch_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
                        const codec_stream *v, float scale, void *out, const int64_t out_stride[2],
-                       int32_t out_dtype, void *workspace, const Plan &p, const void *fuse_k,
+                       int32_t out_dtype, void *workspace, const DecodePlan &p, const void *fuse_k,
                        const int64_t kn_stride[2], const void *fuse_v, const int64_t vn_stride[2],
                        hipStream_t stream) {
   DecodeArgs a;
@@ -321,8 +329,7 @@ int launch_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, con
   if (lr > 0) return CODEC_ERR_HIP;
   return CODEC_OK;
 }
-
-}  // namespace
+}  // namespace cdattn
 
 extern "C" {
 
@@ -400,7 +407,7 @@ int codec_decode_workspace_bytes(const codec_stream *k, const codec_stream *v, i
   if (!bytes) return CODEC_ERR_NULL;
   const int rc = check_decode(k, v, Hq);
   if (rc) return rc;
-  const Plan p = make_plan(k, v, Hq);
+  const DecodePlan p = make_plan(k, v, Hq);
   if (!p.ok) return CODEC_ERR_UNSUPPORTED;
   *bytes = p.bytes;
   return CODEC_OK;
@@ -409,7 +416,7 @@ int codec_decode_workspace_bytes(const codec_stream *k, const codec_stream *v, i
 int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
                            const codec_stream *v, float scale, void *out, const int64_t out_stride[2],
                            int32_t out_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  Plan p;
+  DecodePlan p;
   const int rc = check_decode_call(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, workspace,
                                    workspace_bytes, &p);
   if (rc) return rc;
@@ -435,7 +442,7 @@ int codec_decode_attention_append(const void *q, const int64_t q_stride[2], int6
       s->n_tail += 1;
     }
   }
-  Plan p;
+  DecodePlan p;
   rc = check_decode_call(q, q_stride, Hq, &k2, &v2, scale, out, out_stride, out_dtype, workspace,
                          workspace_bytes, &p);
   if (rc) return rc;

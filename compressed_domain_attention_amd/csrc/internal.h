@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime.h>
 
+struct codec_stream;   // include/cdattn.h
+
 namespace cdattn {
 
 constexpr int kMaxR = 32;      // tokens per block
@@ -155,6 +157,29 @@ constexpr int decode_tile_rows(int D, int kf, int vf) {
 }
 
 int launch_decode(int D, int GS, int SP, int kf, int vf, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
+
+// Split plan of a decode: group size, query groups per kv head, padded kept
+// rows, splits per (b, kv head, query group), blocks per split, workgroups,
+// and the workspace layout (counters, then (max, sum) pairs, then partial
+// accumulators).  A pure function of the shapes.
+struct DecodePlan {
+  bool ok;
+  int GS, NQG, SP, ns;
+  int64_t pairs, chunk, n_wg;
+  size_t off_ml, off_acc, bytes;
+};
+
+// Validation of a decode call apart from its workspace; no HIP call.
+int decode_check_args(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
+                      const codec_stream *v, float scale, const void *out, const int64_t out_stride[2],
+                      int32_t out_dtype, DecodePlan *p);
+// The decode launch for validated arguments and a workspace of p.bytes
+// (fuse_k / fuse_v non-null: one new token joins the tail as slot n_tail).
+int launch_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
+                       const codec_stream *v, float scale, void *out, const int64_t out_stride[2],
+                       int32_t out_dtype, void *workspace, const DecodePlan &p, const void *fuse_k,
+                       const int64_t kn_stride[2], const void *fuse_v, const int64_t vn_stride[2],
+                       hipStream_t stream);
 #define CDATTN_DECL_DECODE(K, V) \
   int launch_decode_##K##_##V(int D, int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
 CDATTN_DECL_DECODE(i8, i8)

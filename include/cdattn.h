@@ -225,6 +225,35 @@ int codec_decode_attention_append(const void *q, const int64_t q_stride[2], int6
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * codec_decode_attention_noalloc -- codec_decode_attention without a caller
+ * workspace, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments (minus the workspace), kernels, split plan and results as
+ * codec_decode_attention, bit for bit.  The split partials and arrival
+ * counters live in a library-owned device array of CODEC_SCRATCH_BYTES per
+ * GPU (zero when the library is loaded, held until the process ends; every
+ * completed call leaves its counters at zero again).  The call allocates
+ * nothing; its first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress, which may load the library's code onto the
+ * device) and keeps the address, so make that first call outside graph
+ * capture; later calls may be captured.
+ * Limit: a decode whose split plan has more than one split per (b, kv head,
+ * query group) needs codec_decode_workspace_bytes(k, v, Hq) of scratch and
+ * is rejected with CODEC_ERR_WORKSPACE when that exceeds CODEC_SCRATCH_BYTES
+ * (only the largest head_dim / group-size shapes with about 255 (b, kv head)
+ * pairs reach it); a single-split plan uses none.
+ * Concurrency: all calls on one GPU share the array, so calls that overlap
+ * on that GPU (different HIP streams, or one graph replayed on two streams)
+ * race and must be serialised by the caller.
+ * Errors: those of codec_decode_attention (WORKSPACE as above), UNSUPPORTED
+ * (device index of 64 or more), HIP (including a failed address lookup).
+ */
+#define CODEC_SCRATCH_BYTES (4u << 20)
+int codec_decode_attention_noalloc(const void *q, const int64_t q_stride[2], int64_t Hq,
+                                   const codec_stream *k, const codec_stream *v, float scale, void *out,
+                                   const int64_t out_stride[2], int32_t out_dtype, hipStream_t stream);
+
+/*
  * codec_materialise -- the decoded (materialised) view of a stream, e.g. for
  * prefill attention.  cache.py ``_CodecStream.read`` / ``_decode_pending``:
  * the view is the archived blocks decoded, X_hat = M^T C block by block

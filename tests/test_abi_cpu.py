@@ -38,7 +38,8 @@ def test_header_symbols_exported(lib):
     names = declared_functions()
     assert set(names) == {"codec_basis", "codec_encode_blocks", "codec_append_step",
                           "codec_decode_workspace_bytes", "codec_decode_attention", "codec_status_string",
-                          "codec_materialise", "codec_crop", "codec_select_batch", "codec_decode_attention_append"}
+                          "codec_materialise", "codec_crop", "codec_select_batch", "codec_decode_attention_append",
+                          "codec_decode_attention_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -296,3 +297,43 @@ def test_decode_append_validation(lib):
     assert call(kk=kf, vv=vf) == CAPACITY
     for s in (k, v, kf, vf):
         assert s.n_blocks == 16 and s.n_tail in (3, 7)
+
+
+SCRATCH_BYTES = 4 << 20      # CODEC_SCRATCH_BYTES
+
+
+def test_decode_noalloc_validation(lib):
+    # the same argument checks as codec_decode_attention (no workspace), all
+    # before any HIP call
+    k = stream(n_blocks=16, capacity=16)
+    v = stream(n_blocks=16, capacity=16)
+    two = bd._I64_2(2048, 128)
+
+    def dec(q=FAKE, Hq=16, scale=0.1, out=FAKE, odt=bd.FMT_F32, qs=two, kk=k, vv=v):
+        return lib.codec_decode_attention_noalloc(q, qs, Hq, ctypes.byref(kk), ctypes.byref(vv), ctypes.c_float(scale),
+                                                  out, two, odt, None)
+
+    assert dec(q=None) == NULL
+    assert dec(out=None) == NULL
+    assert dec(Hq=6) == SHAPE
+    assert dec(scale=0.0) == SCALE
+    assert dec(odt=bd.FMT_I8) == FORMAT
+    assert dec(q=FAKE + 2) == SHAPE
+    assert dec(vv=stream(n_blocks=16, capacity=16, keep=3)) == SHAPE
+    assert dec(kk=stream(), vv=stream()) == SHAPE
+    assert dec(kk=stream(head_dim=96), vv=stream(head_dim=96)) == UNSUPPORTED
+    assert lib.codec_decode_attention_noalloc(FAKE, None, 16, ctypes.byref(k), ctypes.byref(v), ctypes.c_float(0.1),
+                                              FAKE, two, bd.FMT_F32, None) == NULL
+
+
+def test_decode_noalloc_rejects_plans_beyond_the_scratch(lib):
+    # 255 (b, kv head) pairs, eight-head groups, head_dim 256: two splits per
+    # pair and more partials than the scratch array holds -> WORKSPACE,
+    # before any HIP call; the plan's workspace size says the same
+    kw = dict(batch=255, heads=1, head_dim=256, n_blocks=4096, capacity=4096)
+    k, v = stream(**kw), stream(**kw)
+    rc, need = ws_bytes(lib, k, v, 8)
+    assert rc == OK and need > SCRATCH_BYTES
+    two = bd._I64_2(2048, 256)
+    assert lib.codec_decode_attention_noalloc(FAKE, two, 8, ctypes.byref(k), ctypes.byref(v), ctypes.c_float(0.1),
+                                              FAKE, two, bd.FMT_F32, None) == WORKSPACE
