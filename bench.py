@@ -192,17 +192,62 @@ def archive_ops(w, streams, dev, rounds=3):
                              "what": "all batch rows of one layer's key stream, reversed, into new buffers"}}
 
 
-def cpu_baseline(w, k, v, q, budget_s=12.0):
+def read_ceiling(per_launch, L, dev, cap_stream, rounds=4):
+    """The streaming-read ceiling for this size: one plain read of
+    `per_launch` bytes (the decode's algorithmic bytes) per launch, rotating
+    over L buffers at their own addresses like the decode's layers, captured
+    in a graph and timed with events on the capture stream; the fastest of
+    several grid sizes (codec_measure_read: 16-byte loads, sixteen requested
+    together per thread)."""
+    nbytes = -(-per_launch // 16) * 16
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(L)]
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    best = None
+    for wg in (256, 512, 1024, 2048, 4096):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            for _ in range(rounds):
+                for b in bufs:
+                    cda.measure_read(b, sink, wg)
+        with torch.cuda.stream(cap_stream):
+            g.replay()
+            e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e_a.record(cap_stream)
+            for _ in range(5):
+                g.replay()
+            e_b.record(cap_stream)
+        torch.cuda.synchronize()
+        us = e_a.elapsed_time(e_b) * 1e3 / (5 * rounds * L)
+        if best is None or us < best[0]:
+            best = (us, wg)
+    del bufs
+    us, wg = best
+    return {"kernel": "read_kernel", "avg_launch_us": round(us, 3), "bytes": nbytes, "workgroups": wg,
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 2),
+            "what": f"one plain read of the decode's algorithmic bytes per launch, {L} buffers rotated, graph-timed; "
+                    f"fastest of 256..4096 workgroups"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, k, v, q, budget_s=12.0, budget_1t_s=5.0):
     """The fp64 oracle on the host cores, on a bounded sample: whole-sequence
     decode attention of one kv head (with its G query heads) at a time,
     cycling over the kv heads until the time budget is spent (the archives
-    are encoded once, outside the timed part).  Returns the JSON object."""
+    are encoded once, outside the timed part).  BLAS threads are set to the
+    cores this process may run on; a second, shorter sample runs on one
+    thread.  Returns the JSON object."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
     R, S = w.R, w.S
     n = w.T // R
     per_head = n * S * (w.D * EB[w.kfmt] + (4 if w.kfmt == "i8" else 0) + w.D * EB[w.vfmt]
@@ -215,18 +260,29 @@ def cpu_baseline(w, k, v, q, budget_s=12.0):
         kx = syn.bf16_to_numpy(k[b:b + 1, h:h + 1, :w.T])
         vx = syn.bf16_to_numpy(v[b:b + 1, h:h + 1, :w.T])
         arch.append((b, h, O.encode(kx, R, S, w.kfmt), O.encode(vx, R, S, w.vfmt)))
-    done, t_used = 0, 0.0
-    while t_used < budget_s:
-        b, h, ka, va = arch[done % len(arch)]
-        qs = qn[b:b + 1, h * w.G:(h + 1) * w.G]
-        t1 = time.perf_counter()
-        O.decode_attention(qs, ka, va, scale)
-        t_used += time.perf_counter() - t1
-        done += 1
+
+    def run(budget):
+        done, t_used = 0, 0.0
+        while t_used < budget:
+            b, h, ka, va = arch[done % len(arch)]
+            qs = qn[b:b + 1, h * w.G:(h + 1) * w.G]
+            t1 = time.perf_counter()
+            O.decode_attention(qs, ka, va, scale)
+            t_used += time.perf_counter() - t1
+            done += 1
+        return done, t_used
+
+    with threadpool_limits(limits=cores):
+        done, t_used = run(budget_s)
+    with threadpool_limits(limits=1):
+        done1, t_used1 = run(budget_1t_s)
     return {"value": round(done * per_head / t_used / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "threads_setting": f"BLAS threads = len(os.sched_getaffinity(0)) = {cores}", "cpu_model": cpu_model(),
+            "value_1_thread": round(done1 * per_head / t_used1 / 1e9, 4),
             "sample": f"{done} whole-archive decodes ({w.T} tokens, one kv head with its {w.G} query heads each), "
                       f"cycling over {len(arch)} of the {w.B * w.Hkv} kv heads; fp64 numpy; "
-                      f"{t_used:.1f}s of oracle time"}
+                      f"{t_used:.1f}s of oracle time on {cores} threads, then {done1} decodes in {t_used1:.1f}s "
+                      f"on 1 thread"}
 
 
 def main():
@@ -345,6 +401,8 @@ def main():
     achieved = per_launch / avg_s / 1e9
     traffic = load_traffic(w.name)
     ops = archive_ops(w, streams, dev)
+    print("# timing the streaming-read ceiling", file=sys.stderr, flush=True)
+    ceiling = read_ceiling(per_launch, L, dev, cap_stream)
 
     res = {
         "metric": "decode-attn compressed-KV GB/s + query-heads*tokens/s at 1 GPU; % of HBM peak",
@@ -361,6 +419,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "decode_kernel", "avg_launch_us": round(avg_s * 1e6, 3),
                      "algorithmic_bytes_per_launch": per_launch},
+        "read_ceiling": {**ceiling, "decode_frac_of_ceiling": round(achieved / ceiling["GBps"], 4)},
         "encode": {"avg_ms": round(float(np.mean(enc_ms[1:] or enc_ms)), 4),
                    "bytes": enc_bytes,
                    "GBps": round(enc_bytes / (float(np.mean(enc_ms[1:] or enc_ms)) * 1e-3) / 1e9, 2)},

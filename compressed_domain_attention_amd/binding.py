@@ -72,6 +72,8 @@ def _lib():
         lib.codec_materialise.argtypes = [P, i64, vp, LP, i32, vp]
         lib.codec_crop.argtypes = [P, i64, vp]
         lib.codec_select_batch.argtypes = [P, P, LP, i64, vp]
+        lib.codec_measure_read.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
+        lib.codec_measure_read.restype = ctypes.c_int
         lib.codec_status_string.argtypes = [ctypes.c_int]
         lib.codec_status_string.restype = ctypes.c_char_p
         for name in ("codec_basis", "codec_encode_blocks", "codec_append_step",
@@ -424,6 +426,15 @@ def decode_attention_append(q, k, v, k_new, v_new, scale=None, out=None, out_dty
     k._sync(dk)
     v._sync(dv)
     return out
+
+
+def measure_read(src, sink, workgroups, stream=None):
+    """One streaming read of the whole of `src` (a device tensor, 16-byte
+    aligned, size a multiple of 16 bytes) by `workgroups` workgroups
+    (codec_measure_read; a measurement helper, not part of the method)."""
+    st = ctypes.c_void_p(_torch_stream(src.device, stream).cuda_stream)
+    _check(_lib().codec_measure_read(ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
+                                     ctypes.c_void_p(sink.data_ptr()), int(workgroups), st), "codec_measure_read")
 
 
 def default_scale(D):

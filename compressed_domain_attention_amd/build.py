@@ -16,7 +16,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libcdattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "encode.hip", "archive.hip", "scratch.hip"] + [f"decode_{k}_{v}.hip" for k in ("i8", "bf16", "f32") for v in ("i8", "bf16", "f32")]
+SOURCES = ["api.cpp", "encode.hip", "archive.hip", "scratch.hip", "measure.hip"] + [f"decode_{k}_{v}.hip" for k in ("i8", "bf16", "f32") for v in ("i8", "bf16", "f32")]
 
 # Packed fp32 VALU ops are disabled for all device code.
 # Leading scalar kernel arguments are preloaded into SGPRs at wave launch

@@ -1105,58 +1105,37 @@ __device__ __forceinline__ void process_lv(const TileBuf<D, GS, KF, VF> &B, int 
 // are read from kn / vn (rows past the old tail read zeros from the tail,
 // every other row reads zeros from the new token), and with store_new the
 // lanes holding it also write it to tail slot t_new.
-template <int D, int GS, int SP, int SWR, int RAWK, int RAWV, int EV, typename Prep>
-__device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt, const void *kn, const void *vn,
-                                          int t_new, bool store_new, int lane, h2 (&qh)[GS][8],
-                                          const float (&cq)[GS], float *sw, float (&m_u)[GS], float &m_lane,
-                                          float &l_lane, float (&acc)[GS][EV], float (&alpha)[GS], Prep &&prep) {
-  constexpr int LK = D / 16, RK = 64 / LK, EBK = ebytes(RAWK), EBV = ebytes(RAWV);
-  constexpr int LV = D / EV, RV = 64 / LV, VDW = EV * EBV / 4;
+// issue() requests the first chunk of rows (and the new token) and returns;
+// compute() waits for them, so the caller can request other data in between.
+template <int D, int GS, int SP, int SWR, int RAWK, int RAWV, int EV>
+struct TailPass {
+  static constexpr int LK = D / 16, RK = 64 / LK, EBK = ebytes(RAWK), EBV = ebytes(RAWV);
+  static constexpr int LV = D / EV, RV = 64 / LV, VDW = EV * EBV / 4;
   static_assert(kMaxR % RV == 0 && kMaxR % RK == 0, "tail steps must tile the tail rows");
   // Up to PK key and PV value load steps (about 16 registers of data each,
   // 8 with eight heads per group) are requested together (rows past the tail
   // read zeros), so the first chunk of both costs one round trip.
-  constexpr int BUDGET = GS >= 8 ? 8 : 16;
-  constexpr int PK = cmin(kMaxR / RK, cmax(1, BUDGET / (4 * EBK))), PV = cmin(kMaxR / RV, cmax(1, BUDGET / VDW));
-  const int t_old = t_new >= 0 ? t_new : nt;   // rows held by the tail slab
-  const rsrc_t rk = make_rsrc(kt, (uint32_t)t_old * D * EBK);
-  const rsrc_t rv = make_rsrc(vt, (uint32_t)t_old * D * EBV);
-  constexpr uint32_t kOut = 0x40000000u;        // an offset past every range: the load reads zeros
-  const int rrk = lane / LK, ck = lane % LK;
-  const int rrv = lane / LV, cv = lane % LV;
-  const uint32_t offk = (uint32_t)(rrk * D + ck * 16) * EBK;
-  const uint32_t offv = (uint32_t)(rrv * D + cv * EV) * EBV;
+  static constexpr int BUDGET = GS >= 8 ? 8 : 16;
+  static constexpr int PK = cmin(kMaxR / RK, cmax(1, BUDGET / (4 * EBK))), PV = cmin(kMaxR / RV, cmax(1, BUDGET / VDW));
+  static constexpr uint32_t kOut = 0x40000000u;   // an offset past every range: the load reads zeros
+  const void *kt, *vt;
+  int nt, t_new, rrk, ck, rrv, cv;
+  rsrc_t rk, rv;
+  uint32_t offk, offv;
   // The new token's rows, held by the lanes whose row in a step it is
   // (zeros in every other lane), merged into its step's registers below.
   uint4 knw[EBK];
   uint32_t vnw[VDW];
-  {
-    const rsrc_t rkn = make_rsrc(kn, t_new >= 0 ? (uint32_t)(D * EBK) : 0u);
-    const rsrc_t rvn = make_rsrc(vn, t_new >= 0 ? (uint32_t)(D * EBV) : 0u);
-    const uint32_t onk = t_new >= 0 && rrk == t_new % RK ? (uint32_t)(ck * 16) * EBK : kOut;
-    const uint32_t onv = t_new >= 0 && rrv == t_new % RV ? (uint32_t)(cv * EV) * EBV : kOut;
-#pragma unroll
-    for (int k = 0; k < EBK; ++k) knw[k] = bload128(rkn, onk + 16 * k, 0);
-    if constexpr (VDW % 4 == 0) {
-#pragma unroll
-      for (int k = 0; k < VDW / 4; ++k) {
-        const uint4 t = bload128(rvn, onv + 16 * k, 0);
-        vnw[4 * k] = t.x; vnw[4 * k + 1] = t.y; vnw[4 * k + 2] = t.z; vnw[4 * k + 3] = t.w;
-      }
-    } else {
-      const uint2 t = bload64(rvn, onv, 0);
-      vnw[0] = t.x; vnw[1] = t.y;
-    }
-  }
   uint4 kb[PK][EBK];
   uint32_t vb[PV][VDW];
-  auto load_k = [&](int r00) {
+
+  __device__ __forceinline__ void load_k(int r00) {
 #pragma unroll
     for (int s = 0; s < PK; ++s)
 #pragma unroll
       for (int k = 0; k < EBK; ++k) kb[s][k] = bload128(rk, offk + 16 * k, (r00 + s * RK) * D * EBK);
-  };
-  auto load_v = [&](int r00) {
+  }
+  __device__ __forceinline__ void load_v(int r00) {
 #pragma unroll
     for (int s = 0; s < PV; ++s) {
       if constexpr (VDW % 4 == 0) {
@@ -1165,72 +1144,129 @@ __device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt
           const uint4 t = bload128(rv, offv + 16 * k, (r00 + s * RV) * D * EBV);
           vb[s][4 * k] = t.x; vb[s][4 * k + 1] = t.y; vb[s][4 * k + 2] = t.z; vb[s][4 * k + 3] = t.w;
         }
-      } else {
+      } else if constexpr (VDW == 2) {
         const uint2 t = bload64(rv, offv, (r00 + s * RV) * D * EBV);
         vb[s][0] = t.x; vb[s][1] = t.y;
+      } else {
+        static_assert(VDW == 1, "value words per lane: 1, 2 or a multiple of 4");
+        vb[s][0] = __builtin_bit_cast(uint32_t, bloadf(rv, offv, (r00 + s * RV) * D * EBV));
       }
     }
-  };
-  // OR the new token into the step that holds its row (its lanes read zeros from the slab)
-  auto merge_k = [&](int r00) {
+  }
+  // OR the new token into the step that holds its row (its lanes read zeros
+  // from the slab).  Every step takes an OR with the token or with zero, so
+  // no step is picked by a computed index (which would put the rows in
+  // scratch memory).
+  __device__ __forceinline__ void merge_k(int r00) {
 #pragma unroll
-    for (int s = 0; s < PK; ++s)
-      if (t_new >= r00 + s * RK && t_new < r00 + (s + 1) * RK) {
-#pragma unroll
-        for (int k = 0; k < EBK; ++k)
-          kb[s][k] = make_uint4(kb[s][k].x | knw[k].x, kb[s][k].y | knw[k].y, kb[s][k].z | knw[k].z,
-                                kb[s][k].w | knw[k].w);
-      }
-  };
-  auto merge_v = [&](int r00) {
-#pragma unroll
-    for (int s = 0; s < PV; ++s)
-      if (t_new >= r00 + s * RV && t_new < r00 + (s + 1) * RV) {
-#pragma unroll
-        for (int k = 0; k < VDW; ++k) vb[s][k] |= vnw[k];
-      }
-  };
-  // the new token's rows into tail slot t_new (the lanes that hold it)
-  auto store_new_rows = [&]() {
-    if (!store_new) return;
-    if (rrk == t_new % RK) {
+    for (int s = 0; s < PK; ++s) {
+      const bool hit = t_new >= r00 + s * RK && t_new < r00 + (s + 1) * RK;
 #pragma unroll
       for (int k = 0; k < EBK; ++k)
-        *reinterpret_cast<uint4 *>(static_cast<char *>(const_cast<void *>(kt)) +
-                                   (size_t)(t_new * D + ck * 16) * EBK + 16 * k) = knw[k];
+        kb[s][k] = make_uint4(kb[s][k].x | (hit ? knw[k].x : 0u), kb[s][k].y | (hit ? knw[k].y : 0u),
+                              kb[s][k].z | (hit ? knw[k].z : 0u), kb[s][k].w | (hit ? knw[k].w : 0u));
     }
-    if (rrv == t_new % RV) {
-      uint32_t *dst = reinterpret_cast<uint32_t *>(static_cast<char *>(const_cast<void *>(vt)) +
-                                                   (size_t)(t_new * D + cv * EV) * EBV);
+  }
+  __device__ __forceinline__ void merge_v(int r00) {
 #pragma unroll
-      for (int k = 0; k < VDW; ++k) dst[k] = vnw[k];
+    for (int s = 0; s < PV; ++s) {
+      const bool hit = t_new >= r00 + s * RV && t_new < r00 + (s + 1) * RV;
+#pragma unroll
+      for (int k = 0; k < VDW; ++k) vb[s][k] |= hit ? vnw[k] : 0u;
     }
-  };
-  load_k(0);
-  load_v(0);
-  merge_k(0);
-  store_new_rows();
-  prep();   // the query in the VALU layout, its loads issued before the tail's
-  kcompute<D, GS, SWR, RAWK, PK, EBK>(kb, nt, lane, qh, cq, sw, 0);
-  for (int r00 = PK * RK; r00 < nt; r00 += PK * RK) {
-    load_k(r00);
-    merge_k(r00);
-    kcompute<D, GS, SWR, RAWK, PK, EBK>(kb, nt, lane, qh, cq, sw, r00);
   }
-  wave_lds_sync();
-  Basis<SP> unit;
-  unit.unit(lane);
-  logits_any<GS, SP, SWR>(unit, sw, nt, 1, 1, lane, m_u, m_lane, l_lane, alpha);
-  rescale(acc, alpha);
-  wave_lds_sync();
-  merge_v(0);
-  vcompute<D, GS, SWR, RAWV, PV, VDW, EV>(vb, nt, lane, sw, acc, 0);
-  for (int r00 = PV * RV; r00 < nt; r00 += PV * RV) {
-    load_v(r00);
-    merge_v(r00);
-    vcompute<D, GS, SWR, RAWV, PV, VDW, EV>(vb, nt, lane, sw, acc, r00);
+
+  __device__ __forceinline__ void issue(const void *kt_, const void *vt_, int nt_, const void *kn, const void *vn,
+                                        int t_new_, int lane) {
+    kt = kt_;
+    vt = vt_;
+    nt = nt_;
+    t_new = t_new_;
+    const int t_old = t_new >= 0 ? t_new : nt;   // rows held by the tail slab
+    rk = make_rsrc(kt, (uint32_t)t_old * D * EBK);
+    rv = make_rsrc(vt, (uint32_t)t_old * D * EBV);
+    rrk = lane / LK;
+    ck = lane % LK;
+    rrv = lane / LV;
+    cv = lane % LV;
+    offk = (uint32_t)(rrk * D + ck * 16) * EBK;
+    offv = (uint32_t)(rrv * D + cv * EV) * EBV;
+    {
+      const rsrc_t rkn = make_rsrc(kn, t_new >= 0 ? (uint32_t)(D * EBK) : 0u);
+      const rsrc_t rvn = make_rsrc(vn, t_new >= 0 ? (uint32_t)(D * EBV) : 0u);
+      const uint32_t onk = t_new >= 0 && rrk == t_new % RK ? (uint32_t)(ck * 16) * EBK : kOut;
+      const uint32_t onv = t_new >= 0 && rrv == t_new % RV ? (uint32_t)(cv * EV) * EBV : kOut;
+#pragma unroll
+      for (int k = 0; k < EBK; ++k) knw[k] = bload128(rkn, onk + 16 * k, 0);
+      if constexpr (VDW % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < VDW / 4; ++k) {
+          const uint4 t = bload128(rvn, onv + 16 * k, 0);
+          vnw[4 * k] = t.x; vnw[4 * k + 1] = t.y; vnw[4 * k + 2] = t.z; vnw[4 * k + 3] = t.w;
+        }
+      } else if constexpr (VDW == 2) {
+        const uint2 t = bload64(rvn, onv, 0);
+        vnw[0] = t.x; vnw[1] = t.y;
+      } else {
+        vnw[0] = __builtin_bit_cast(uint32_t, bloadf(rvn, onv, 0));
+      }
+    }
+    load_k(0);
+    load_v(0);
   }
-  wave_lds_sync();
+
+  template <typename Prep>
+  __device__ __forceinline__ void compute(bool store_new, int lane, h2 (&qh)[GS][8], const float (&cq)[GS], float *sw,
+                                          float (&m_u)[GS], float &m_lane, float &l_lane, float (&acc)[GS][EV],
+                                          float (&alpha)[GS], Prep &&prep) {
+    merge_k(0);
+    // the new token's rows into tail slot t_new (the lanes that hold it)
+    if (store_new) {
+      if (rrk == t_new % RK) {
+#pragma unroll
+        for (int k = 0; k < EBK; ++k)
+          *reinterpret_cast<uint4 *>(static_cast<char *>(const_cast<void *>(kt)) +
+                                     (size_t)(t_new * D + ck * 16) * EBK + 16 * k) = knw[k];
+      }
+      if (rrv == t_new % RV) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(static_cast<char *>(const_cast<void *>(vt)) +
+                                                     (size_t)(t_new * D + cv * EV) * EBV);
+#pragma unroll
+        for (int k = 0; k < VDW; ++k) dst[k] = vnw[k];
+      }
+    }
+    prep();   // the query in the VALU layout, its loads issued before the tail's
+    kcompute<D, GS, SWR, RAWK, PK, EBK>(kb, nt, lane, qh, cq, sw, 0);
+    for (int r00 = PK * RK; r00 < nt; r00 += PK * RK) {
+      load_k(r00);
+      merge_k(r00);
+      kcompute<D, GS, SWR, RAWK, PK, EBK>(kb, nt, lane, qh, cq, sw, r00);
+    }
+    wave_lds_sync();
+    Basis<SP> unit;
+    unit.unit(lane);
+    logits_any<GS, SP, SWR>(unit, sw, nt, 1, 1, lane, m_u, m_lane, l_lane, alpha);
+    rescale(acc, alpha);
+    wave_lds_sync();
+    merge_v(0);
+    vcompute<D, GS, SWR, RAWV, PV, VDW, EV>(vb, nt, lane, sw, acc, 0);
+    for (int r00 = PV * RV; r00 < nt; r00 += PV * RV) {
+      load_v(r00);
+      merge_v(r00);
+      vcompute<D, GS, SWR, RAWV, PV, VDW, EV>(vb, nt, lane, sw, acc, r00);
+    }
+    wave_lds_sync();
+  }
+};
+
+template <int D, int GS, int SP, int SWR, int RAWK, int RAWV, int EV, typename Prep>
+__device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt, const void *kn, const void *vn,
+                                          int t_new, bool store_new, int lane, h2 (&qh)[GS][8],
+                                          const float (&cq)[GS], float *sw, float (&m_u)[GS], float &m_lane,
+                                          float &l_lane, float (&acc)[GS][EV], float (&alpha)[GS], Prep &&prep) {
+  TailPass<D, GS, SP, SWR, RAWK, RAWV, EV> tp;
+  tp.issue(kt, vt, nt, kn, vn, t_new, lane);
+  tp.compute(store_new, lane, qh, cq, sw, m_u, m_lane, l_lane, acc, alpha, prep);
 }
 
 // The first tiles' addresses come as separate leading arguments (row counts
@@ -1361,7 +1397,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
     }
   }
 
-  // ---- the raw tail: one wave of the last split, on the VALU paths
+  // ---- the raw tail: one wave of the last split (the one with the fewest
+  // tiles), on the VALU paths
   const bool tail_wave = a.n_tail + a.fuse_new > 0 && split == a.ns - 1 && wave == ntiles % W;
   // tail accumulator beside the MFMA layout: ET columns per lane, few registers
   constexpr int ET = C::VM ? cmax(D / 64, 16 / GS) : 1, LT = D / ET;

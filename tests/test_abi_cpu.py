@@ -44,6 +44,19 @@ def test_header_symbols_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_measure_header_symbols_and_checks(lib):
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "cdattn_measure.h")).read(), flags=re.S)
+    names = re.findall(r"^int\s+(codec_\w+)\s*\(", text, flags=re.M)
+    assert names == ["codec_measure_read"]
+    assert hasattr(lib, "codec_measure_read")
+    assert lib.codec_measure_read(None, 16, FAKE, 4, None) == NULL
+    assert lib.codec_measure_read(FAKE, 16, None, 4, None) == NULL
+    assert lib.codec_measure_read(FAKE + 8, 16, FAKE, 4, None) == SHAPE
+    assert lib.codec_measure_read(FAKE, 24, FAKE, 4, None) == SHAPE
+    assert lib.codec_measure_read(FAKE, 0, FAKE, 4, None) == SHAPE
+    assert lib.codec_measure_read(FAKE, 16, FAKE, 0, None) == SHAPE
+
+
 def test_status_strings(lib):
     seen = set()
     for s in range(10):
