@@ -45,7 +45,7 @@ def decode_bytes(w, n_blocks, n_tail):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("decode_impl.h", "internal.h"):
+    for f in ("decode_impl.h", "internal.h", "basis.h", "basis_dev.h"):
         h.update(open(os.path.join(ROOT, "compressed_domain_attention_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -285,6 +285,75 @@ def cpu_baseline(w, k, v, q, budget_s=12.0, budget_1t_s=5.0):
                       f"on 1 thread"}
 
 
+def graph_time_us(fn, stream, rounds=4, reps=5):
+    """Average time of one fn() call: fn captured `rounds` times into one HIP
+    graph on `stream`, the graph replayed `reps` times, timed with events on
+    that stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(rounds):
+            fn()
+    with torch.cuda.stream(stream):
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * rounds)
+
+
+def layer_launch_bound(w, L, dev):
+    """What one launch per step across L layers could save at most: L decode
+    launches (one per layer's archive, as a model runs them) against one
+    launch over the same bytes (the L layers' archives as L times the batch
+    rows, which a model cannot do: each layer's query needs the previous
+    layer's output), and the fixed cost of one launch: the intercept of the
+    launch time against the context length (full, half and quarter length
+    keep the same split count), i.e. launch, prologue, tail, merge and
+    combine, the part that a resident multi-layer kernel could hide."""
+    cs = torch.cuda.Stream()
+    k, v = syn.workload_kv_device(w, T=w.T, device=dev)
+    q = syn.workload_query(w, 0).to(dev)
+
+    def make(kk, vv, B, T):
+        ks = cda.CodecStream(B, w.Hkv, w.D, w.R, w.S, fmt=w.kfmt, device=dev)
+        vs = cda.CodecStream(B, w.Hkv, w.D, w.R, w.S, fmt=w.vfmt, device=dev)
+        ks.encode(kk[:, :, :T])
+        vs.encode(vv[:, :, :T])
+        return ks, vs
+
+    layers = [make(k, v, w.B, w.T) for _ in range(L)]
+    merged = make(k.repeat(L, 1, 1, 1), v.repeat(L, 1, 1, 1), w.B * L, w.T)
+    lengths = [w.T, w.T // 2, w.T // 4]
+    shorter = {T: [make(k, v, w.B, T) for _ in range(L)] for T in lengths[1:]}
+    qm = q.repeat(L, 1, 1, 1)
+    outs = [torch.empty((w.B, w.Hq, 1, w.D), dtype=torch.float32, device=dev) for _ in range(L)]
+    om = torch.empty((w.B * L, w.Hq, 1, w.D), dtype=torch.float32, device=dev)
+    need = max(cda.decode_workspace_bytes(*layers[0], w.Hq), cda.decode_workspace_bytes(*merged, w.Hq))
+    ws = torch.zeros(need + 4096, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def per_layer(group):
+        def fn():
+            for li, (ks, vs) in enumerate(group):
+                cda.decode_attention(q, ks, vs, out=outs[li], workspace=ws)
+        return fn
+
+    t_layers = graph_time_us(per_layer(layers), cs)
+    t_merged = graph_time_us(lambda: cda.decode_attention(qm, *merged, out=om, workspace=ws), cs)
+    per_len = [t_layers / L] + [graph_time_us(per_layer(shorter[T]), cs) / L for T in lengths[1:]]
+    slope, intercept = np.polyfit(np.array(lengths, dtype=np.float64), np.array(per_len), 1)
+    return {"workload": w.name, "layers": L, "per_layer_launches_us": round(t_layers, 2),
+            "one_merged_launch_us": round(t_merged, 2), "saving_bound_us": round(t_layers - t_merged, 2),
+            "saving_bound_frac": round(1 - t_merged / t_layers, 4),
+            "launch_us_by_tokens": {str(T): round(t, 3) for T, t in zip(lengths, per_len)},
+            "fixed_cost_per_launch_us": round(float(intercept), 3),
+            "us_per_million_tokens": round(float(slope) * 1e6, 3),
+            "bytes_per_layer": decode_bytes(w, layers[0][0].n_blocks, layers[0][0].n_tail)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -295,6 +364,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", type=int, default=0, metavar="N",
                     help="launch sequence for rocprofv3 counter passes: N decodes and N calibration copies")
+    ap.add_argument("--layer-launch-bound", action="store_true",
+                    help="time L per-layer decode launches against one launch over the same bytes, and print that")
     ap.add_argument("--traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="summarise two rocprofv3 --pmc runs into profiles/decode_<workload>_traffic.json")
     args = ap.parse_args()
@@ -311,6 +382,9 @@ def main():
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.layer_launch_bound:
+        print(json.dumps(layer_launch_bound(w, args.layers, dev)), flush=True)
+        return
     L, K, W = args.layers, args.steps, args.warmup
     extra = K + W
     print(f"# generating {w.name}: B={w.B} Hkv={w.Hkv} T={w.T}+{extra} D={w.D}", file=sys.stderr, flush=True)

@@ -1,16 +1,28 @@
 // Host side of the C ABI declared in include/cdattn.h: argument validation
-// (always before any HIP call), the DCT basis, the split plan of the decode,
-// and kernel launches.  No allocation, no synchronisation, no state.
+// (always before any launch), the DCT basis, the split plan of the decode,
+// and kernel launches.  No allocation and no synchronisation; the only state
+// is the per-device, per-kernel split target the plan asks the runtime for
+// once.
 
 #include <math.h>
 #include <string.h>
 
+#include <array>
+#include <map>
+#include <mutex>
+
+#include "basis.h"
 #include "cdattn.h"
 #include "internal.h"
 
 using namespace cdattn;
 
 namespace {
+
+// The codec's basis table (see basis.h), host copy.
+const float kBasisHost[kBasisEntries] = {
+#include "cdattn_basis_table.inc"
+};
 
 bool fmt_ok(int f) { return f == CODEC_F32 || f == CODEC_BF16 || f == CODEC_I8 || f == CODEC_PNG; }
 bool raw_ok(int f) { return f == CODEC_F32 || f == CODEC_BF16; }
@@ -19,18 +31,12 @@ int elem_bytes(int f) { return (f == CODEC_F32 || f == CODEC_PNG) ? 4 : (f == CO
 int row_fmt(int f) { return f == CODEC_PNG ? CODEC_F32 : f; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Analysis basis in double, rounded to fp32 (flashcodec-kv README "Math":
-// M[j, i] = c_j cos(pi (2i + 1) j / (2R)), c_0 = sqrt(1/R), c_j = sqrt(2/R)).
-double basis_entry(int R, int j, int i) {
-  const double cj = j == 0 ? sqrt(1.0 / R) : sqrt(2.0 / R);
-  return cj * cos(M_PI * (2 * i + 1) * j / (2.0 * R));
-}
-
 int check_stream(const codec_stream *s) {
   if (!s) return CODEC_ERR_NULL;
   if (s->block < 1 || s->block > CODEC_MAX_BLOCK) return CODEC_ERR_SHAPE;
   if (s->keep < 1 || s->keep > s->block || s->keep > CODEC_MAX_KEEP) return CODEC_ERR_SHAPE;
   if (s->head_dim < 1) return CODEC_ERR_SHAPE;
+  if (s->head_dim > kMaxD || s->head_dim % 8 != 0) return CODEC_ERR_UNSUPPORTED;
   if (s->batch < 1 || s->heads < 1) return CODEC_ERR_SHAPE;
   if (s->batch * s->heads > (int64_t)1 << 31) return CODEC_ERR_SHAPE;
   if (!fmt_ok(s->fmt) || !raw_ok(s->raw_dtype)) return CODEC_ERR_FORMAT;
@@ -44,7 +50,6 @@ int check_stream(const codec_stream *s) {
   if (!aligned16(s->tail) || (s->rows && !aligned16(s->rows)) ||
       (s->fmt == CODEC_I8 && s->scales && !aligned16(s->scales)))
     return CODEC_ERR_SHAPE;
-  if (s->head_dim != 64 && s->head_dim != 128 && s->head_dim != 256) return CODEC_ERR_UNSUPPORTED;
   return CODEC_OK;
 }
 
@@ -53,29 +58,15 @@ bool same_geometry(const codec_stream *a, const codec_stream *b) {
          a->heads == b->heads && a->n_blocks == b->n_blocks && a->n_tail == b->n_tail;
 }
 
-// Analysis matrix M[j*R + i] of a stream's rows: the fp32 DCT-II basis, or
-// for PNG mode the anchor / first-order difference rows (README "Math", PNG
-// item: delta_i = x_i - x_{i-1}, x_0 kept).
-void fill_M(int fmt, int R, int S, float *M) {
-  for (int j = 0; j < S; ++j)
-    for (int i = 0; i < R; ++i)
-      M[j * R + i] = fmt == CODEC_PNG ? (i == j ? 1.0f : (j > 0 && i == j - 1 ? -1.0f : 0.0f))
-                                      : (float)basis_entry(R, j, i);
-}
-
-// Synthesis entry A[i][j] (token i from row j): M^T for the DCT formats, the
-// cumulative sum for PNG mode (x_hat_i = x_0 + sum_{j=1..i} delta_j).
-float synth_entry(int fmt, int R, int i, int j) {
-  return fmt == CODEC_PNG ? (j <= i ? 1.0f : 0.0f) : (float)basis_entry(R, j, i);
-}
-
 EncodeArgs stream_encode_args(const codec_stream *s) {
   EncodeArgs e;
   memset(&e, 0, sizeof(e));
   e.raw = s->raw_dtype;
   e.fmt = row_fmt(s->fmt);
+  e.png = s->fmt == CODEC_PNG ? 1 : 0;
   e.R = s->block;
   e.S = s->keep;
+  e.D = s->head_dim;
   e.H = s->heads;
   e.n0 = s->n_blocks;
   e.cap = s->capacity;
@@ -87,10 +78,36 @@ EncodeArgs stream_encode_args(const codec_stream *s) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workgroups that fill MI355X once: 256 CUs x 1 resident 8-wave workgroup.
-constexpr int64_t kTargetWorkgroups = 256;
+// Workgroups that fill a device once when the runtime cannot be asked (a
+// host without a GPU): MI355X's 256 CUs with one 8-wave decode workgroup each.
+constexpr int64_t kDefaultTargetWorkgroups = 256;
 
-DecodePlan make_plan(const codec_stream *k, const codec_stream *v, int64_t Hq) {
+// Workgroups that fill device `dev` once with decode kernel instance (D, GS,
+// SP, kf, vf): its CU count times the instance's workgroups resident per CU
+// (the kernel's registers and LDS decide), at most kMaxTargetWorkgroups.
+// Asked once per device and instance, then kept.
+int64_t target_workgroups(int dev, int D, int GS, int SP, int kf, int vf, bool full) {
+  static std::mutex mu;
+  static std::map<std::array<int, 7>, int64_t> known;
+  if (dev < 0) return kDefaultTargetWorkgroups;
+  const std::array<int, 7> key{dev, D, GS, SP, kf, vf, full ? 1 : 0};
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = known.find(key);
+  if (it != known.end()) return it->second;
+  int64_t t = kDefaultTargetWorkgroups;
+  int cus = 0, cur = -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0 &&
+      hipGetDevice(&cur) == hipSuccess && (cur == dev || hipSetDevice(dev) == hipSuccess)) {
+    const int per_cu = resident_decode(D, GS, SP, kf, vf, full);   // asks the current device
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (per_cu > 0) t = (int64_t)cus * per_cu;
+  }
+  if (t > kMaxTargetWorkgroups) t = kMaxTargetWorkgroups;
+  known[key] = t;
+  return t;
+}
+
+DecodePlan make_plan(const codec_stream *k, const codec_stream *v, int64_t Hq, int dev) {
   DecodePlan p;
   const int64_t G = Hq / k->heads;
   p.GS = decode_group_size((int)G);
@@ -98,15 +115,19 @@ DecodePlan make_plan(const codec_stream *k, const codec_stream *v, int64_t Hq) {
   p.SP = decode_pad_keep(k->keep);
   p.pairs = k->batch * k->heads * p.NQG;
   const int64_t n = k->n_blocks;
-  const int64_t NB = decode_tile_rows(k->head_dim, row_fmt(k->fmt), row_fmt(v->fmt)) / k->keep;   // blocks per tile
+  const int DP = pad_dim(k->head_dim);   // compute width of the kernels
+  const int64_t NB = decode_tile_rows(DP, row_fmt(k->fmt), row_fmt(v->fmt)) / k->keep;   // blocks per tile
   p.ok = NB >= 1;
+  p.target = p.ok ? target_workgroups(dev, DP, p.GS, p.SP, row_fmt(k->fmt), row_fmt(v->fmt), DP == k->head_dim)
+                  : kDefaultTargetWorkgroups;
   if (n == 0 || !p.ok) {
     p.ns = 1;
     p.chunk = 0;
   } else {
-    // one 8-wave workgroup per CU; every wave of a split gets a tile or more
+    // enough splits to fill the device once; every wave of a split gets a
+    // tile or more
     const int64_t tiles = (n + NB - 1) / NB;
-    int64_t ns = (kTargetWorkgroups + p.pairs - 1) / p.pairs;
+    int64_t ns = (p.target + p.pairs - 1) / p.pairs;
     const int64_t ns_max = (tiles + kDecodeWaves - 1) / kDecodeWaves;
     if (ns > ns_max) ns = ns_max;
     if (ns < 1) ns = 1;
@@ -119,14 +140,15 @@ DecodePlan make_plan(const codec_stream *k, const codec_stream *v, int64_t Hq) {
   // Arrival counters live in a fixed region at the start of every workspace,
   // so calls of different shapes that share one workspace never see another
   // call's partials where they expect a zero counter.  More than one split
-  // only happens below kTargetWorkgroups pairs, which bounds the region.
-  if (p.ns > 1 && p.pairs > kTargetWorkgroups) p.ok = false;
+  // only happens below p.target <= kMaxTargetWorkgroups pairs, which bounds
+  // the region.
+  if (p.ns > 1 && p.pairs > kMaxTargetWorkgroups) p.ok = false;
   // the launch: grid z = batch rows x kv heads, row counts per (b, h) in 32 bits
   if (k->batch * k->heads > 65535 || k->capacity * k->keep > INT32_MAX || v->capacity * v->keep > INT32_MAX)
     p.ok = false;
-  const size_t counters = (size_t)kTargetWorkgroups * kCounterStride * 4;
+  const size_t counters = (size_t)kMaxTargetWorkgroups * kCounterStride * 4;
   const size_t ml = align256((size_t)p.pairs * p.ns * p.GS * 2 * 4);
-  const size_t acc = (size_t)p.pairs * p.ns * p.GS * k->head_dim * 4;
+  const size_t acc = (size_t)p.pairs * p.ns * p.GS * DP * 4;
   p.off_ml = counters;
   p.off_acc = counters + ml;
   p.bytes = counters + ml + acc;
@@ -159,19 +181,50 @@ int decode_pad_keep(int S) {
   while (sp < S) sp *= 2;
   return sp;
 }
-int launch_decode(int D, int GS, int SP, int kf, int vf, const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
+int launch_decode(int D, int GS, int SP, int kf, int vf, bool full, const DecodeArgs &a, int64_t n_wg,
+                  hipStream_t stream) {
   switch (kf * 3 + vf) {
-    case I8 * 3 + I8: return launch_decode_i8_i8(D, GS, SP, a, n_wg, stream);
-    case I8 * 3 + BF16: return launch_decode_i8_bf16(D, GS, SP, a, n_wg, stream);
-    case I8 * 3 + F32: return launch_decode_i8_f32(D, GS, SP, a, n_wg, stream);
-    case BF16 * 3 + I8: return launch_decode_bf16_i8(D, GS, SP, a, n_wg, stream);
-    case BF16 * 3 + BF16: return launch_decode_bf16_bf16(D, GS, SP, a, n_wg, stream);
-    case BF16 * 3 + F32: return launch_decode_bf16_f32(D, GS, SP, a, n_wg, stream);
-    case F32 * 3 + I8: return launch_decode_f32_i8(D, GS, SP, a, n_wg, stream);
-    case F32 * 3 + BF16: return launch_decode_f32_bf16(D, GS, SP, a, n_wg, stream);
-    case F32 * 3 + F32: return launch_decode_f32_f32(D, GS, SP, a, n_wg, stream);
+    case I8 * 3 + I8:
+      return full ? launch_decode_i8_i8(D, GS, SP, a, n_wg, stream) : launch_decode_i8_i8_pad(D, GS, SP, a, n_wg, stream);
+    case I8 * 3 + BF16:
+      return full ? launch_decode_i8_bf16(D, GS, SP, a, n_wg, stream) : launch_decode_i8_bf16_pad(D, GS, SP, a, n_wg, stream);
+    case I8 * 3 + F32:
+      return full ? launch_decode_i8_f32(D, GS, SP, a, n_wg, stream) : launch_decode_i8_f32_pad(D, GS, SP, a, n_wg, stream);
+    case BF16 * 3 + I8:
+      return full ? launch_decode_bf16_i8(D, GS, SP, a, n_wg, stream) : launch_decode_bf16_i8_pad(D, GS, SP, a, n_wg, stream);
+    case BF16 * 3 + BF16:
+      return full ? launch_decode_bf16_bf16(D, GS, SP, a, n_wg, stream) : launch_decode_bf16_bf16_pad(D, GS, SP, a, n_wg, stream);
+    case BF16 * 3 + F32:
+      return full ? launch_decode_bf16_f32(D, GS, SP, a, n_wg, stream) : launch_decode_bf16_f32_pad(D, GS, SP, a, n_wg, stream);
+    case F32 * 3 + I8:
+      return full ? launch_decode_f32_i8(D, GS, SP, a, n_wg, stream) : launch_decode_f32_i8_pad(D, GS, SP, a, n_wg, stream);
+    case F32 * 3 + BF16:
+      return full ? launch_decode_f32_bf16(D, GS, SP, a, n_wg, stream) : launch_decode_f32_bf16_pad(D, GS, SP, a, n_wg, stream);
+    case F32 * 3 + F32:
+      return full ? launch_decode_f32_f32(D, GS, SP, a, n_wg, stream) : launch_decode_f32_f32_pad(D, GS, SP, a, n_wg, stream);
     default: return -1;
   }
+}
+int resident_decode(int D, int GS, int SP, int kf, int vf, bool full) {
+  switch (kf * 3 + vf) {
+    case I8 * 3 + I8: return full ? resident_decode_i8_i8(D, GS, SP) : resident_decode_i8_i8_pad(D, GS, SP);
+    case I8 * 3 + BF16: return full ? resident_decode_i8_bf16(D, GS, SP) : resident_decode_i8_bf16_pad(D, GS, SP);
+    case I8 * 3 + F32: return full ? resident_decode_i8_f32(D, GS, SP) : resident_decode_i8_f32_pad(D, GS, SP);
+    case BF16 * 3 + I8: return full ? resident_decode_bf16_i8(D, GS, SP) : resident_decode_bf16_i8_pad(D, GS, SP);
+    case BF16 * 3 + BF16: return full ? resident_decode_bf16_bf16(D, GS, SP) : resident_decode_bf16_bf16_pad(D, GS, SP);
+    case BF16 * 3 + F32: return full ? resident_decode_bf16_f32(D, GS, SP) : resident_decode_bf16_f32_pad(D, GS, SP);
+    case F32 * 3 + I8: return full ? resident_decode_f32_i8(D, GS, SP) : resident_decode_f32_i8_pad(D, GS, SP);
+    case F32 * 3 + BF16: return full ? resident_decode_f32_bf16(D, GS, SP) : resident_decode_f32_bf16_pad(D, GS, SP);
+    case F32 * 3 + F32: return full ? resident_decode_f32_f32(D, GS, SP) : resident_decode_f32_f32_pad(D, GS, SP);
+    default: return -1;
+  }
+}
+int stream_device(hipStream_t stream, int *dev) {
+  if (stream == nullptr) return hipGetDevice(dev) == hipSuccess ? CODEC_OK : CODEC_ERR_HIP;
+  hipDevice_t d = 0;
+  if (hipStreamGetDevice(stream, &d) != hipSuccess) return CODEC_ERR_HIP;
+  *dev = (int)d;
+  return CODEC_OK;
 }
 }  // namespace cdattn
 
@@ -221,9 +274,8 @@ int launch_append_step(codec_stream *k, codec_stream *v, const void *k_new, cons
   }
   A.t = k->n_tail;
   A.complete = complete;
-  fill_M(k->fmt, k->block, k->keep, A.M);
   (void)hipGetLastError();
-  if (launch_append(k->head_dim, A, k->batch * k->heads, stream) != 0) return CODEC_ERR_HIP;
+  if (launch_append(A, k->batch * k->heads, stream) != 0) return CODEC_ERR_HIP;
   for (codec_stream *s : {k, v}) {
     if (complete) {
       s->n_blocks += 1;
@@ -238,11 +290,11 @@ int launch_append_step(codec_stream *k, codec_stream *v, const void *k_new, cons
 }  // namespace
 
 namespace cdattn {
-// Validation of a decode call apart from its workspace (no HIP call); fills
-// the plan.
+// Validation of a decode call apart from its workspace; fills the plan for
+// the device of `stream` (no launch).
 int decode_check_args(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
                       const codec_stream *v, float scale, const void *out, const int64_t out_stride[2],
-                      int32_t out_dtype, DecodePlan *p) {
+                      int32_t out_dtype, hipStream_t stream, DecodePlan *p) {
   if (!q || !q_stride || !out || !out_stride) return CODEC_ERR_NULL;
   int rc = check_decode(k, v, Hq);
   if (rc) return rc;
@@ -251,18 +303,21 @@ int decode_check_args(const void *q, const int64_t q_stride[2], int64_t Hq, cons
   if (!aligned16(q) || q_stride[0] < 0 || q_stride[1] < 0 || q_stride[0] % 8 || q_stride[1] % 8)
     return CODEC_ERR_SHAPE;
   if (out_stride[0] < 0 || out_stride[1] < 0) return CODEC_ERR_SHAPE;
-  *p = make_plan(k, v, Hq);
+  int dev = -1;
+  if (stream_device(stream, &dev) != CODEC_OK) dev = -1;
+  *p = make_plan(k, v, Hq, dev);
   if (!p->ok) return CODEC_ERR_UNSUPPORTED;
   return CODEC_OK;
 }
 }  // namespace cdattn
 
 namespace {
-// Validation of codec_decode_attention (no HIP call); fills the plan.
+// Validation of codec_decode_attention (no launch); fills the plan.
 int check_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
                       const codec_stream *v, float scale, const void *out, const int64_t out_stride[2],
-                      int32_t out_dtype, const void *workspace, size_t workspace_bytes, DecodePlan *p) {
-  const int rc = decode_check_args(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, p);
+                      int32_t out_dtype, const void *workspace, size_t workspace_bytes, hipStream_t stream,
+                      DecodePlan *p) {
+  const int rc = decode_check_args(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, stream, p);
   if (rc) return rc;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < p->bytes)
     return CODEC_ERR_WORKSPACE;
@@ -294,6 +349,7 @@ int launch_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, con
   a.kf = row_fmt(k->fmt);
   a.vf = row_fmt(v->fmt);
   a.png = k->fmt == CODEC_PNG ? 1 : 0;
+  a.Dm = k->head_dim;
   a.kraw = k->raw_dtype;
   a.vraw = v->raw_dtype;
   a.H = (int32_t)k->heads;
@@ -324,7 +380,8 @@ int launch_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, con
   a.part_ml = reinterpret_cast<float *>(ws + p.off_ml);
   a.part_acc = reinterpret_cast<float *>(ws + p.off_acc);
   (void)hipGetLastError();
-  const int lr = launch_decode(k->head_dim, p.GS, p.SP, row_fmt(k->fmt), row_fmt(v->fmt), a, p.n_wg, stream);
+  const int DP = pad_dim(k->head_dim);
+  const int lr = launch_decode(DP, p.GS, p.SP, row_fmt(k->fmt), row_fmt(v->fmt), DP == k->head_dim, a, p.n_wg, stream);
   if (lr < 0) return CODEC_ERR_UNSUPPORTED;
   if (lr > 0) return CODEC_ERR_HIP;
   return CODEC_OK;
@@ -353,7 +410,7 @@ int codec_basis(int32_t R, int32_t S, float *A_host) {
   if (!A_host) return CODEC_ERR_NULL;
   if (R < 1 || R > CODEC_MAX_BLOCK || S < 1 || S > R || S > CODEC_MAX_KEEP) return CODEC_ERR_SHAPE;
   for (int i = 0; i < R; ++i)
-    for (int j = 0; j < S; ++j) A_host[i * S + j] = (float)basis_entry(R, j, i);
+    for (int j = 0; j < S; ++j) A_host[i * S + j] = kBasisHost[basis_index(R, j, i)];
   return CODEC_OK;
 }
 
@@ -375,20 +432,17 @@ int codec_encode_blocks(codec_stream *s, const void *x, const int64_t x_stride[3
       if (x_stride[i] < 0 || x_stride[i] % 8 != 0) return CODEC_ERR_SHAPE;
   }
   if (T == 0) return CODEC_OK;
-  EncodeLaunch L;
-  memset(&L, 0, sizeof(L));
-  L.e = stream_encode_args(s);
-  L.e.src0 = x;
-  L.e.s0_b = x_stride[0];
-  L.e.s0_h = x_stride[1];
-  L.e.s0_t = x_stride[2];
-  L.e.src1 = x;
-  L.e.split_i = (int32_t)R;
-  L.e.n_new = n_new;
-  L.e.n_copy = t;
-  fill_M(s->fmt, (int)R, s->keep, L.M);
+  EncodeArgs e = stream_encode_args(s);
+  e.src0 = x;
+  e.s0_b = x_stride[0];
+  e.s0_h = x_stride[1];
+  e.s0_t = x_stride[2];
+  e.src1 = x;
+  e.split_i = (int32_t)R;
+  e.n_new = n_new;
+  e.n_copy = t;
   (void)hipGetLastError();
-  rc = launch_encode(s->head_dim, L, s->batch * s->heads, stream);
+  rc = launch_encode(e, s->batch * s->heads, stream);
   if (rc < 0) return CODEC_ERR_UNSUPPORTED;   // grid beyond 2^31 - 1 workgroups
   if (rc > 0) return CODEC_ERR_HIP;
   s->n_blocks += n_new;
@@ -407,7 +461,9 @@ int codec_decode_workspace_bytes(const codec_stream *k, const codec_stream *v, i
   if (!bytes) return CODEC_ERR_NULL;
   const int rc = check_decode(k, v, Hq);
   if (rc) return rc;
-  const DecodePlan p = make_plan(k, v, Hq);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const DecodePlan p = make_plan(k, v, Hq, dev);
   if (!p.ok) return CODEC_ERR_UNSUPPORTED;
   *bytes = p.bytes;
   return CODEC_OK;
@@ -418,7 +474,7 @@ int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
                            int32_t out_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream) {
   DecodePlan p;
   const int rc = check_decode_call(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, workspace,
-                                   workspace_bytes, &p);
+                                   workspace_bytes, stream, &p);
   if (rc) return rc;
   return launch_decode_call(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, workspace, p, nullptr,
                             nullptr, nullptr, nullptr, stream);
@@ -444,7 +500,7 @@ int codec_decode_attention_append(const void *q, const int64_t q_stride[2], int6
   }
   DecodePlan p;
   rc = check_decode_call(q, q_stride, Hq, &k2, &v2, scale, out, out_stride, out_dtype, workspace,
-                         workspace_bytes, &p);
+                         workspace_bytes, stream, &p);
   if (rc) return rc;
   if (complete) {
     // the token completes a block: archive it, then attend.  If the decode
@@ -482,14 +538,13 @@ ViewArgs stream_view_args(const codec_stream *s) {
   a.tail = s->tail;
   a.rf = row_fmt(s->fmt);
   a.raw = s->raw_dtype;
+  a.png = s->fmt == CODEC_PNG ? 1 : 0;
   a.R = s->block;
   a.S = s->keep;
   a.D = s->head_dim;
   a.H = s->heads;
   a.BH = s->batch * s->heads;
   a.cap = s->capacity;
-  for (int i = 0; i < s->block; ++i)
-    for (int j = 0; j < s->keep; ++j) a.A[i * s->keep + j] = synth_entry(s->fmt, s->block, i, j);
   return a;
 }
 

@@ -26,6 +26,7 @@
 // (b, h, block) per group of D/8 lanes, the basis staged in LDS as fp64.
 // Writes of R tokens per block dominate the traffic.
 
+#include "basis_dev.h"
 #include "internal.h"
 
 namespace cdattn {
@@ -114,26 +115,30 @@ struct RowWords {
 
 // Grid: x = chunks of items, y = kv head, z = batch row.  Item k of (b, h) is
 // block blk0 + k (decoded) for k < nblk; item nblk copies the raw tail when
-// n_copy > 0.  A group of D/EPL lanes takes one item, EPL elements each.
+// n_copy > 0.  A group of D/EPL lanes takes one item, EPL elements each; the
+// threads past the last whole group (when D/EPL does not divide 256) take no
+// item.
 template <int RF, int SP, int EPL>
 __global__ __launch_bounds__(256) void view_kernel(ViewArgs a) {
   __shared__ double sA[kMaxR * SP];   // A[i][j] as fp64, zero past column S
+  constexpr int NAU = (kMaxR * SP + 255) / 256;   // basis entries staged per thread
   const int lpi = a.D / EPL;                     // lanes per item
-  const int64_t k = (int64_t)blockIdx.x * (256 / lpi) + threadIdx.x / lpi;
+  const int ipw = 256 / lpi;                     // items per workgroup
+  const int64_t k = (int)threadIdx.x < ipw * lpi ? (int64_t)blockIdx.x * ipw + threadIdx.x / lpi : INT64_MAX;
   const int d0 = EPL * (threadIdx.x % lpi);
   const int64_t h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = b * a.H + h;
   const int R = a.R, S = a.S;
-  // The basis entries (two per thread cover R * SP <= 512) and the block's
-  // coefficient rows are requested together (rows past S repeat row S-1, in
-  // range, and are zeroed below); the basis is staged once its words land.
+  // The basis entries (from the table) and the block's coefficient rows are
+  // requested together (rows past S repeat row S-1, in range, and are zeroed
+  // below); the basis is staged once its words land.
   const int nA = R * SP;
-  float av[2];
+  float av[NAU];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < NAU; ++u) {
     const int t = (int)threadIdx.x + 256 * u, tc = t < nA ? t : nA - 1;
     const int j = tc % SP;
-    av[u] = a.A[(tc / SP) * S + (j < S ? j : 0)];
+    av[u] = synthesis_entry(a.png, R, tc / SP, j < S ? j : 0);
   }
   RowWords<RF, EPL> rw[SP];
   if (k < a.nblk) {
@@ -142,40 +147,64 @@ __global__ __launch_bounds__(256) void view_kernel(ViewArgs a) {
     for (int j = 0; j < SP; ++j) rw[j].load(a.rows, a.scales, row0 + (j < S ? j : S - 1), a.D, d0);
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < NAU; ++u) {
     const int t = (int)threadIdx.x + 256 * u;
     if (t < nA) sA[t] = t % SP < S ? (double)av[u] : 0.0;
   }
   __syncthreads();
   if (k < a.nblk) {
-    double c[SP][EPL];
-#pragma unroll
-    for (int j = 0; j < SP; ++j) {
-      rw[j].values(c[j]);
-      if (j >= S) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) c[j][e] = 0.0;
-      }
-    }
     const int64_t tbase = b * a.o_sb + h * a.o_sh + (k * R + a.o_t0) * a.o_st + d0;
-#pragma unroll 2
-    for (int i = 0; i < a.tok_limit; ++i) {
-#pragma clang fp contract(off)   // products and sums rounded separately (the contract)
-      double x[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) x[e] = 0.0;
-      // Columns j >= S add 0 * 0 = +0.0, which leaves x unchanged: x starts
-      // at +0.0 and round-to-nearest sums never produce -0.0 from it.
+    if constexpr (SP <= 16) {
+      double c[SP][EPL];
 #pragma unroll
       for (int j = 0; j < SP; ++j) {
-        const double Aij = sA[i * SP + j];
+        rw[j].values(c[j]);
+        if (j >= S) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] = x[e] + Aij * c[j][e];
+          for (int e = 0; e < EPL; ++e) c[j][e] = 0.0;
+        }
       }
-      float o[EPL];
+#pragma unroll 2
+      for (int i = 0; i < a.tok_limit; ++i) {
+#pragma clang fp contract(off)   // products and sums rounded separately (the contract)
+        double x[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = (float)x[e];
-      store_out<EPL>(a.dst, tbase + i * a.o_st, a.out, o);
+        for (int e = 0; e < EPL; ++e) x[e] = 0.0;
+        // Columns j >= S add 0 * 0 = +0.0, which leaves x unchanged: x starts
+        // at +0.0 and round-to-nearest sums never produce -0.0 from it.
+#pragma unroll
+        for (int j = 0; j < SP; ++j) {
+          const double Aij = sA[i * SP + j];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) x[e] = x[e] + Aij * c[j][e];
+        }
+        float o[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] = (float)x[e];
+        store_out<EPL>(a.dst, tbase + i * a.o_st, a.out, o);
+      }
+    } else {
+      // more than 16 kept rows: the rows stay as stored words and each is
+      // widened where it is used (the same products and sums, in the same
+      // order, without holding SP x EPL doubles)
+      for (int i = 0; i < a.tok_limit; ++i) {
+#pragma clang fp contract(off)   // products and sums rounded separately (the contract)
+        double x[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x[e] = 0.0;
+#pragma unroll
+        for (int j = 0; j < SP; ++j) {
+          double cj[EPL];
+          rw[j].values(cj);
+          const double Aij = sA[i * SP + j];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) x[e] = x[e] + Aij * (j < S ? cj[e] : 0.0);
+        }
+        float o[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] = (float)x[e];
+        store_out<EPL>(a.dst, tbase + i * a.o_st, a.out, o);
+      }
     }
   } else if (k == a.nblk && a.n_copy > 0) {
     const int64_t src = bh * (int64_t)R * a.D + d0;
@@ -189,7 +218,10 @@ __global__ __launch_bounds__(256) void view_kernel(ViewArgs a) {
 }
 
 // Batch gather: unit u = (i, h) of the destination copies the archived rows,
-// their scales and the R tail slots of source row idx[i], head h.
+// their scales and the R tail slots of source row idx[i], head h, in words
+// of W bytes (16, or 8 when a slab of int8 rows with head_dim % 16 == 8 and
+// an odd row count is not a multiple of 16 bytes).
+template <typename W>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs g) {
   const int64_t u = blockIdx.y;                          // i * H + h within this launch
   const int64_t i = g.i0 + u / g.H, h = u % g.H;
@@ -197,10 +229,10 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs g) {
   const int64_t s_bh = sb * g.H + h, d_bh = i * g.H + h;
   const int64_t stride = (int64_t)gridDim.x * 256;
   const int64_t t0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  {   // rows: the first n_blocks*S*D*eb bytes of the (b, h) slab, 16 bytes per lane
-    const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const char *>(g.src_rows) + s_bh * g.slab_bytes);
-    uint4 *dst = reinterpret_cast<uint4 *>(static_cast<char *>(g.dst_rows) + d_bh * g.dst_slab_bytes);
-    for (int64_t k = t0; k < g.row_bytes / 16; k += stride) dst[k] = src[k];
+  {   // rows: the first n_blocks*S*D*eb bytes of the (b, h) slab
+    const W *src = reinterpret_cast<const W *>(static_cast<const char *>(g.src_rows) + s_bh * g.slab_bytes);
+    W *dst = reinterpret_cast<W *>(static_cast<char *>(g.dst_rows) + d_bh * g.dst_slab_bytes);
+    for (int64_t k = t0; k < g.row_bytes / (int64_t)sizeof(W); k += stride) dst[k] = src[k];
   }
   if (g.src_scales) {
     const float *src = g.src_scales + s_bh * g.scale_slab;
@@ -208,9 +240,9 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs g) {
     for (int64_t k = t0; k < g.n_scales; k += stride) dst[k] = src[k];
   }
   {   // tail: all R slots
-    const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const char *>(g.src_tail) + s_bh * g.tail_bytes);
-    uint4 *dst = reinterpret_cast<uint4 *>(static_cast<char *>(g.dst_tail) + d_bh * g.tail_bytes);
-    for (int64_t k = t0; k < g.tail_bytes / 16; k += stride) dst[k] = src[k];
+    const W *src = reinterpret_cast<const W *>(static_cast<const char *>(g.src_tail) + s_bh * g.tail_bytes);
+    W *dst = reinterpret_cast<W *>(static_cast<char *>(g.dst_tail) + d_bh * g.tail_bytes);
+    for (int64_t k = t0; k < g.tail_bytes / (int64_t)sizeof(W); k += stride) dst[k] = src[k];
   }
 }
 
@@ -221,6 +253,7 @@ int launch_view_rf(int SP, const ViewArgs &a, dim3 grid, hipStream_t stream) {
     case 4: hipLaunchKernelGGL((view_kernel<RF, 4, 8>), grid, dim3(256), 0, stream, a); break;
     case 8: hipLaunchKernelGGL((view_kernel<RF, 8, 8>), grid, dim3(256), 0, stream, a); break;
     case 16: hipLaunchKernelGGL((view_kernel<RF, 16, 4>), grid, dim3(256), 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((view_kernel<RF, 32, 4>), grid, dim3(256), 0, stream, a); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;
@@ -229,8 +262,8 @@ int launch_view_rf(int SP, const ViewArgs &a, dim3 grid, hipStream_t stream) {
 }  // namespace
 
 int launch_view(const ViewArgs &a, hipStream_t stream) {
-  const int SP = a.S <= 2 ? 2 : (a.S <= 4 ? 4 : (a.S <= 8 ? 8 : 16));
-  const int EPL = SP == 16 ? 4 : 8;
+  const int SP = a.S <= 2 ? 2 : (a.S <= 4 ? 4 : (a.S <= 8 ? 8 : (a.S <= 16 ? 16 : 32)));
+  const int EPL = SP >= 16 ? 4 : 8;
   const int64_t items = a.nblk + (a.n_copy > 0 ? 1 : 0);   // per (b, h)
   const int64_t per_wg = 256 / (a.D / EPL);
   const int64_t gx = (items + per_wg - 1) / per_wg;
@@ -252,7 +285,11 @@ int launch_gather(const GatherArgs &g, int64_t n_units, hipStream_t stream) {
   int64_t gx = (work + 255) / 256;
   if (gx < 1) gx = 1;
   if (gx > 64) gx = 64;
-  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)gx, (unsigned)n_units), dim3(256), 0, stream, g);
+  const bool w16 = (g.slab_bytes | g.dst_slab_bytes | g.row_bytes | g.tail_bytes) % 16 == 0;
+  if (w16)
+    hipLaunchKernelGGL(gather_kernel<uint4>, dim3((unsigned)gx, (unsigned)n_units), dim3(256), 0, stream, g);
+  else
+    hipLaunchKernelGGL(gather_kernel<uint2>, dim3((unsigned)gx, (unsigned)n_units), dim3(256), 0, stream, g);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -39,6 +39,7 @@
 
 #include <type_traits>
 
+#include "basis_dev.h"
 #include "internal.h"
 
 namespace cdattn {
@@ -200,58 +201,80 @@ struct TileBuf {
   VBuf<D, GS, KF, VF> v;
 };
 
+// One tile of coefficient rows: its K and V rows and scales, its row count,
+// and the head_dim dm of the rows in memory (their pitch; the kernel's
+// compute width D is dm rounded up to 64, 128 or 256).
 struct TileRef {
   const char *k;
   const char *v;
   const float *ks;
   const float *vs;
   int nrows;
+  int dm;
 };
+
+constexpr uint32_t kOutOfRange = 0x40000000u;   // a buffer offset past every range: the load reads zeros
 
 template <int D, int GS, int KF, int VF>
 __device__ __forceinline__ void issue_k(TileBuf<D, GS, KF, VF> &B, const TileRef &T, int lane) {
   using C = Cfg<D, GS, KF, VF>;
-  const rsrc_t rk = make_rsrc(T.k, (uint32_t)T.nrows * D * C::EBK);
+  const int dm = T.dm;
+  const rsrc_t rk = make_rsrc(T.k, (uint32_t)T.nrows * dm * C::EBK);
   if constexpr (C::KM) {
-    const uint32_t vk = (uint32_t)((lane % 16) * D + 16 * (lane / 16));
+    // columns past dm read the next row's codes (or zeros past the tile):
+    // they meet zero query digits
+    const uint32_t vk = (uint32_t)((lane % 16) * dm + 16 * (lane / 16));
 #pragma unroll
     for (int rg = 0; rg < C::RG; ++rg)
 #pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) B.k.k[rg][kk] = bload128(rk, vk + 64 * kk, rg * 16 * D);
+      for (int kk = 0; kk < C::KK; ++kk) B.k.k[rg][kk] = bload128(rk, vk + 64 * kk, rg * 16 * dm);
     const rsrc_t rs = make_rsrc(T.ks, (uint32_t)T.nrows * 4);
 #pragma unroll
     for (int rg = 0; rg < C::RG; ++rg) B.k.ks[rg] = bloadf(rs, 4 * (lane % 16), 64 * rg);
   } else {
+    // 16 columns per lane in KQ loads of 16 / KQ columns; loads past dm read zeros
     const int rrk = lane / C::LK, ck = lane % C::LK;
-    const uint32_t vk = (uint32_t)(rrk * D + ck * 16) * C::EBK;
+    const uint32_t vk = (uint32_t)(rrk * dm + ck * 16) * C::EBK;
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s)
 #pragma unroll
-      for (int k = 0; k < C::KQ; ++k) B.k.k[s][k] = bload128(rk, vk + 16 * k, s * C::RK * D * C::EBK);
+      for (int k = 0; k < C::KQ; ++k)
+        B.k.k[s][k] = bload128(rk, ck * 16 + k * (16 / C::KQ) < dm ? vk + 16 * k : kOutOfRange, s * C::RK * dm * C::EBK);
   }
 }
 
 template <int D, int GS, int KF, int VF>
 __device__ __forceinline__ void issue_v(TileBuf<D, GS, KF, VF> &B, const TileRef &T, int lane) {
   using C = Cfg<D, GS, KF, VF>;
-  const rsrc_t rv = make_rsrc(T.v, (uint32_t)T.nrows * D * C::EBV);
+  const int dm = T.dm;
+  const rsrc_t rv = make_rsrc(T.v, (uint32_t)T.nrows * dm * C::EBV);
   if constexpr (C::VM) {
+    // chunk c of a lane: 16-byte column chunk lane % NCP of tile row
+    // lane / NCP + c * 64 / NCP (NCP chunks per row at the compute width;
+    // with dm == D that is byte 16 * (lane + 64 c) of the tile).  Chunks past
+    // the row's dm columns read zeros; an int8 chunk that straddles dm brings
+    // 8 bytes of the next row into columns past dm, which are never output.
+    constexpr int NCP = C::RBV / 16;
+    const uint32_t vbase = 16 * (lane % NCP) < dm * C::EBV
+                               ? (uint32_t)((lane / NCP) * dm * C::EBV + 16 * (lane % NCP))
+                               : kOutOfRange;
 #pragma unroll
-    for (int c = 0; c < C::VQ; ++c) B.v.v[c] = bload128(rv, 16 * lane, 1024 * c);
+    for (int c = 0; c < C::VQ; ++c) B.v.v[c] = bload128(rv, vbase, c * (64 / NCP) * dm * C::EBV);
     if constexpr (VF == I8) B.v.vs = bloadf(make_rsrc(T.vs, (uint32_t)T.nrows * 4), 4 * lane, 0);
   } else {
     const int rrv = lane / C::LV, cv = lane % C::LV;
-    const uint32_t vv = (uint32_t)(rrv * D + cv * C::EV) * C::EBV;
+    const uint32_t vv = (uint32_t)(rrv * dm + cv * C::EV) * C::EBV;
 #pragma unroll
     for (int s = 0; s < C::VSTEPS; ++s) {
       if constexpr (C::VDW % 4 == 0) {
 #pragma unroll
         for (int k = 0; k < C::VDW / 4; ++k) {
-          const uint4 t = bload128(rv, vv + 16 * k, s * C::RV * D * C::EBV);
+          const uint4 t = bload128(rv, cv * C::EV + k * (16 / C::EBV) < dm ? vv + 16 * k : kOutOfRange,
+                                   s * C::RV * dm * C::EBV);
           B.v.v[s][4 * k] = t.x; B.v.v[s][4 * k + 1] = t.y; B.v.v[s][4 * k + 2] = t.z; B.v.v[s][4 * k + 3] = t.w;
         }
       } else {
-        const uint2 t = bload64(rv, vv, s * C::RV * D * C::EBV);
+        const uint2 t = bload64(rv, cv * C::EV < dm ? vv : kOutOfRange, s * C::RV * dm * C::EBV);
         B.v.v[s][0] = t.x; B.v.v[s][1] = t.y;
       }
     }
@@ -291,28 +314,35 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // output head of the MFMA at this lane, 4*nb + lane/16.  Every wave converts
 // its own copy: the raw loads are issued before the first tile's, the
 // conversion runs once they have landed.
-template <int D, int GS>
+template <int D, int GS, bool FULL>
 struct QRegMfma {
   static constexpr int KK = D / 64, NBN = cdiv(GS, 4);
   uint4 raw[NBN][KK][2];
+  // Plain global loads (the lanes read different heads; a buffer resource
+  // per lane would have to be made uniform one head at a time), issued
+  // unconditionally so that no wait is needed until the conversion.  Rows
+  // narrower than D (FULL false): a half of 8 columns at or past a.Dm (a
+  // multiple of 8) reads column 0 instead, and the conversion takes it as
+  // zero.
   __device__ __forceinline__ void load(const DecodeArgs &a, int b, int hq0, int lane) {
     const int n = lane % 16, G = lane / 16;
 #pragma unroll
     for (int nb = 0; nb < NBN; ++nb) {
       const int g = 4 * nb + n / 4;
       const int gl = g < GS ? g : 0;   // columns of absent heads read a live one and are zeroed below
+      const uint4 *qh = reinterpret_cast<const uint4 *>(a.q + (int64_t)b * a.q_sb + (int64_t)(hq0 + gl) * a.q_sh);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (int64_t)b * a.q_sb + (int64_t)(hq0 + gl) * a.q_sh +
-                                                          64 * kk + 16 * G);
-        raw[nb][kk][0] = qp[0];
-        raw[nb][kk][1] = qp[1];
-      }
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int c = 64 * kk + 16 * G + 8 * hf;
+          raw[nb][kk][hf] = qh[FULL || c < a.Dm ? c / 8 : 0];
+        }
     }
   }
   __device__ __forceinline__ void convert(const DecodeArgs &a, int lane, uint4 (&qB)[KK][NBN],
                                           float (&cqq)[NBN]) const {
-    const int n = lane % 16, which = n % 4;
+    const int n = lane % 16, which = n % 4, G = lane / 16;
 #pragma unroll
     for (int nb = 0; nb < NBN; ++nb) {
       const bool live = 4 * nb + n / 4 < GS;
@@ -324,8 +354,9 @@ struct QRegMfma {
                                 raw[nb][kk][1].x, raw[nb][kk][1].y, raw[nb][kk][1].z, raw[nb][kk][1].w};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          qf[kk][2 * t] = live ? bf16lo(wv[t]) : 0.0f;
-          qf[kk][2 * t + 1] = live ? bf16hi(wv[t]) : 0.0f;
+          const bool in = live && (FULL || 64 * kk + 16 * G + 8 * (t / 4) < a.Dm);
+          qf[kk][2 * t] = in ? bf16lo(wv[t]) : 0.0f;
+          qf[kk][2 * t + 1] = in ? bf16hi(wv[t]) : 0.0f;
           amax = fmaxf(amax, fmaxf(fabsf(qf[kk][2 * t]), fabsf(qf[kk][2 * t + 1])));
         }
       }
@@ -574,17 +605,22 @@ __device__ __forceinline__ void rescale_mfma(float (&acc)[MBK][NBK], const float
 // fp16 pairs of the lane's 16 key elements (lane % (D/16) picks them),
 // pre-scaled per head by a power of two into fp16 range; loads issued first,
 // converted once other loads are in flight.
-template <int D, int GS>
+template <int D, int GS, bool FULL>
 struct QRegValu {
   static constexpr int LK = D / 16;
   uint4 raw[GS][2];
+  // Unconditional loads (no wait before the conversion).  Rows narrower than
+  // D (FULL false): a half of 8 columns at or past a.Dm (a multiple of 8)
+  // reads column 0 instead, and the conversion takes it as zero.
   __device__ __forceinline__ void load(const DecodeArgs &a, int b, int hq0, int lane) {
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
-      const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (int64_t)b * a.q_sb + (int64_t)(hq0 + g) * a.q_sh +
-                                                        (lane % LK) * 16);
-      raw[g][0] = qp[0];
-      raw[g][1] = qp[1];
+      const uint4 *qh = reinterpret_cast<const uint4 *>(a.q + (int64_t)b * a.q_sb + (int64_t)(hq0 + g) * a.q_sh);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int c = (lane % LK) * 16 + 8 * hf;
+        raw[g][hf] = qh[FULL || c < a.Dm ? c / 8 : 0];
+      }
     }
   }
   __device__ __forceinline__ void convert(const DecodeArgs &a, int lane, h2 (&qh)[GS][8], float (&cq)[GS]) const {
@@ -596,8 +632,9 @@ struct QRegValu {
       float amax = 0.0f;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        qf[2 * t] = bf16lo(wv[t]);
-        qf[2 * t + 1] = bf16hi(wv[t]);
+        const bool in = FULL || (lane % LK) * 16 + 8 * (t / 4) < a.Dm;
+        qf[2 * t] = in ? bf16lo(wv[t]) : 0.0f;
+        qf[2 * t + 1] = in ? bf16hi(wv[t]) : 0.0f;
         amax = fmaxf(amax, fmaxf(fabsf(qf[2 * t]), fabsf(qf[2 * t + 1])));
       }
       amax = group_red<LK, true>(amax);
@@ -716,12 +753,15 @@ struct Basis {
   static constexpr int SK = SP < 4 ? 1 : SP / 4;   // 4-coefficient steps
   float az[2][SK];   // A operand of z, token tile rt: A[16 rt + l%16][4 kk + l/16]
   float bw[2][4];    // B operand of w, token tile rt: A[16 rt + 4 (l/16) + kk][l%16]
+  float bwh[2][4];   // SP > 16: the same for coefficients 16 .. 31, A[..][16 + l%16]
   int rt_n;          // token tiles of 16: 1 if R <= 16 else 2
   // SP = 2 with R <= 8: two items per MFMA column (item half h = rows 8h ..
   // of z, coefficients 2h .. of its B operand, columns S h .. of w):
   // A operand of z, A'[l%16][l/16]; B operand of w, B'[l/16][l%16] per step
   float azp;
   float bwp[4];
+  // Operand registers from the workgroup's copy sA of the synthesis basis
+  // (entry r * SP + j, zero past row R and column S).
   __device__ __forceinline__ void load(const float *sA, int R, int S, int lane) {
     const int lo = lane % 16, hi = lane / 16;
     rt_n = R > 16 ? 2 : 1;
@@ -745,6 +785,7 @@ struct Basis {
       for (int kk = 0; kk < 4; ++kk) {
         const int r = 16 * rt + 4 * hi + kk, j = lo;
         bw[rt][kk] = (r < R && j < S) ? sA[r * SP + j] : 0.0f;
+        if constexpr (SP > 16) bwh[rt][kk] = (r < R && 16 + j < S) ? sA[r * SP + 16 + j] : 0.0f;
       }
     }
   }
@@ -756,7 +797,10 @@ struct Basis {
 #pragma unroll
       for (int kk = 0; kk < SK; ++kk) az[rt][kk] = (rt == 0 && kk == 0 && lane == 0) ? 1.0f : 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) bw[rt][kk] = (rt == 0 && kk == 0 && lane == 0) ? 1.0f : 0.0f;
+      for (int kk = 0; kk < 4; ++kk) {
+        bw[rt][kk] = (rt == 0 && kk == 0 && lane == 0) ? 1.0f : 0.0f;
+        bwh[rt][kk] = 0.0f;
+      }
     }
   }
 };
@@ -815,7 +859,7 @@ __device__ __forceinline__ void logits_any(const Basis<SP> &A, float *sw, int nb
 #pragma unroll 2
   for (int ig = 0; ig < ngroups; ++ig) {
     const bool ok = ig * 16 + col < items;
-    v4f w = {0.0f, 0.0f, 0.0f, 0.0f};
+    v4f w = {0.0f, 0.0f, 0.0f, 0.0f}, wh = w;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       if (rt < A.rt_n) {
@@ -828,14 +872,28 @@ __device__ __forceinline__ void logits_any(const Basis<SP> &A, float *sw, int nb
         }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) w = __builtin_amdgcn_mfma_f32_16x16x4f32(p[kk], A.bw[rt][kk], w, 0, 0, 0);
+        if constexpr (SP > 16) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) wh = __builtin_amdgcn_mfma_f32_16x16x4f32(p[kk], A.bwh[rt][kk], wh, 0, 0, 0);
+        }
       }
     }
     // lane (hi, j = col) holds w of items ig*16 + 4 hi + i, coefficient j
+    // (and coefficient 16 + j in wh)
     if (col < S) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int it = ig * 16 + 4 * hi + i;
         if (it < items) sw[(it % GS) * SWR + (it / GS) * S + col] = w[i];
+      }
+    }
+    if constexpr (SP > 16) {
+      if (16 + col < S) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int it = ig * 16 + 4 * hi + i;
+          if (it < items) sw[(it % GS) * SWR + (it / GS) * S + 16 + col] = wh[i];
+        }
       }
     }
   }
@@ -921,6 +979,20 @@ __device__ __forceinline__ void logits(const Basis<SP> &A, float *sw, int nb, in
         const int it = ig * 16 + 4 * hi + i;
         const bool ok = col < S && it < items;
         sw[ok ? (it % GS) * SWR + (it / GS) * S + col : GS * SWR + lane] = (w0[i] + w1[i]) + (w2[i] + w3[i]);
+      }
+      if constexpr (SP > 16) {
+        // coefficients 16 .. 31
+        w0 = w1 = w2 = w3 = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        w0 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[0], A.bwh[0][0], w0, 0, 0, 0);
+        w1 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[1], A.bwh[0][1], w1, 0, 0, 0);
+        w2 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[2], A.bwh[0][2], w2, 0, 0, 0);
+        w3 = __builtin_amdgcn_mfma_f32_16x16x4f32(p[3], A.bwh[0][3], w3, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int it = ig * 16 + 4 * hi + i;
+          const bool ok = 16 + col < S && it < items;
+          sw[ok ? (it % GS) * SWR + (it / GS) * S + 16 + col : GS * SWR + lane] = (w0[i] + w1[i]) + (w2[i] + w3[i]);
+        }
       }
     }
   }
@@ -1117,11 +1189,15 @@ struct TailPass {
   // read zeros), so the first chunk of both costs one round trip.
   static constexpr int BUDGET = GS >= 8 ? 8 : 16;
   static constexpr int PK = cmin(kMaxR / RK, cmax(1, BUDGET / (4 * EBK))), PV = cmin(kMaxR / RV, cmax(1, BUDGET / VDW));
-  static constexpr uint32_t kOut = 0x40000000u;   // an offset past every range: the load reads zeros
+  static constexpr uint32_t kOut = kOutOfRange;
+  // 16-byte loads per row step: EBK for a key row's 16 columns, NVL for a
+  // value row's EV columns
+  static constexpr int NVL = VDW % 4 == 0 ? VDW / 4 : 1;
   const void *kt, *vt;
-  int nt, t_new, rrk, ck, rrv, cv;
+  int nt, t_new, rrk, ck, rrv, cv, dm;
   rsrc_t rk, rv;
-  uint32_t offk, offv;
+  // per load: the lane's offset, or kOut for columns at or past dm
+  uint32_t offk[EBK], offv[NVL];
   // The new token's rows, held by the lanes whose row in a step it is
   // (zeros in every other lane), merged into its step's registers below.
   uint4 knw[EBK];
@@ -1133,7 +1209,7 @@ struct TailPass {
 #pragma unroll
     for (int s = 0; s < PK; ++s)
 #pragma unroll
-      for (int k = 0; k < EBK; ++k) kb[s][k] = bload128(rk, offk + 16 * k, (r00 + s * RK) * D * EBK);
+      for (int k = 0; k < EBK; ++k) kb[s][k] = bload128(rk, offk[k], (r00 + s * RK) * dm * EBK);
   }
   __device__ __forceinline__ void load_v(int r00) {
 #pragma unroll
@@ -1141,15 +1217,15 @@ struct TailPass {
       if constexpr (VDW % 4 == 0) {
 #pragma unroll
         for (int k = 0; k < VDW / 4; ++k) {
-          const uint4 t = bload128(rv, offv + 16 * k, (r00 + s * RV) * D * EBV);
+          const uint4 t = bload128(rv, offv[k], (r00 + s * RV) * dm * EBV);
           vb[s][4 * k] = t.x; vb[s][4 * k + 1] = t.y; vb[s][4 * k + 2] = t.z; vb[s][4 * k + 3] = t.w;
         }
       } else if constexpr (VDW == 2) {
-        const uint2 t = bload64(rv, offv, (r00 + s * RV) * D * EBV);
+        const uint2 t = bload64(rv, offv[0], (r00 + s * RV) * dm * EBV);
         vb[s][0] = t.x; vb[s][1] = t.y;
       } else {
         static_assert(VDW == 1, "value words per lane: 1, 2 or a multiple of 4");
-        vb[s][0] = __builtin_bit_cast(uint32_t, bloadf(rv, offv, (r00 + s * RV) * D * EBV));
+        vb[s][0] = __builtin_bit_cast(uint32_t, bloadf(rv, offv[0], (r00 + s * RV) * dm * EBV));
       }
     }
   }
@@ -1177,23 +1253,29 @@ struct TailPass {
   }
 
   __device__ __forceinline__ void issue(const void *kt_, const void *vt_, int nt_, const void *kn, const void *vn,
-                                        int t_new_, int lane) {
+                                        int t_new_, int dm_, int lane) {
     kt = kt_;
     vt = vt_;
     nt = nt_;
     t_new = t_new_;
+    dm = dm_;
     const int t_old = t_new >= 0 ? t_new : nt;   // rows held by the tail slab
-    rk = make_rsrc(kt, (uint32_t)t_old * D * EBK);
-    rv = make_rsrc(vt, (uint32_t)t_old * D * EBV);
+    rk = make_rsrc(kt, (uint32_t)t_old * dm * EBK);
+    rv = make_rsrc(vt, (uint32_t)t_old * dm * EBV);
     rrk = lane / LK;
     ck = lane % LK;
     rrv = lane / LV;
     cv = lane % LV;
-    offk = (uint32_t)(rrk * D + ck * 16) * EBK;
-    offv = (uint32_t)(rrv * D + cv * EV) * EBV;
+#pragma unroll
+    for (int k = 0; k < EBK; ++k)
+      offk[k] = ck * 16 + k * (16 / EBK) < dm ? (uint32_t)(rrk * dm + ck * 16) * EBK + 16 * k : kOut;
+#pragma unroll
+    for (int k = 0; k < NVL; ++k)
+      offv[k] = cv * EV + k * (16 / EBV) < dm ? (uint32_t)(rrv * dm + cv * EV) * EBV + 16 * k : kOut;
     {
-      const rsrc_t rkn = make_rsrc(kn, t_new >= 0 ? (uint32_t)(D * EBK) : 0u);
-      const rsrc_t rvn = make_rsrc(vn, t_new >= 0 ? (uint32_t)(D * EBV) : 0u);
+      // the new token's range ends at its dm columns: columns past it read zeros
+      const rsrc_t rkn = make_rsrc(kn, t_new >= 0 ? (uint32_t)(dm * EBK) : 0u);
+      const rsrc_t rvn = make_rsrc(vn, t_new >= 0 ? (uint32_t)(dm * EBV) : 0u);
       const uint32_t onk = t_new >= 0 && rrk == t_new % RK ? (uint32_t)(ck * 16) * EBK : kOut;
       const uint32_t onv = t_new >= 0 && rrv == t_new % RV ? (uint32_t)(cv * EV) * EBV : kOut;
 #pragma unroll
@@ -1220,19 +1302,22 @@ struct TailPass {
                                           float (&m_u)[GS], float &m_lane, float &l_lane, float (&acc)[GS][EV],
                                           float (&alpha)[GS], Prep &&prep) {
     merge_k(0);
-    // the new token's rows into tail slot t_new (the lanes that hold it)
+    // the new token's rows into tail slot t_new (the lanes that hold it;
+    // columns below dm only)
     if (store_new) {
       if (rrk == t_new % RK) {
 #pragma unroll
         for (int k = 0; k < EBK; ++k)
-          *reinterpret_cast<uint4 *>(static_cast<char *>(const_cast<void *>(kt)) +
-                                     (size_t)(t_new * D + ck * 16) * EBK + 16 * k) = knw[k];
+          if (ck * 16 + k * (16 / EBK) < dm)
+            *reinterpret_cast<uint4 *>(static_cast<char *>(const_cast<void *>(kt)) +
+                                       (size_t)(t_new * dm + ck * 16) * EBK + 16 * k) = knw[k];
       }
       if (rrv == t_new % RV) {
         uint32_t *dst = reinterpret_cast<uint32_t *>(static_cast<char *>(const_cast<void *>(vt)) +
-                                                     (size_t)(t_new * D + cv * EV) * EBV);
+                                                     (size_t)(t_new * dm + cv * EV) * EBV);
 #pragma unroll
-        for (int k = 0; k < VDW; ++k) dst[k] = vnw[k];
+        for (int k = 0; k < VDW; ++k)
+          if (cv * EV + (4 * (k / 4)) * (4 / EBV) < dm) dst[k] = vnw[k];
       }
     }
     prep();   // the query in the VALU layout, its loads issued before the tail's
@@ -1261,18 +1346,21 @@ struct TailPass {
 
 template <int D, int GS, int SP, int SWR, int RAWK, int RAWV, int EV, typename Prep>
 __device__ __forceinline__ void tail_pass(const void *kt, const void *vt, int nt, const void *kn, const void *vn,
-                                          int t_new, bool store_new, int lane, h2 (&qh)[GS][8],
+                                          int t_new, int dm, bool store_new, int lane, h2 (&qh)[GS][8],
                                           const float (&cq)[GS], float *sw, float (&m_u)[GS], float &m_lane,
                                           float &l_lane, float (&acc)[GS][EV], float (&alpha)[GS], Prep &&prep) {
   TailPass<D, GS, SP, SWR, RAWK, RAWV, EV> tp;
-  tp.issue(kt, vt, nt, kn, vn, t_new, lane);
+  tp.issue(kt, vt, nt, kn, vn, t_new, dm, lane);
   tp.compute(store_new, lane, qh, cq, sw, m_u, m_lane, l_lane, acc, alpha, prep);
 }
 
 // The first tiles' addresses come as separate leading arguments (row counts
 // in 32 bits) so that they can be preloaded into scalar registers at wave
 // launch; everything else is in `a`.
-template <int D, int GS, int SP, int KF, int VF>
+//
+// FULL: the rows' head_dim a.Dm equals the compute width D (the row pitch is
+// a constant and no column needs masking); otherwise a.Dm < D, a multiple of 8.
+template <int D, int GS, int SP, int KF, int VF, bool FULL>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *krows, const char *vrows,
                                                                    const float *kscales, const float *vscales,
                                                                    int32_t k_bh_rows, int32_t v_bh_rows,
@@ -1305,6 +1393,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
   const int64_t pairq = bh * a.NQG + qg;
   const int hq0 = h * a.G + qg * GS;
   const int R = a.R, S = a.S;
+  const int dm = FULL ? D : a.Dm;   // head_dim in memory (D is the compute width)
 
   const WL L(lds_raw + wave * WL::BYTES);
   Basis<SP> bas;
@@ -1332,48 +1421,63 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
   const int64_t r1s = r0s + chunk_rows < n_rows ? r0s + chunk_rows : n_rows;
   const int nrs = r1s > r0s ? (int)(r1s - r0s) : 0;
   const int ntiles = (nrs + tile_rows - 1) / tile_rows;
-  const int64_t k_bh = bh * k_bh_rows, v_bh = bh * v_bh_rows;
+  // The split's first rows (tile t of the split starts t * tile_rows rows
+  // later), computed once so that few uniform values stay live in the loop.
   // Tiles past the split's end are empty (zero rows): their loads are out of
   // range and return zeros without touching memory, so every buffer is
   // re-requested unconditionally and the number of loads in flight is the
   // same on every path (the compiler's wait counts stay exact).
+  const int64_t k0 = bh * k_bh_rows + r0s, v0 = bh * v_bh_rows + r0s;
+  const char *kw = krows + k0 * dm * C::EBK;
+  const char *vw = vrows + v0 * dm * C::EBV;
+  const float *ksw = KF == I8 ? kscales + k0 : nullptr;
+  const float *vsw = VF == I8 ? vscales + v0 : nullptr;
+  const int kstep = tile_rows * dm * C::EBK, vstep = tile_rows * dm * C::EBV;   // bytes per tile
   auto tile_ref = [&](int t) {
     TileRef T;
-    const int64_t row0 = r0s + (int64_t)t * tile_rows;
-    const int64_t left = r1s - row0;
-    T.k = krows + (k_bh + row0) * D * C::EBK;
-    T.v = vrows + (v_bh + row0) * D * C::EBV;
-    T.ks = KF == I8 ? kscales + k_bh + row0 : nullptr;
-    T.vs = VF == I8 ? vscales + v_bh + row0 : nullptr;
-    T.nrows = (int)(left < 0 ? 0 : (left < tile_rows ? left : tile_rows));
+    const int row0 = t * tile_rows;   // within the split
+    const int left = nrs - row0;
+    T.k = kw + (int64_t)t * kstep;
+    T.v = vw + (int64_t)t * vstep;
+    T.ks = KF == I8 ? ksw + row0 : nullptr;
+    T.vs = VF == I8 ? vsw + row0 : nullptr;
+    T.nrows = left < 0 ? 0 : (left < tile_rows ? left : tile_rows);
+    T.dm = dm;
     return T;
   };
 
+  // The synthesis basis from the table: A[r][j] = M[j][r] (the values the
+  // encoder and the view use), or PNG mode's cumulative sum [j <= r], entry
+  // r * SP + j of the workgroup's copy sA.  Only the threads that own an
+  // entry inside the R x S matrix read the table (a few cache lines, once per
+  // workgroup: every thread, or every lane reading its own operand entries,
+  // would queue many more requests on those lines at launch), and they do it
+  // before any other load (loads return in order).
+  constexpr int NAU = (kMaxR * SP + NT - 1) / NT;
+  float a_pre[NAU];
+#pragma unroll
+  for (int u = 0; u < NAU; ++u) {
+    const int i = tid + u * NT, r = i / SP, j = i % SP;
+    a_pre[u] = r < R && j < S ? synthesis_entry(a.png, R, r, j) : 0.0f;
+  }
   // Tiles stream through NBUF register buffers per wave.  The query loads
   // are issued before the first tile's, and the set-up work (basis, query
   // conversion) runs while the tile is in flight.
-  using QR = typename std::conditional<C::KM, QRegMfma<D, GS>, QRegValu<D, GS>>::type;
+  using QR = typename std::conditional<C::KM, QRegMfma<D, GS, FULL>, QRegValu<D, GS, FULL>>::type;
   QR qr;
   qr.load(a, b, hq0, lane);
   // NBUF register buffers per wave: the first NBUF tiles are requested at once
   TileBuf<D, GS, KF, VF> bufs[C::NBUF];
 #pragma unroll
   for (int i = 0; i < C::NBUF; ++i) issue(bufs[i], tile_ref(wave + i * W), lane);
-  // A[r][j] = c_j cos(pi (2r + 1) j / (2R)), the orthonormal DCT-II synthesis
-  // (flashcodec-kv README, "Math"), entry r * SP + j per thread, zero padded.
-  // PNG mode (README "Math", PNG item): token r = anchor + deltas 1..r, A[r][j] = [j <= r].
-  float a_arg = 0.0f;
-  if (tid < R * SP && tid % SP < S) {
-    const int r = tid / SP, j = tid % SP;
-    const float cj = j == 0 ? sqrtf(1.0f / (float)R) : sqrtf(2.0f / (float)R);
-    a_arg = a.png ? (j <= r ? 1.0f : 0.0f) : cj * cospif((float)((2 * r + 1) * j) / (float)(2 * R));
-  }
-  if (tid < kMaxR * SP) sA[tid] = a_arg;
   // weights of rows past a tile's end multiply zero data: keep them finite
   for (int i = lane; i < SWR * GS; i += 64) L.sw[i] = 0.0f;
   // bf16 value rows past the staged tile meet zero weights: keep them zero (not NaN)
   if constexpr (C::VM && VF == BF16)
     for (int i = lane; i < SWR * C::RBV / 16; i += 64) reinterpret_cast<uint4 *>(L.vl)[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int u = 0; u < NAU; ++u)
+    if (tid + u * NT < kMaxR * SP) sA[tid + u * NT] = a_pre[u];
   __syncthreads();
   bas.load(sA, R, S, lane);
   if constexpr (C::KM)
@@ -1410,15 +1514,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
   if (tail_wave) {
     // MFMA key path: the VALU-layout query is loaded here and converted once
     // the tail's own loads are in flight
-    QRegValu<D, GS> qv;
+    QRegValu<D, GS, FULL> qv;
     if constexpr (C::KM) qv.load(a, b, hq0, lane);
     auto prep = [&]() {
       if constexpr (C::KM) qv.convert(a, lane, Q.qh, Q.cq);
     };
     const int nt = a.n_tail + a.fuse_new;
     const int ebk = a.kraw == BF16 ? 2 : 4, ebv = a.vraw == BF16 ? 2 : 4;
-    const char *kt = static_cast<const char *>(a.ktail) + bh * (int64_t)R * D * ebk;
-    const char *vt = static_cast<const char *>(a.vtail) + bh * (int64_t)R * D * ebv;
+    const char *kt = static_cast<const char *>(a.ktail) + bh * (int64_t)R * dm * ebk;
+    const char *vt = static_cast<const char *>(a.vtail) + bh * (int64_t)R * dm * ebv;
     // a fused new token: row n_tail of the tail, stored to its slot by query group 0
     const int t_new = a.fuse_new ? a.n_tail : -1;
     const bool store_new = a.fuse_new && qg == 0;
@@ -1428,16 +1532,16 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
     auto run = [&](auto &tacc) {
       constexpr int E = sizeof(tacc[0]) / sizeof(float);
       if (a.kraw == BF16 && a.vraw == BF16)
-        tail_pass<D, GS, SP, SWR, BF16, BF16, E>(kt, vt, nt, kn, vn, t_new, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
+        tail_pass<D, GS, SP, SWR, BF16, BF16, E>(kt, vt, nt, kn, vn, t_new, dm, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
                                                  m_lane, l_lane, tacc, alpha, prep);
       else if (a.kraw == F32 && a.vraw == F32)
-        tail_pass<D, GS, SP, SWR, F32, F32, E>(kt, vt, nt, kn, vn, t_new, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
+        tail_pass<D, GS, SP, SWR, F32, F32, E>(kt, vt, nt, kn, vn, t_new, dm, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
                                                m_lane, l_lane, tacc, alpha, prep);
       else if (a.kraw == BF16)
-        tail_pass<D, GS, SP, SWR, BF16, F32, E>(kt, vt, nt, kn, vn, t_new, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
+        tail_pass<D, GS, SP, SWR, BF16, F32, E>(kt, vt, nt, kn, vn, t_new, dm, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
                                                 m_lane, l_lane, tacc, alpha, prep);
       else
-        tail_pass<D, GS, SP, SWR, F32, BF16, E>(kt, vt, nt, kn, vn, t_new, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
+        tail_pass<D, GS, SP, SWR, F32, BF16, E>(kt, vt, nt, kn, vn, t_new, dm, store_new, lane, Q.qh, Q.cq, L.sw, m_u,
                                                 m_lane, l_lane, tacc, alpha, prep);
     };
     if constexpr (C::VM) {
@@ -1522,7 +1626,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
     }
   };
 
+  // columns at or past dm are compute padding: never stored
   auto store_out = [&](int g, int d, float o) {
+    if (d >= dm) return;
     const int64_t off = b * a.o_sb + (int64_t)(hq0 + g) * a.o_sh + d;
     if (a.out_f32) {
       static_cast<float *>(a.out)[off] = o;
@@ -1655,7 +1761,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
   if (tid == 0) __hip_atomic_store(a.counters + pairq * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int GS, int SP, int KF, int VF>
+template <int D, int GS, int SP, int KF, int VF, bool FULL>
 int launch_one(const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
   using C = Cfg<D, GS, KF, VF>;
   const unsigned gy = (unsigned)a.NQG;
@@ -1665,41 +1771,66 @@ int launch_one(const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
   if (gz > 65535 || a.k_bh_rows > INT32_MAX || a.v_bh_rows > INT32_MAX || chunk_rows > INT32_MAX ||
       n_rows > INT32_MAX)
     return -1;
-  hipLaunchKernelGGL((decode_kernel<D, GS, SP, KF, VF>), dim3((unsigned)a.ns, gy, (unsigned)gz),
+  hipLaunchKernelGGL((decode_kernel<D, GS, SP, KF, VF, FULL>), dim3((unsigned)a.ns, gy, (unsigned)gz),
                      dim3(64 * kDecodeWaves), 0, stream, static_cast<const char *>(a.krows),
                      static_cast<const char *>(a.vrows), a.kscales, a.vscales, (int32_t)a.k_bh_rows,
                      (int32_t)a.v_bh_rows, (int32_t)chunk_rows, (int32_t)n_rows, (int32_t)tile_rows, a);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-template <int D, int GS, int KF, int VF>
-int launch_sp(int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
+// One kernel instance, picked at run time from (D, GS, SP): launched, or
+// asked how many of its workgroups one CU holds at a time.
+template <bool FULL>
+struct LaunchOp {
+  const DecodeArgs &a;
+  int64_t n_wg;
+  hipStream_t stream;
+  template <int D, int GS, int SP, int KF, int VF>
+  int run() const { return launch_one<D, GS, SP, KF, VF, FULL>(a, n_wg, stream); }
+};
+
+template <bool FULL>
+struct ResidentOp {
+  // workgroups of the instance resident on one CU of the current device
+  // (its registers and LDS decide; -1 if the runtime cannot say)
+  template <int D, int GS, int SP, int KF, int VF>
+  int run() const {
+    int n = 0;
+    const hipError_t e =
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, GS, SP, KF, VF, FULL>, 64 * kDecodeWaves, 0);
+    return e == hipSuccess ? n : -1;
+  }
+};
+
+template <int D, int GS, int KF, int VF, class Op>
+int by_sp(int SP, const Op &op) {
   switch (SP) {
-    case 2: return launch_one<D, GS, 2, KF, VF>(a, n_wg, stream);
-    case 4: return launch_one<D, GS, 4, KF, VF>(a, n_wg, stream);
-    case 8: return launch_one<D, GS, 8, KF, VF>(a, n_wg, stream);
-    case 16: return launch_one<D, GS, 16, KF, VF>(a, n_wg, stream);
+    case 2: return op.template run<D, GS, 2, KF, VF>();
+    case 4: return op.template run<D, GS, 4, KF, VF>();
+    case 8: return op.template run<D, GS, 8, KF, VF>();
+    case 16: return op.template run<D, GS, 16, KF, VF>();
+    case 32: return op.template run<D, GS, 32, KF, VF>();
     default: return -1;
   }
 }
 
-template <int D, int KF, int VF>
-int launch_gs(int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
+template <int D, int KF, int VF, class Op>
+int by_gs(int GS, int SP, const Op &op) {
   switch (GS) {
-    case 1: return launch_sp<D, 1, KF, VF>(SP, a, n_wg, stream);
-    case 2: return launch_sp<D, 2, KF, VF>(SP, a, n_wg, stream);
-    case 4: return launch_sp<D, 4, KF, VF>(SP, a, n_wg, stream);
-    case 8: return launch_sp<D, 8, KF, VF>(SP, a, n_wg, stream);
+    case 1: return by_sp<D, 1, KF, VF>(SP, op);
+    case 2: return by_sp<D, 2, KF, VF>(SP, op);
+    case 4: return by_sp<D, 4, KF, VF>(SP, op);
+    case 8: return by_sp<D, 8, KF, VF>(SP, op);
     default: return -1;
   }
 }
 
-template <int KF, int VF>
-int launch_fmt(int D, int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream) {
+template <int KF, int VF, class Op>
+int by_dim(int D, int GS, int SP, const Op &op) {
   switch (D) {
-    case 64: return launch_gs<64, KF, VF>(GS, SP, a, n_wg, stream);
-    case 128: return launch_gs<128, KF, VF>(GS, SP, a, n_wg, stream);
-    case 256: return launch_gs<256, KF, VF>(GS, SP, a, n_wg, stream);
+    case 64: return by_gs<64, KF, VF>(GS, SP, op);
+    case 128: return by_gs<128, KF, VF>(GS, SP, op);
+    case 256: return by_gs<256, KF, VF>(GS, SP, op);
     default: return -1;
   }
 }

@@ -26,6 +26,7 @@
 // VALU, one wave per block, lanes along head_dim.  MFMA is not used because
 // the contract fixes the order of the R additions.
 
+#include "basis_dev.h"
 #include "internal.h"
 
 namespace cdattn {
@@ -145,20 +146,17 @@ __device__ inline int8_t quantise(double c, float s32, double inv) {
   return (int8_t)min((int)r, 127);
 }
 
-// Encode block `n` (call-relative) of stream row (b, h) into archive slot
-// a.n0 + n.  One wave; lane owns head_dim elements [lane*EPL, lane*EPL+EPL).
-// The basis is copied from Mfill (the kernel arguments) into the wave's own
-// LDS slice M after the first round's loads are issued, so both are in
-// flight together.
-template <int EPL, int SP, int U, int RAW>
-__device__ void encode_sums(const EncodeArgs &a, float *M, const float *Mfill, int64_t b, int64_t h, int64_t n,
-                            int lane, double (&c)[SP][EPL]) {
-  const int d0 = lane * EPL;
+// Rows j0 .. j0+JP-1 of block `n` (call-relative) of stream row (b, h): one
+// wave, lane holding head_dim elements [d0, d0+EPL) (d0c: where it reads
+// them; lanes past head_dim read column 0 and store nothing).  U tokens per
+// round, their loads all in flight together (token i comes from src0 below
+// split_i, else from src1; indices past R repeat token R-1 and are not
+// used).  Products are added in token order (the contract's summation
+// order); the basis entries come from the table (uniform indices).
+template <int EPL, int JP, int U, int RAW>
+__device__ void encode_sums(const EncodeArgs &a, int j0, int64_t b, int64_t h, int64_t n, int d0c,
+                            double (&c)[JP][EPL]) {
   const int R = a.R, S = a.S;
-  // U tokens per round, their loads all in flight together (token i comes
-  // from src0 below split_i, else from src1; indices past R repeat token R-1
-  // and are not used).  Products are added in token order (the contract's
-  // summation order).
   for (int i0 = 0; i0 < R; i0 += U) {
     float x[U][EPL];
 #pragma unroll
@@ -166,25 +164,20 @@ __device__ void encode_sums(const EncodeArgs &a, float *M, const float *Mfill, i
       const int i = i0 + u < R ? i0 + u : R - 1;
       const bool f0 = i < a.split_i;
       const void *src = f0 ? a.src0 : a.src1;
-      const int64_t off = f0 ? b * a.s0_b + h * a.s0_h + (n * R + i) * a.s0_t + d0 : b * a.s1_b + h * a.s1_h + d0;
+      const int64_t off = f0 ? b * a.s0_b + h * a.s0_h + (n * R + i) * a.s0_t + d0c : b * a.s1_b + h * a.s1_h + d0c;
       load_raw_t<EPL, RAW>(src, off, x[u]);
-    }
-    if (i0 == 0) {
-      for (int k = lane; k < S * R; k += 64) M[k] = Mfill[k];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u;
       if (i < R) {
 #pragma unroll
-        for (int j = 0; j < SP; ++j) {
+        for (int jj = 0; jj < JP; ++jj) {
+          const int j = j0 + jj;
           if (j < S) {
-            const double m = (double)M[j * R + i];
+            const double m = (double)analysis_entry(a.png, R, j, i);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) c[j][e] = fma(m, (double)x[u][e], c[j][e]);
+            for (int e = 0; e < EPL; ++e) c[jj][e] = fma(m, (double)x[u][e], c[jj][e]);
           }
         }
       }
@@ -192,49 +185,60 @@ __device__ void encode_sums(const EncodeArgs &a, float *M, const float *Mfill, i
   }
 }
 
-// U tokens' loads in flight per round: sixteen for a lone block (latency
-// bound), eight when many blocks are in flight.
-template <int EPL, int SP, bool PIPE>
-__device__ void encode_block(const EncodeArgs &a, float *M, const float *Mfill, int64_t b, int64_t h,
-                             int64_t n, int lane) {
-  constexpr int D = EPL * 64;
+// Encode block `n` (call-relative) of stream row (b, h) into archive slot
+// a.n0 + n, JP rows per pass over the tokens.  One wave; lane owns head_dim
+// elements [lane*EPL, lane*EPL+EPL).  U tokens' loads in flight per round:
+// sixteen for a lone block (latency bound), eight when many blocks are in
+// flight.
+template <int EPL, int JP, bool PIPE>
+__device__ void encode_block(const EncodeArgs &a, int64_t b, int64_t h, int64_t n, int lane) {
   const int d0 = lane * EPL;
+  const bool dlive = d0 < a.D;
+  const int d0c = dlive ? d0 : 0;
   const int S = a.S;
-  double c[SP][EPL];
-#pragma unroll
-  for (int j = 0; j < SP; ++j)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) c[j][e] = 0.0;  // +0.0
   constexpr int U = PIPE ? 16 : 8;
-  if (a.raw == BF16)
-    encode_sums<EPL, SP, U, BF16>(a, M, Mfill, b, h, n, lane, c);
-  else
-    encode_sums<EPL, SP, U, F32>(a, M, Mfill, b, h, n, lane, c);
-
   const int64_t slot = (b * a.H + h) * a.cap + a.n0 + n;
+  for (int j0 = 0; j0 < S; j0 += JP) {
+    double c[JP][EPL];
 #pragma unroll
-  for (int j = 0; j < SP; ++j) {
-    if (j >= S) break;
-    const int64_t row = (slot * S + j) * D + d0;
-    if (a.fmt == F32) {
-      float *p = static_cast<float *>(a.rows) + row;
+    for (int jj = 0; jj < JP; ++jj)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) p[e] = (float)c[j][e];
-    } else if (a.fmt == BF16) {
-      uint16_t *p = static_cast<uint16_t *>(a.rows) + row;
+      for (int e = 0; e < EPL; ++e) c[jj][e] = 0.0;  // +0.0
+    if (a.raw == BF16)
+      encode_sums<EPL, JP, U, BF16>(a, j0, b, h, n, d0c, c);
+    else
+      encode_sums<EPL, JP, U, F32>(a, j0, b, h, n, d0c, c);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) p[e] = bf16_rne((float)c[j][e]);
-    } else {
-      double amax = 0.0;
+    for (int jj = 0; jj < JP; ++jj) {
+      const int j = j0 + jj;
+      if (j >= S) break;
+      const int64_t row = (slot * S + j) * a.D + d0;
+      if (a.fmt == F32) {
+        if (dlive) {
+          float *p = static_cast<float *>(a.rows) + row;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) amax = fmax(amax, fabs(c[j][e]));
-      amax = wave_max_f64(amax);
-      const float s32 = (float)(amax / 127.0);
-      const double inv = s32 != 0.0f ? 1.0 / (double)s32 : 0.0;
-      int8_t *p = static_cast<int8_t *>(a.rows) + row;
+          for (int e = 0; e < EPL; ++e) p[e] = (float)c[jj][e];
+        }
+      } else if (a.fmt == BF16) {
+        if (dlive) {
+          uint16_t *p = static_cast<uint16_t *>(a.rows) + row;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) p[e] = quantise(c[j][e], s32, inv);
-      if (lane == 0) a.scales[slot * S + j] = s32;
+          for (int e = 0; e < EPL; ++e) p[e] = bf16_rne((float)c[jj][e]);
+        }
+      } else {
+        double amax = 0.0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) amax = fmax(amax, fabs(c[jj][e]));
+        amax = wave_max_f64(dlive ? amax : 0.0);
+        const float s32 = (float)(amax / 127.0);
+        const double inv = s32 != 0.0f ? 1.0 / (double)s32 : 0.0;
+        if (dlive) {
+          int8_t *p = static_cast<int8_t *>(a.rows) + row;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) p[e] = quantise(c[jj][e], s32, inv);
+        }
+        if (lane == 0) a.scales[slot * S + j] = s32;
+      }
     }
   }
 }
@@ -244,6 +248,7 @@ __device__ void encode_block(const EncodeArgs &a, float *M, const float *Mfill, 
 template <int EPL, int RAW>
 __device__ void copy_tail(const EncodeArgs &a, int64_t b, int64_t h, int64_t bh, int lane) {
   const int d0 = lane * EPL;
+  if (d0 >= a.D) return;
   for (int i0 = 0; i0 < a.n_copy; i0 += 8) {
     float x[8][EPL];
 #pragma unroll
@@ -253,22 +258,20 @@ __device__ void copy_tail(const EncodeArgs &a, int64_t b, int64_t h, int64_t bh,
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (i0 + u < a.n_copy) store_raw<EPL>(a.tail, ((bh * a.R) + i0 + u) * (EPL * 64) + d0, RAW, x[u]);
+      if (i0 + u < a.n_copy) store_raw<EPL>(a.tail, ((bh * a.R) + i0 + u) * a.D + d0, RAW, x[u]);
   }
 }
 
 // Grid: x = (b, h) * per_bh + wave-group; each wave one block (or the tail copy).
-template <int EPL, int SP>
-__global__ __launch_bounds__(64 * kEncodeWaves) void encode_kernel(EncodeLaunch L, int64_t per_bh) {
-  const EncodeArgs &a = L.e;
-  __shared__ float sM[kEncodeWaves][kMaxS * kMaxR];   // one basis copy per wave
+template <int EPL, int JP>
+__global__ __launch_bounds__(64 * kEncodeWaves) void encode_kernel(EncodeArgs a, int64_t per_bh) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t bh = blockIdx.x / per_bh;
   const int64_t n = (blockIdx.x % per_bh) * kEncodeWaves + wave;
   const int64_t b = bh / a.H, h = bh % a.H;
   if (n < a.n_new) {
-    encode_block<EPL, SP, false>(a, sM[wave], L.M, b, h, n, lane);
+    encode_block<EPL, JP, false>(a, b, h, n, lane);
   } else if (n == a.n_new && a.n_copy > 0) {
     // raw remainder -> tail slots 0 .. n_copy-1, verbatim
     if (a.raw == BF16)
@@ -302,20 +305,19 @@ __device__ inline double group_max_f64(double v) {
 // formed JC at a time: each token is widened to fp64 once per pass and
 // feeds the JC rows' sums, each element by the same fp64 FMA chain in token
 // order as encode_block, so rows, codes and scales are identical.  A pass
-// past row S - 1 computes unused sums (its basis reads stay inside
-// EncodeLaunch::M).  Each token's sums sit behind its own (uniform) u < R
-// test even when R == RP: the branch keeps the scheduler from widening every
-// token at once, which would take twice the registers.  Waves past the
-// block waves copy the raw remainder of one (b, h) row each.  The basis comes
-// from the kernel arguments through scalar loads (its index is uniform).
+// past row S - 1 computes unused sums (from row R - 1's basis entries).
+// Each token's sums sit behind its own (uniform) u < R test even when
+// R == RP: the branch keeps the scheduler from widening every token at once,
+// which would take twice the registers.  Waves past the block waves copy the
+// raw remainder of one (b, h) row each.  The basis comes from the table
+// through scalar loads (its index is uniform).  A head_dim below the compute
+// width LPB * 8 leaves the lanes past it reading column 0 and storing nothing.
 template <int LPB, int RP, int JC, int RAW>
 __global__ __launch_bounds__(64 * kEncodeWaves) __attribute__((amdgpu_waves_per_eu(
-    RAW == BF16 ? (RP == 8 ? 4 : 3) : (RP == 8 ? 3 : 2)))) void encode_wide_kernel(EncodeLaunch L, int64_t BH,
+    RAW == BF16 ? (RP == 8 ? 4 : 3) : (RP == 8 ? 3 : 2)))) void encode_wide_kernel(EncodeArgs a, int64_t BH,
                                                                          int64_t block_waves) {
-  const EncodeArgs &a = L.e;
-  constexpr int D = LPB * 8, BPW = 64 / LPB, EPL = D / 64;
+  constexpr int DP = LPB * 8, BPW = 64 / LPB, EPL = DP / 64;
   constexpr int WPT = RAW == BF16 ? 1 : 2;   // 16-byte words per token and lane
-  static_assert((kMaxS + JC - 1) * 16 + RP <= kMaxS * kMaxR, "basis reads stay inside M");
   const int lane = threadIdx.x & 63;
   const int64_t gw = (int64_t)blockIdx.x * kEncodeWaves + (threadIdx.x >> 6);
   const int R = a.R, S = a.S;
@@ -331,8 +333,9 @@ __global__ __launch_bounds__(64 * kEncodeWaves) __attribute__((amdgpu_waves_per_
   const int64_t bh = gbc / a.n_new, n = gbc % a.n_new;
   const int64_t b = bh / a.H, h = bh % a.H;
   const int d0 = (lane % LPB) * 8;
+  const bool dlive = d0 < a.D;
   const char *src = static_cast<const char *>(a.src0) +
-                    (b * a.s0_b + h * a.s0_h + n * R * a.s0_t + d0) * (RAW == BF16 ? 2 : 4);
+                    (b * a.s0_b + h * a.s0_h + n * R * a.s0_t + (dlive ? d0 : 0)) * (RAW == BF16 ? 2 : 4);
   const int64_t tstride = a.s0_t * (RAW == BF16 ? 2 : 4);
   uint4 x[RP][WPT];
 #pragma unroll
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(64 * kEncodeWaves) __attribute__((amdgpu_waves_per_
         for (int e = 0; e < 8; ++e) xd[e] = elem(u, e);
 #pragma unroll
         for (int jj = 0; jj < JC; ++jj) {
-          const double m = (double)L.M[(j0 + jj) * R + u];
+          const double m = (double)analysis_entry(a.png, R, j0 + jj < R ? j0 + jj : R - 1, u);
 #pragma unroll
           for (int e = 0; e < 8; ++e) c[jj][e] = fma(m, xd[e], c[jj][e]);
         }
@@ -374,9 +377,9 @@ __global__ __launch_bounds__(64 * kEncodeWaves) __attribute__((amdgpu_waves_per_
     for (int jj = 0; jj < JC; ++jj) {
       const int j = j0 + jj;
       if (j >= S) break;
-      const int64_t row = (slot * S + j) * D + d0;
+      const int64_t row = (slot * S + j) * a.D + d0;
       if (a.fmt == F32) {
-        if (live) {
+        if (live && dlive) {
           float4 *p = reinterpret_cast<float4 *>(static_cast<float *>(a.rows) + row);
           p[0] = make_float4((float)c[jj][0], (float)c[jj][1], (float)c[jj][2], (float)c[jj][3]);
           p[1] = make_float4((float)c[jj][4], (float)c[jj][5], (float)c[jj][6], (float)c[jj][7]);
@@ -386,22 +389,20 @@ __global__ __launch_bounds__(64 * kEncodeWaves) __attribute__((amdgpu_waves_per_
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           w[k] = (uint32_t)bf16_rne((float)c[jj][2 * k]) | ((uint32_t)bf16_rne((float)c[jj][2 * k + 1]) << 16);
-        if (live)
+        if (live && dlive)
           *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.rows) + row) = make_uint4(w[0], w[1], w[2], w[3]);
       } else {
         double amax = 0.0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) amax = fmax(amax, fabs(c[jj][e]));
-        amax = group_max_f64<LPB>(amax);
+        amax = group_max_f64<LPB>(dlive ? amax : 0.0);
         const float s32 = (float)(amax / 127.0);
         const double inv = s32 != 0.0f ? 1.0 / (double)s32 : 0.0;
         uint32_t w[2] = {0u, 0u};
 #pragma unroll
         for (int e = 0; e < 8; ++e) w[e / 4] |= (uint32_t)(uint8_t)quantise(c[jj][e], s32, inv) << (8 * (e % 4));
-        if (live) {
-          *reinterpret_cast<uint2 *>(static_cast<int8_t *>(a.rows) + row) = make_uint2(w[0], w[1]);
-          if (lane % LPB == 0) a.scales[slot * S + j] = s32;
-        }
+        if (live && dlive) *reinterpret_cast<uint2 *>(static_cast<int8_t *>(a.rows) + row) = make_uint2(w[0], w[1]);
+        if (live && lane % LPB == 0) a.scales[slot * S + j] = s32;
       }
     }
     // The token words count as changed here, so a second pass widens them
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(64 * kEncodeWaves) __attribute__((amdgpu_waves_per_
 }
 
 // Grid: x = (b, h), y = stream (0 keys, 1 values); one wave each.
-template <int EPL, int SP>
+template <int EPL, int JP>
 __global__ __launch_bounds__(64) void append_kernel(AppendArgs A) {
   const EncodeArgs &a = A.e[blockIdx.y];
   const int lane = threadIdx.x;
@@ -423,42 +424,42 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs A) {
   if (A.complete) {
     // tail slots 0..R-2 plus the new token form the block; slot R-1 of the
     // tail is not written since the tail empties.
-    __shared__ float sM[kMaxS * kMaxR];
-    encode_block<EPL, SP, true>(a, sM, A.M, b, h, 0, lane);
+    encode_block<EPL, JP, true>(a, b, h, 0, lane);
   } else {
     const int d0 = lane * EPL;
+    if (d0 >= a.D) return;
     float x[EPL];
     load_raw<EPL>(a.src1, b * a.s1_b + h * a.s1_h + d0, a.raw, x);
-    store_raw<EPL>(a.tail, ((bh * a.R) + A.t) * (EPL * 64) + d0, a.raw, x);
+    store_raw<EPL>(a.tail, ((bh * a.R) + A.t) * a.D + d0, a.raw, x);
   }
 }
 
+// Rows per pass of the one-wave-per-block encode: the padded keep count, at
+// most eight.
+int rows_per_pass(int S) { return S <= 2 ? 2 : (S <= 4 ? 4 : 8); }
+
 template <int EPL>
-int launch_encode_epl(int SP, const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
-  const int64_t units = L.e.n_new + (L.e.n_copy > 0 ? 1 : 0);
+int launch_encode_epl(const EncodeArgs &e, int64_t BH, hipStream_t stream) {
+  const int64_t units = e.n_new + (e.n_copy > 0 ? 1 : 0);
   if (units == 0) return 0;
   const int64_t per_bh = (units + kEncodeWaves - 1) / kEncodeWaves;
   if (per_bh * BH > 0x7FFFFFFF) return -1;
   const dim3 grid((unsigned)(per_bh * BH)), block(64 * kEncodeWaves);
-  switch (SP) {
-    case 2: hipLaunchKernelGGL((encode_kernel<EPL, 2>), grid, block, 0, stream, L, per_bh); break;
-    case 4: hipLaunchKernelGGL((encode_kernel<EPL, 4>), grid, block, 0, stream, L, per_bh); break;
-    case 8: hipLaunchKernelGGL((encode_kernel<EPL, 8>), grid, block, 0, stream, L, per_bh); break;
-    case 16: hipLaunchKernelGGL((encode_kernel<EPL, 16>), grid, block, 0, stream, L, per_bh); break;
-    default: return -1;
+  switch (rows_per_pass(e.S)) {
+    case 2: hipLaunchKernelGGL((encode_kernel<EPL, 2>), grid, block, 0, stream, e, per_bh); break;
+    case 4: hipLaunchKernelGGL((encode_kernel<EPL, 4>), grid, block, 0, stream, e, per_bh); break;
+    default: hipLaunchKernelGGL((encode_kernel<EPL, 8>), grid, block, 0, stream, e, per_bh); break;
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
 template <int EPL>
-int launch_append_epl(int SP, const AppendArgs &A, int64_t BH, hipStream_t stream) {
+int launch_append_epl(const AppendArgs &A, int64_t BH, hipStream_t stream) {
   const dim3 grid((unsigned)BH, 2), block(64);
-  switch (SP) {
+  switch (rows_per_pass(A.e[0].S)) {
     case 2: hipLaunchKernelGGL((append_kernel<EPL, 2>), grid, block, 0, stream, A); break;
     case 4: hipLaunchKernelGGL((append_kernel<EPL, 4>), grid, block, 0, stream, A); break;
-    case 8: hipLaunchKernelGGL((append_kernel<EPL, 8>), grid, block, 0, stream, A); break;
-    case 16: hipLaunchKernelGGL((append_kernel<EPL, 16>), grid, block, 0, stream, A); break;
-    default: return -1;
+    default: hipLaunchKernelGGL((append_kernel<EPL, 8>), grid, block, 0, stream, A); break;
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
@@ -466,68 +467,64 @@ int launch_append_epl(int SP, const AppendArgs &A, int64_t BH, hipStream_t strea
 }  // namespace
 
 template <int LPB, int RP, int JC>
-int launch_encode_wide(const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
+int launch_encode_wide(const EncodeArgs &e, int64_t BH, hipStream_t stream) {
   constexpr int BPW = 64 / LPB;
-  const int64_t block_waves = (BH * L.e.n_new + BPW - 1) / BPW;
-  const int64_t waves = block_waves + (L.e.n_copy > 0 ? BH : 0);
+  const int64_t block_waves = (BH * e.n_new + BPW - 1) / BPW;
+  const int64_t waves = block_waves + (e.n_copy > 0 ? BH : 0);
   if (waves == 0) return 0;
   if ((waves + kEncodeWaves - 1) / kEncodeWaves > 0x7FFFFFFF) return -1;
   const dim3 grid((unsigned)((waves + kEncodeWaves - 1) / kEncodeWaves)), block(64 * kEncodeWaves);
-  if (L.e.raw == BF16)
-    hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, JC, BF16>), grid, block, 0, stream, L, BH, block_waves);
+  if (e.raw == BF16)
+    hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, JC, BF16>), grid, block, 0, stream, e, BH, block_waves);
   else
-    hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, JC, F32>), grid, block, 0, stream, L, BH, block_waves);
+    hipLaunchKernelGGL((encode_wide_kernel<LPB, RP, JC, F32>), grid, block, 0, stream, e, BH, block_waves);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
 // Rows per pass: S itself up to 4 (no unused sums), else passes of 4.
 template <int LPB, int RP>
-int launch_encode_wide_j(const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
-  switch (L.e.S) {
+int launch_encode_wide_j(const EncodeArgs &e, int64_t BH, hipStream_t stream) {
+  switch (e.S) {
     case 1:
-    case 2: return launch_encode_wide<LPB, RP, 2>(L, BH, stream);
-    case 3: return launch_encode_wide<LPB, RP, 3>(L, BH, stream);
-    default: return launch_encode_wide<LPB, RP, 4>(L, BH, stream);
+    case 2: return launch_encode_wide<LPB, RP, 2>(e, BH, stream);
+    case 3: return launch_encode_wide<LPB, RP, 3>(e, BH, stream);
+    default: return launch_encode_wide<LPB, RP, 4>(e, BH, stream);
   }
 }
 
 template <int LPB>
-int launch_encode_wide_r(const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
-  return L.e.R <= 8 ? launch_encode_wide_j<LPB, 8>(L, BH, stream) : launch_encode_wide_j<LPB, 16>(L, BH, stream);
+int launch_encode_wide_r(const EncodeArgs &e, int64_t BH, hipStream_t stream) {
+  return e.R <= 8 ? launch_encode_wide_j<LPB, 8>(e, BH, stream) : launch_encode_wide_j<LPB, 16>(e, BH, stream);
 }
 
 // Returns 0 on success, 1 on a HIP launch error, -1 if no kernel exists.
 // Blocks of up to 16 tokens from one source with 16-byte aligned rows take
-// the wide-lane kernel; the rest one wave per block.
-int launch_encode(int D, const EncodeLaunch &L, int64_t BH, hipStream_t stream) {
-  const EncodeArgs &e = L.e;
+// the wide-lane kernel; the rest one wave per block.  The kernels work at
+// the compute width of the head_dim (64, 128 or 256).
+int launch_encode(const EncodeArgs &e, int64_t BH, hipStream_t stream) {
+  const int DP = pad_dim(e.D);
   const bool wide = e.split_i == e.R && e.R <= 16 && (e.raw == BF16 || e.raw == F32) &&
                     ((uintptr_t)e.src0 | (uintptr_t)e.rows) % 16 == 0 && e.s0_b % 8 == 0 && e.s0_h % 8 == 0 &&
                     e.s0_t % 8 == 0;
   if (wide) {
-    switch (D) {
-      case 64: return launch_encode_wide_r<8>(L, BH, stream);
-      case 128: return launch_encode_wide_r<16>(L, BH, stream);
-      case 256: return launch_encode_wide_r<32>(L, BH, stream);
-      default: return -1;
+    switch (DP) {
+      case 64: return launch_encode_wide_r<8>(e, BH, stream);
+      case 128: return launch_encode_wide_r<16>(e, BH, stream);
+      default: return launch_encode_wide_r<32>(e, BH, stream);
     }
   }
-  const int SP = decode_pad_keep(L.e.S);
-  switch (D) {
-    case 64: return launch_encode_epl<1>(SP, L, BH, stream);
-    case 128: return launch_encode_epl<2>(SP, L, BH, stream);
-    case 256: return launch_encode_epl<4>(SP, L, BH, stream);
-    default: return -1;
+  switch (DP) {
+    case 64: return launch_encode_epl<1>(e, BH, stream);
+    case 128: return launch_encode_epl<2>(e, BH, stream);
+    default: return launch_encode_epl<4>(e, BH, stream);
   }
 }
 
-int launch_append(int D, const AppendArgs &A, int64_t BH, hipStream_t stream) {
-  const int SP = decode_pad_keep(A.e[0].S);
-  switch (D) {
-    case 64: return launch_append_epl<1>(SP, A, BH, stream);
-    case 128: return launch_append_epl<2>(SP, A, BH, stream);
-    case 256: return launch_append_epl<4>(SP, A, BH, stream);
-    default: return -1;
+int launch_append(const AppendArgs &A, int64_t BH, hipStream_t stream) {
+  switch (pad_dim(A.e[0].D)) {
+    case 64: return launch_append_epl<1>(A, BH, stream);
+    case 128: return launch_append_epl<2>(A, BH, stream);
+    default: return launch_append_epl<4>(A, BH, stream);
   }
 }
 

@@ -12,7 +12,13 @@ struct codec_stream;   // include/cdattn.h
 namespace cdattn {
 
 constexpr int kMaxR = 32;      // tokens per block
-constexpr int kMaxS = 16;      // kept frequencies
+constexpr int kMaxS = 32;      // kept frequencies
+constexpr int kMaxD = 256;     // head_dim (a multiple of 8)
+
+// Compute width of the kernels for head_dim D: the next of 64, 128 and 256.
+// Rows in memory keep their own pitch D; columns past D are read as zeros
+// (or multiply zero query digits) and never written.
+constexpr int pad_dim(int D) { return D <= 64 ? 64 : (D <= 128 ? 128 : 256); }
 constexpr int kDecodeWaves = 8;   // waves per decode workgroup
 constexpr int kEncodeWaves = 4;   // waves (one block each) per encode workgroup
 
@@ -30,7 +36,9 @@ struct EncodeArgs {
   int32_t split_i;        // R for a plain run of tokens, R-1 for an append
   int32_t raw;            // Fmt of the source tokens (BF16 or F32)
   int32_t fmt;            // Fmt of the coefficient rows
+  int32_t png;            // 1: PNG mode analysis (anchor and differences), else the DCT-II table
   int32_t R, S;
+  int32_t D;              // head_dim: row pitch of tokens, rows and tail
   int64_t H;              // heads (b = bh / H)
   int64_t n_new;          // blocks to encode per (b, h)
   int64_t n0;             // first destination slot
@@ -42,22 +50,16 @@ struct EncodeArgs {
   void *tail;             // [B][H][R][D], raw dtype
 };
 
-struct EncodeLaunch {
-  EncodeArgs e;
-  float M[kMaxS * kMaxR]; // analysis basis, M[j*R + i] = fp32(c_j cos(..))
-};
-
 // Append one token: tail slot t <- new token; if t + 1 == R the same launch
 // encodes the block (tail slots 0..R-2 and the new token) into slot n.
 struct AppendArgs {
   EncodeArgs e[2];        // [0] = keys, [1] = values; src0 = tail, src1 = new
   int32_t t;              // tail slot the new token goes to
   int32_t complete;       // 1 if this token completes a block
-  float M[kMaxS * kMaxR]; // shared analysis basis (keys and values share R, S)
 };
 
-int launch_encode(int D, const EncodeLaunch &a, int64_t BH, hipStream_t stream);
-int launch_append(int D, const AppendArgs &a, int64_t BH, hipStream_t stream);
+int launch_encode(const EncodeArgs &a, int64_t BH, hipStream_t stream);
+int launch_append(const AppendArgs &a, int64_t BH, hipStream_t stream);
 
 // ------------------------------------------------------ view, crop, gather --
 // Decoded view: blocks blk0 .. blk0+nblk-1 of every (b, h); token i of block
@@ -68,6 +70,7 @@ struct ViewArgs {
   const float *scales;    // [BH][cap][S] (I8)
   const void *tail;       // [BH][R][D] of raw
   int32_t rf, raw, out;   // row, tail and view formats
+  int32_t png;            // 1: PNG mode synthesis (cumulative sum)
   int32_t R, S, D;
   int64_t H, BH, cap;
   int64_t blk0, nblk;
@@ -75,7 +78,6 @@ struct ViewArgs {
   int32_t n_copy;
   void *dst;
   int64_t o_sb, o_sh, o_st, o_t0;
-  float A[kMaxR * kMaxS]; // synthesis basis, A[i*S + j] = fp32(M[j][i])
 };
 
 constexpr int kGatherChunk = 256;   // destination batch rows per gather launch
@@ -120,6 +122,7 @@ struct DecodeArgs {
   int32_t kf, vf;         // row formats
   int32_t kraw, vraw;     // tail formats
   int32_t png;            // 1: PNG mode synthesis (cumulative sum), else the DCT-II basis
+  int32_t Dm;             // head_dim: row pitch in memory (<= the kernel's compute width)
   // Fused append (fuse_new = 1): one new key / value token per (b, h) joins
   // the raw tail as slot n_tail (it does not complete a block); the tail
   // pass reads it from knew / vnew and query group 0 stores it to the slot.
@@ -144,6 +147,9 @@ int decode_pad_keep(int S);
 
 constexpr int kMaxSplits = 256;   // splits per (b, kv head, query group)
 constexpr int kCounterStride = 64; // uint32 slots between arrival counters (256 bytes)
+// Decode workgroups that fill a device once, at most (the arrival-counter
+// region of every workspace holds this many counters: 256 KiB).
+constexpr int kMaxTargetWorkgroups = 1024;
 
 // Coefficient rows per decode tile: about 8 KB of key plus value rows.  The
 // MFMA value paths (int8 / bf16 rows) work in 32-row chunks, so a tile below
@@ -156,23 +162,35 @@ constexpr int decode_tile_rows(int D, int kf, int vf) {
   return (vf == I8 || vf == BF16) && rows < 32 && 32 * rb <= 12288 ? 32 : rows;
 }
 
-int launch_decode(int D, int GS, int SP, int kf, int vf, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
+// Decode kernel instances: compute width D (64, 128, 256), group size GS,
+// padded kept rows SP, row formats kf / vf; `full` selects the instance for
+// rows whose head_dim is D (else a.Dm < D).
+int launch_decode(int D, int GS, int SP, int kf, int vf, bool full, const DecodeArgs &a, int64_t n_wg,
+                  hipStream_t stream);
+// Workgroups of a decode kernel instance that one CU of the current device
+// holds at a time (-1 if unknown).
+int resident_decode(int D, int GS, int SP, int kf, int vf, bool full);
+// The device `stream` belongs to (the current device for the null stream).
+int stream_device(hipStream_t stream, int *dev);
 
 // Split plan of a decode: group size, query groups per kv head, padded kept
-// rows, splits per (b, kv head, query group), blocks per split, workgroups,
-// and the workspace layout (counters, then (max, sum) pairs, then partial
-// accumulators).  A pure function of the shapes.
+// rows, the workgroups that fill the device once, splits per (b, kv head,
+// query group), blocks per split, workgroups, and the workspace layout
+// (counters, then (max, sum) pairs, then partial accumulators).  A function
+// of the shapes and of the device's CU count and the kernel's occupancy.
 struct DecodePlan {
   bool ok;
   int GS, NQG, SP, ns;
-  int64_t pairs, chunk, n_wg;
+  int64_t target, pairs, chunk, n_wg;
   size_t off_ml, off_acc, bytes;
 };
 
-// Validation of a decode call apart from its workspace; no HIP call.
+// Validation of a decode call apart from its workspace; fills the plan for
+// the device of `stream` (no launch; the first call per device and kernel
+// instance asks the runtime for its CU count and the kernel's occupancy).
 int decode_check_args(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
                       const codec_stream *v, float scale, const void *out, const int64_t out_stride[2],
-                      int32_t out_dtype, DecodePlan *p);
+                      int32_t out_dtype, hipStream_t stream, DecodePlan *p);
 // The decode launch for validated arguments and a workspace of p.bytes
 // (fuse_k / fuse_v non-null: one new token joins the tail as slot n_tail).
 int launch_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, const codec_stream *k,
@@ -180,8 +198,12 @@ int launch_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, con
                        int32_t out_dtype, void *workspace, const DecodePlan &p, const void *fuse_k,
                        const int64_t kn_stride[2], const void *fuse_v, const int64_t vn_stride[2],
                        hipStream_t stream);
-#define CDATTN_DECL_DECODE(K, V) \
-  int launch_decode_##K##_##V(int D, int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream);
+#define CDATTN_DECL_DECODE(K, V)                                                                             \
+  int launch_decode_##K##_##V(int D, int GS, int SP, const DecodeArgs &a, int64_t n_wg, hipStream_t stream); \
+  int resident_decode_##K##_##V(int D, int GS, int SP);                                                      \
+  int launch_decode_##K##_##V##_pad(int D, int GS, int SP, const DecodeArgs &a, int64_t n_wg,                \
+                                    hipStream_t stream);                                                     \
+  int resident_decode_##K##_##V##_pad(int D, int GS, int SP);
 CDATTN_DECL_DECODE(i8, i8)
 CDATTN_DECL_DECODE(i8, bf16)
 CDATTN_DECL_DECODE(i8, f32)

@@ -28,15 +28,6 @@ constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 void *g_scratch[kMaxDevices];   // address of `scratch` on each device, once looked up
 
-// The device `stream` belongs to (the current device for the null stream).
-int stream_device(hipStream_t stream, int *dev) {
-  if (stream == nullptr) return hipGetDevice(dev) == hipSuccess ? CODEC_OK : CODEC_ERR_HIP;
-  hipDevice_t d = 0;
-  if (hipStreamGetDevice(stream, &d) != hipSuccess) return CODEC_ERR_HIP;
-  *dev = (int)d;
-  return CODEC_OK;
-}
-
 // Device address of `scratch` on the device of `stream`: looked up on the
 // first call for that device, with that device current, then kept.
 int scratch_on(hipStream_t stream, void **ptr) {
@@ -66,7 +57,7 @@ extern "C" int codec_decode_attention_noalloc(const void *q, const int64_t q_str
                                               void *out, const int64_t out_stride[2], int32_t out_dtype,
                                               hipStream_t stream) {
   DecodePlan p;
-  int rc = decode_check_args(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, &p);
+  int rc = decode_check_args(q, q_stride, Hq, k, v, scale, out, out_stride, out_dtype, stream, &p);
   if (rc) return rc;
   // a single split writes the output directly and touches no scratch
   if (p.ns > 1 && p.bytes > (size_t)CODEC_SCRATCH_BYTES) return CODEC_ERR_WORKSPACE;

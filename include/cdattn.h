@@ -19,9 +19,12 @@
  * Conventions for every call
  *   - Tensor pointers are DEVICE pointers unless stated otherwise.
  *   - Strides are in elements.  The head_dim axis is always contiguous.
- *   - Every call validates all arguments synchronously BEFORE any HIP call;
- *     on error it returns a non-zero status, enqueues nothing and changes
- *     nothing (stream counters included).
+ *   - Every call validates all arguments synchronously BEFORE it enqueues
+ *     anything; on error it returns a non-zero status, enqueues nothing and
+ *     changes nothing (stream counters included).  The decode calls' split
+ *     plan asks the runtime, once per device and kernel, for the stream's
+ *     device, its CU count and the kernel's occupancy; every other check
+ *     makes no HIP call.
  *   - Work is enqueued on the caller's `stream` and the call returns without
  *     waiting.  The library allocates no memory and keeps no pointer past
  *     the call.  The caller owns every buffer.
@@ -66,8 +69,12 @@ enum {
 
 /* Limits of this build. */
 #define CODEC_MAX_BLOCK 32   /* R: tokens per block                            */
-#define CODEC_MAX_KEEP 16    /* S: kept frequencies (S <= R)                   */
-/* head_dim D must be 64, 128 or 256.  GQA group G = Hq / H must be >= 1.     */
+#define CODEC_MAX_KEEP 32    /* S: kept frequencies (S <= R)                   */
+#define CODEC_MAX_HEAD_DIM 256
+/* head_dim D: 8 .. 256, a multiple of 8 (other values: UNSUPPORTED; the
+ * pages' kernel declines only D > 256).  The kernels compute at D rounded up
+ * to 64, 128 or 256; rows in memory keep the pitch D.  GQA group G = Hq / H
+ * must be >= 1.                                                              */
 
 /*
  * One compressed key or value stream: the archive of complete blocks and the
@@ -91,7 +98,7 @@ enum {
 typedef struct codec_stream {
   int32_t block;      /* R, 1 .. CODEC_MAX_BLOCK                          */
   int32_t keep;       /* S, 1 .. min(R, CODEC_MAX_KEEP)                    */
-  int32_t head_dim;   /* D, 64 | 128 | 256                                 */
+  int32_t head_dim;   /* D, 8 .. 256, a multiple of 8                      */
   int32_t fmt;        /* CODEC_F32 | CODEC_BF16 | CODEC_I8 (rows)          */
   int32_t raw_dtype;  /* CODEC_BF16 | CODEC_F32 (raw tokens and tail)      */
   int32_t n_tail;     /* raw tokens in the tail, 0 .. R-1                  */
@@ -163,8 +170,13 @@ int codec_append_step(codec_stream *k, codec_stream *v,
 
 /*
  * codec_decode_workspace_bytes -- workspace needed by codec_decode_attention
- * for these streams and Hq query heads (a pure function of the shapes).
- * The workspace holds a fixed 64 KiB region of arrival counters (one per
+ * for these streams and Hq query heads on the current device.  The split
+ * count, and so the size, follows from the shapes and from the number of
+ * decode workgroups that fill the device once (its CU count times the
+ * kernel's workgroups resident per CU, asked of the runtime once per device
+ * and kernel; 256 on a host without a GPU, at most 1024): a decode on a
+ * stream of another device of the same kind plans the same.
+ * The workspace holds a fixed 256 KiB region of arrival counters (one per
  * (b, kv head, query group), 256 bytes apart) followed by the per-split
  * (max, sum, acc) partials.  It must be zero-filled once before its first
  * use; every completed decode call leaves the counters at zero again, so
@@ -194,6 +206,14 @@ int codec_decode_workspace_bytes(const codec_stream *k, const codec_stream *v,
  * Errors: NULL, SHAPE (includes an empty sequence), FORMAT, SCALE,
  * WORKSPACE, UNSUPPORTED (no kernel for the shape, B * H above 65535, or
  * 2^31 or more coefficient rows per (b, h) in a stream's capacity), HIP.
+ * Shapes with a kernel: a decode tile must hold whole blocks, so S may not
+ * exceed the tile's rows, 8192 / (D' (bytes per key element + bytes per
+ * value element)) with D' = D rounded up to 64, 128 or 256, raised to 32
+ * when the values are int8 or bf16 and 32 such rows take at most 12 KB.
+ * That is S <= 32 for int8 keys and values up to D = 128 and S <= 16 at
+ * D <= 256; bf16 keys and values: 32 / 16 / 8 at D' = 64 / 128 / 256; fp32
+ * (and PNG) keys and values: 16 / 8 / 4.  Other S give UNSUPPORTED (from
+ * codec_decode_workspace_bytes as well).
  */
 int codec_decode_attention(const void *q, const int64_t q_stride[2], int64_t Hq,
                            const codec_stream *k, const codec_stream *v, float scale,

@@ -68,7 +68,7 @@ def test_status_strings(lib):
 
 @pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 12, 16, 31, 32])
 def test_basis_bitwise_equals_oracle(lib, R):
-    for S in range(1, min(R, 16) + 1):
+    for S in range(1, R + 1):
         A = (ctypes.c_float * (R * S))()
         assert lib.codec_basis(R, S, A) == OK
         got = np.frombuffer(A, dtype=np.float32).reshape(R, S)
@@ -77,12 +77,12 @@ def test_basis_bitwise_equals_oracle(lib, R):
 
 
 def test_basis_errors(lib):
-    A = (ctypes.c_float * 64)()
+    A = (ctypes.c_float * 1024)()
     assert lib.codec_basis(8, 2, None) == NULL
     assert lib.codec_basis(0, 1, A) == SHAPE
     assert lib.codec_basis(8, 9, A) == SHAPE
     assert lib.codec_basis(33, 2, A) == SHAPE
-    assert lib.codec_basis(32, 17, A) == SHAPE
+    assert lib.codec_basis(32, 33, A) == SHAPE
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
@@ -104,9 +104,10 @@ def encode(lib, s, x=FAKE, strides=(4096, 1024, 128), T=40):
 
 def test_encode_validation(lib):
     assert encode(lib, None) == NULL
-    for kw, want in [({"block": 0}, SHAPE), ({"block": 33}, SHAPE), ({"keep": 9}, SHAPE), ({"keep": 17, "block": 32}, SHAPE),
+    for kw, want in [({"block": 0}, SHAPE), ({"block": 33}, SHAPE), ({"keep": 9}, SHAPE), ({"keep": 33, "block": 32}, SHAPE),
                      ({"fmt": 7}, FORMAT), ({"raw_dtype": bd.FMT_I8}, FORMAT), ({"n_tail": 3}, STATE),
-                     ({"n_tail": 8}, STATE), ({"capacity": 4}, CAPACITY), ({"head_dim": 96}, UNSUPPORTED),
+                     ({"n_tail": 8}, STATE), ({"capacity": 4}, CAPACITY), ({"head_dim": 100}, UNSUPPORTED),
+                     ({"head_dim": 264}, UNSUPPORTED), ({"head_dim": 4}, UNSUPPORTED),
                      ({"head_dim": 0}, SHAPE), ({"batch": 0}, SHAPE), ({"tail": None}, NULL),
                      ({"rows": None}, NULL), ({"scales": None}, NULL), ({"tail": FAKE + 4}, SHAPE),
                      ({"n_blocks": 10, "capacity": 8}, CAPACITY)]:
@@ -274,7 +275,7 @@ def test_png_mode_validation(lib):
     # PNG mode keeps S = R rows; keys and values share the synthesis
     assert encode(lib, stream(fmt=bd.FMT_PNG, keep=2, block=8)) == SHAPE
     assert encode(lib, stream(fmt=bd.FMT_PNG, keep=16, block=16), T=0) == OK
-    assert encode(lib, stream(fmt=bd.FMT_PNG, keep=32, block=32)) == SHAPE    # beyond CODEC_MAX_KEEP
+    assert encode(lib, stream(fmt=bd.FMT_PNG, keep=31, block=32)) == SHAPE    # PNG keeps all R rows
     two = bd._I64_2(1024, 128)
     k = stream(fmt=bd.FMT_PNG, keep=8, block=8)
     v = stream(fmt=bd.FMT_F32, keep=8, block=8)
@@ -334,7 +335,7 @@ def test_decode_noalloc_validation(lib):
     assert dec(q=FAKE + 2) == SHAPE
     assert dec(vv=stream(n_blocks=16, capacity=16, keep=3)) == SHAPE
     assert dec(kk=stream(), vv=stream()) == SHAPE
-    assert dec(kk=stream(head_dim=96), vv=stream(head_dim=96)) == UNSUPPORTED
+    assert dec(kk=stream(head_dim=100), vv=stream(head_dim=100)) == UNSUPPORTED
     assert lib.codec_decode_attention_noalloc(FAKE, None, 16, ctypes.byref(k), ctypes.byref(v), ctypes.c_float(0.1),
                                               FAKE, two, bd.FMT_F32, None) == NULL
 

@@ -128,12 +128,12 @@ def test_fullsize_long_context_fused_steps():
 
 
 def _ns_from_workspace(nbytes, pairs, GS, D):
-    """Split count of a decode from its workspace size: a 64 KiB counter
+    """Split count of a decode from its workspace size: a 256 KiB counter
     region, then (max, sum) pairs (256-byte aligned) and the D-wide
     partial accumulators, each per (pair, split, head)."""
     for ns in range(1, 257):
         ml = -(-(pairs * ns * GS * 8) // 256) * 256
-        if 65536 + ml + pairs * ns * GS * D * 4 == nbytes:
+        if 262144 + ml + pairs * ns * GS * D * 4 == nbytes:
             return ns
     raise AssertionError(f"workspace size {nbytes} matches no split count")
 
