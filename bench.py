@@ -360,7 +360,8 @@ def main():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="long128k", choices=sorted(syn.WORKLOADS))
-    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layers rotated per step (default: enough for 512 MiB of archives, twice the MALL; 8 to 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", type=int, default=0, metavar="N",
                     help="launch sequence for rocprofv3 counter passes: N decodes and N calibration copies")
@@ -374,6 +375,8 @@ def main():
         sys.exit(2)
 
     w = syn.WORKLOADS[args.workload]
+    if args.layers <= 0:
+        args.layers = min(64, max(8, -(-(512 << 20) // decode_bytes(w, w.n_blocks, w.n_tail))))
     if args.traffic:
         traffic_summary(w, *args.traffic)
         return
