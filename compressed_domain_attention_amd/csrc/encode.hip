@@ -152,12 +152,25 @@ __device__ inline int8_t quantise(double c, float s32, double inv) {
 // round, their loads all in flight together (token i comes from src0 below
 // split_i, else from src1; indices past R repeat token R-1 and are not
 // used).  Products are added in token order (the contract's summation
-// order); the basis entries come from the table (uniform indices).
+// order).  A round's basis entries are requested from the table with its
+// tokens, lane jj * U + u of mr holding row j0 + jj, token i0 + u, and each
+// product takes its entry with a lane read at a constant lane (no scalar
+// load and wait per product).
 template <int EPL, int JP, int U, int RAW>
 __device__ void encode_sums(const EncodeArgs &a, int j0, int64_t b, int64_t h, int64_t n, int d0c,
                             double (&c)[JP][EPL]) {
   const int R = a.R, S = a.S;
+  const int lane = threadIdx.x & 63;
+  constexpr int NM = (JP * U + 63) / 64;
   for (int i0 = 0; i0 < R; i0 += U) {
+    float mr[NM];
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      const int l = 64 * q + lane, jj = l / U, u = l % U, j = j0 + jj, i = i0 + u;
+      const bool in = jj < JP && j < S && i < R;
+      const float m = analysis_entry(a.png, R, in ? j : 0, in ? i : 0);   // unconditional load
+      mr[q] = in ? m : 0.0f;
+    }
     float x[U][EPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -175,7 +188,8 @@ __device__ void encode_sums(const EncodeArgs &a, int j0, int64_t b, int64_t h, i
         for (int jj = 0; jj < JP; ++jj) {
           const int j = j0 + jj;
           if (j < S) {
-            const double m = (double)analysis_entry(a.png, R, j, i);
+            const double m = (double)__int_as_float(
+                __builtin_amdgcn_readlane(__float_as_int(mr[(jj * U + u) / 64]), (jj * U + u) % 64));
 #pragma unroll
             for (int e = 0; e < EPL; ++e) c[jj][e] = fma(m, (double)x[u][e], c[jj][e]);
           }
@@ -305,13 +319,17 @@ __device__ inline double group_max_f64(double v) {
 // formed JC at a time: each token is widened to fp64 once per pass and
 // feeds the JC rows' sums, each element by the same fp64 FMA chain in token
 // order as encode_block, so rows, codes and scales are identical.  A pass
-// past row S - 1 computes unused sums (from row R - 1's basis entries).
+// past row S - 1 computes sums that are never stored (zero entries past row R - 1).
 // Each token's sums sit behind its own (uniform) u < R test even when
 // R == RP: the branch keeps the scheduler from widening every token at once,
 // which would take twice the registers.  Waves past the block waves copy the
-// raw remainder of one (b, h) row each.  The basis comes from the table
-// through scalar loads (its index is uniform).  A head_dim below the compute
-// width LPB * 8 leaves the lanes past it reading column 0 and storing nothing.
+// raw remainder of one (b, h) row each.  A pass's basis entries sit in one
+// register (lane jj * RP + u holds row j0 + jj, token u), requested at the
+// start of the pass (for the first pass right after the tokens), and each FMA
+// takes its entry with a lane read at a constant lane: no memory wait inside
+// the token loop.  A
+// head_dim below the compute width LPB * 8 leaves the lanes past it reading
+// column 0 and storing nothing.
 template <int LPB, int RP, int JC, int RAW>
 __global__ __launch_bounds__(64 * kEncodeWaves) __attribute__((amdgpu_waves_per_eu(
     RAW == BF16 ? (RP == 8 ? 4 : 3) : (RP == 8 ? 3 : 2)))) void encode_wide_kernel(EncodeArgs a, int64_t BH,
@@ -337,6 +355,14 @@ __global__ __launch_bounds__(64 * kEncodeWaves) __attribute__((amdgpu_waves_per_
   const char *src = static_cast<const char *>(a.src0) +
                     (b * a.s0_b + h * a.s0_h + n * R * a.s0_t + (dlive ? d0 : 0)) * (RAW == BF16 ? 2 : 4);
   const int64_t tstride = a.s0_t * (RAW == BF16 ? 2 : 4);
+  static_assert(JC * RP <= 64, "a pass's basis entries fit one register");
+  // entries of the pass that starts at row j0 (unconditional load: no branch around it)
+  auto pass_entries = [&](int j0) {
+    const int jj = lane / RP, u = lane % RP, j = j0 + jj;
+    const bool in = jj < JC && u < R && j < R;
+    const float m = analysis_entry(a.png, R, in ? j : 0, in ? u : 0);
+    return in ? m : 0.0f;
+  };
   uint4 x[RP][WPT];
 #pragma unroll
   for (int u = 0; u < RP; ++u) {
@@ -354,6 +380,7 @@ __global__ __launch_bounds__(64 * kEncodeWaves) __attribute__((amdgpu_waves_per_
   };
   const int64_t slot = (b * a.H + h) * a.cap + a.n0 + n;
   for (int j0 = 0; j0 < S; j0 += JC) {
+    const float mcur = pass_entries(j0);   // the first pass's requested after the tokens
     double c[JC][8];
 #pragma unroll
     for (int jj = 0; jj < JC; ++jj)
@@ -367,7 +394,7 @@ __global__ __launch_bounds__(64 * kEncodeWaves) __attribute__((amdgpu_waves_per_
         for (int e = 0; e < 8; ++e) xd[e] = elem(u, e);
 #pragma unroll
         for (int jj = 0; jj < JC; ++jj) {
-          const double m = (double)analysis_entry(a.png, R, j0 + jj < R ? j0 + jj : R - 1, u);
+          const double m = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mcur), jj * RP + u));
 #pragma unroll
           for (int e = 0; e < 8; ++e) c[jj][e] = fma(m, xd[e], c[jj][e]);
         }
