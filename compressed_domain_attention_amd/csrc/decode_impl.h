@@ -1379,6 +1379,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
   __shared__ __attribute__((aligned(16))) char lds_raw[LDS_BYTES];
   __shared__ __attribute__((aligned(16))) float sA[kMaxR * SP];
   __shared__ int last_flag;
+  static_assert(GS <= 8, "one tail max per head");
+  __shared__ float tail_m[8];   // the tail wave's running max per head right after the tail (MFMA value path)
   float *lds = reinterpret_cast<float *>(lds_raw);
 
   const int tid = threadIdx.x;
@@ -1416,9 +1418,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
   float m_lane = -INFINITY, l_lane = 0.0f;   // running max and sum of this lane's head, (lane % 16) % GS
 
   // ---- this wave's tiles: t = wave, wave + W, ... of the split; a tile is
-  // tile_rows = (TR / S) * S rows (whole blocks), a split chunk_rows rows
-  const int64_t r0s = (int64_t)split * chunk_rows;
-  const int64_t r1s = r0s + chunk_rows < n_rows ? r0s + chunk_rows : n_rows;
+  // tile_rows = (TR / S) * S rows (whole blocks), a split chunk_rows rows.
+  // With a raw tail and several splits the ranges shift by one tile: the
+  // first split (dispatched first) takes one tile more and the last split,
+  // whose wave with the fewest tiles runs the tail, one tile fewer.
+  const int64_t shift = (a.n_tail + a.fuse_new > 0 && a.ns > 1) ? tile_rows : 0;
+  const int64_t r0s = split == 0 ? 0 : (int64_t)split * chunk_rows + shift;
+  const int64_t r1e = (int64_t)(split + 1) * chunk_rows + shift;
+  const int64_t r1s = r1e < n_rows ? r1e : n_rows;
   const int nrs = r1s > r0s ? (int)(r1s - r0s) : 0;
   const int ntiles = (nrs + tile_rows - 1) / tile_rows;
   // The split's first rows (tile t of the split starts t * tile_rows rows
@@ -1484,25 +1491,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
     qr.convert(a, lane, Q.qB, Q.cqq);
   else
     qr.convert(a, lane, Q.qh, Q.cq);
-  for (int t0 = wave; t0 < ntiles; t0 += C::NBUF * W) {
-#pragma unroll
-    for (int i = 0; i < C::NBUF; ++i) {
-      // the buffer's next tile: K rows requested once the K phase is done,
-      // V rows once the V phase is done
-      const int t = t0 + i * W;
-      const int tn = t + C::NBUF * W;
-      const int n0 = tile_ref(t).nrows;
-      if (n0 > 0) process_k<D, GS, SP, KF, VF>(bufs[i], n0, lane, Q, L);
-      issue_k(bufs[i], tile_ref(tn), lane);
-      __builtin_amdgcn_sched_barrier(0);
-      if (n0 > 0) process_lv<D, GS, SP, KF, VF>(bufs[i], n0, S, R, lane, bas, L, m_u, m_lane, l_lane, acc);
-      issue_v(bufs[i], tile_ref(tn), lane);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
   // ---- the raw tail: one wave of the last split (the one with the fewest
-  // tiles), on the VALU paths
+  // tiles; with the shifted ranges the split has a tile fewer), on the VALU
+  // paths, before that wave's tiles (its first tiles are already requested):
+  // the wave with a tile fewer spends the difference on the tail while the
+  // others stream.  The tail's softmax state and sums are where the tiles'
+  // online softmax starts.
   const bool tail_wave = a.n_tail + a.fuse_new > 0 && split == a.ns - 1 && wave == ntiles % W;
   // tail accumulator beside the MFMA layout: ET columns per lane, few registers
   constexpr int ET = C::VM ? cmax(D / 64, 16 / GS) : 1, LT = D / ET;
@@ -1545,10 +1539,34 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
                                                 m_lane, l_lane, tacc, alpha, prep);
     };
     if constexpr (C::VM) {
+      // the tail's sums stay in acct, beside the MFMA layout, which the
+      // tiles' rescales do not reach: the running max here is kept, and the
+      // merge scales acct by exp2(max here - final max)
       run(acct);
       rescale_mfma<GS>(acc.m, alpha, lane);
+      if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < GS; ++g) tail_m[g] = m_u[g];
+      }
     } else {
       run(acc.v);
+    }
+  }
+
+  for (int t0 = wave; t0 < ntiles; t0 += C::NBUF * W) {
+#pragma unroll
+    for (int i = 0; i < C::NBUF; ++i) {
+      // the buffer's next tile: K rows requested once the K phase is done,
+      // V rows once the V phase is done
+      const int t = t0 + i * W;
+      const int tn = t + C::NBUF * W;
+      const int n0 = tile_ref(t).nrows;
+      if (n0 > 0) process_k<D, GS, SP, KF, VF>(bufs[i], n0, lane, Q, L);
+      issue_k(bufs[i], tile_ref(tn), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (n0 > 0) process_lv<D, GS, SP, KF, VF>(bufs[i], n0, S, R, lane, bas, L, m_u, m_lane, l_lane, acc);
+      issue_v(bufs[i], tile_ref(tn), lane);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -1589,9 +1607,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
       wave_lds_sync();
       if (lane < LT) {
 #pragma unroll
-        for (int g = 0; g < GS; ++g)
+        for (int g = 0; g < GS; ++g) {
+          const float f = __builtin_amdgcn_exp2f(tail_m[g] - m_u[g]);   // the tiles' rescales since the tail
 #pragma unroll
-          for (int e = 0; e < ET; ++e) macc[(wave * GS + g) * D + lane * ET + e] += acct[g][e];
+          for (int e = 0; e < ET; ++e) macc[(wave * GS + g) * D + lane * ET + e] += acct[g][e] * f;
+        }
       }
     }
   } else {
