@@ -111,7 +111,7 @@ DecodePlan make_plan(const codec_stream *k, const codec_stream *v, int64_t Hq, i
   DecodePlan p;
   const int64_t G = Hq / k->heads;
   p.GS = decode_group_size((int)G);
-  p.NQG = (int)(G / p.GS);
+  p.NQG = (int)((G + p.GS - 1) / p.GS);
   p.SP = decode_pad_keep(k->keep);
   p.pairs = k->batch * k->heads * p.NQG;
   const int64_t n = k->n_blocks;
@@ -170,11 +170,15 @@ int check_decode(const codec_stream *k, const codec_stream *v, int64_t Hq) {
 }  // namespace
 
 namespace cdattn {
+// Query heads per workgroup: G rounded up to 1, 2, 4 or 8 (at most 8), so
+// every coefficient row is read once per group of up to 8 query heads; a
+// group past the kv head's G heads computes its absent heads on a live
+// head's query and stores nothing for them.
 int decode_group_size(int G) {
-  if (G % 8 == 0) return 8;
-  if (G % 4 == 0) return 4;
-  if (G % 2 == 0) return 2;
-  return 1;
+  if (G >= 8) return 8;
+  int gs = 1;
+  while (gs < G) gs *= 2;
+  return gs;
 }
 int decode_pad_keep(int S) {
   int sp = 2;

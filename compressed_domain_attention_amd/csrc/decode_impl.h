@@ -324,12 +324,13 @@ struct QRegMfma {
   // narrower than D (FULL false): a half of 8 columns at or past a.Dm (a
   // multiple of 8) reads column 0 instead, and the conversion takes it as
   // zero.
-  __device__ __forceinline__ void load(const DecodeArgs &a, int b, int hq0, int lane) {
+  // Heads g >= gv of the group (past the kv head's query heads) read head 0.
+  __device__ __forceinline__ void load(const DecodeArgs &a, int b, int hq0, int gv, int lane) {
     const int n = lane % 16, G = lane / 16;
 #pragma unroll
     for (int nb = 0; nb < NBN; ++nb) {
       const int g = 4 * nb + n / 4;
-      const int gl = g < GS ? g : 0;   // columns of absent heads read a live one and are zeroed below
+      const int gl = g < gv ? g : 0;   // columns of absent heads read a live one and are zeroed below
       const uint4 *qh = reinterpret_cast<const uint4 *>(a.q + (int64_t)b * a.q_sb + (int64_t)(hq0 + gl) * a.q_sh);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
@@ -612,10 +613,12 @@ struct QRegValu {
   // Unconditional loads (no wait before the conversion).  Rows narrower than
   // D (FULL false): a half of 8 columns at or past a.Dm (a multiple of 8)
   // reads column 0 instead, and the conversion takes it as zero.
-  __device__ __forceinline__ void load(const DecodeArgs &a, int b, int hq0, int lane) {
+  // Heads g >= gv of the group (past the kv head's query heads) read head 0.
+  __device__ __forceinline__ void load(const DecodeArgs &a, int b, int hq0, int gv, int lane) {
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
-      const uint4 *qh = reinterpret_cast<const uint4 *>(a.q + (int64_t)b * a.q_sb + (int64_t)(hq0 + g) * a.q_sh);
+      const int gl = g < gv ? g : 0;
+      const uint4 *qh = reinterpret_cast<const uint4 *>(a.q + (int64_t)b * a.q_sb + (int64_t)(hq0 + gl) * a.q_sh);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int c = (lane % LK) * 16 + 8 * hf;
@@ -1394,6 +1397,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
   const int b = (int)(blockIdx.z / (unsigned)a.H);
   const int64_t pairq = bh * a.NQG + qg;
   const int hq0 = h * a.G + qg * GS;
+  // query heads of this group: GS, or fewer in the last group when GS does
+  // not divide the kv head's G query heads (the others are computed on head
+  // 0's query and never stored)
+  const int gv = a.G - qg * GS < GS ? a.G - qg * GS : GS;
   const int R = a.R, S = a.S;
   const int dm = FULL ? D : a.Dm;   // head_dim in memory (D is the compute width)
 
@@ -1472,7 +1479,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
   // conversion) runs while the tile is in flight.
   using QR = typename std::conditional<C::KM, QRegMfma<D, GS, FULL>, QRegValu<D, GS, FULL>>::type;
   QR qr;
-  qr.load(a, b, hq0, lane);
+  qr.load(a, b, hq0, gv, lane);
   // NBUF register buffers per wave: the first NBUF tiles are requested at once
   TileBuf<D, GS, KF, VF> bufs[C::NBUF];
 #pragma unroll
@@ -1509,7 +1516,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
     // MFMA key path: the VALU-layout query is loaded here and converted once
     // the tail's own loads are in flight
     QRegValu<D, GS, FULL> qv;
-    if constexpr (C::KM) qv.load(a, b, hq0, lane);
+    if constexpr (C::KM) qv.load(a, b, hq0, gv, lane);
     auto prep = [&]() {
       if constexpr (C::KM) qv.convert(a, lane, Q.qh, Q.cq);
     };
@@ -1646,9 +1653,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
     }
   };
 
-  // columns at or past dm are compute padding: never stored
+  // columns at or past dm and heads at or past gv are padding: never stored
   auto store_out = [&](int g, int d, float o) {
-    if (d >= dm) return;
+    if (d >= dm || g >= gv) return;
     const int64_t off = b * a.o_sb + (int64_t)(hq0 + g) * a.o_sh + d;
     if (a.out_f32) {
       static_cast<float *>(a.out)[off] = o;

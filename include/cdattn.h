@@ -74,7 +74,9 @@ enum {
 /* head_dim D: 8 .. 256, a multiple of 8 (other values: UNSUPPORTED; the
  * pages' kernel declines only D > 256).  The kernels compute at D rounded up
  * to 64, 128 or 256; rows in memory keep the pitch D.  GQA group G = Hq / H
- * must be >= 1.                                                              */
+ * must be >= 1; the decode reads every coefficient row once per group of up
+ * to 8 query heads (any G: 3 runs as a group of four, 12 as eight plus four).
+ *                                                                            */
 
 /*
  * One compressed key or value stream: the archive of complete blocks and the

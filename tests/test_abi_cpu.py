@@ -155,6 +155,19 @@ def ws_bytes(lib, k, v, Hq):
     return rc, n.value
 
 
+def test_query_groups_round_up(lib):
+    # query heads per workgroup: G rounded up to 1, 2, 4 or 8, then groups of
+    # eight (the last one partial), so each coefficient row is read once per
+    # group; the plan, and so the workspace, is the one of the rounded group
+    big = dict(n_blocks=4096, capacity=4096, heads=1)
+    k, v = stream(**big), stream(**big)
+    same = [(3, 4), (5, 8), (6, 8), (7, 8), (9, 16), (12, 16), (20, 24)]
+    for g, like in same:
+        assert ws_bytes(lib, k, v, g) == ws_bytes(lib, k, v, like), (g, like)
+    # and the rounded groups differ from each other
+    assert len({ws_bytes(lib, k, v, g)[1] for g in (1, 2, 4, 8, 16, 24)}) == 6
+
+
 def test_workspace_plan(lib):
     k = stream(n_blocks=16, capacity=16)
     v = stream(n_blocks=16, capacity=16, fmt=bd.FMT_BF16)

@@ -118,6 +118,16 @@ DECODE_CASES = [
     (1, 16, 2, 128, 8, 2, "i8", "i8", 8 * 150 + 3, "bf16"),
     (1, 8, 2, 256, 8, 3, "i8", "bf16", 8 * 60 + 5, "bf16"),
     (2, 16, 2, 64, 8, 2, "i8", "bf16", 8 * 70 + 1, "bf16"),
+    # query groups that do not divide the kv head's G heads: G = 3 runs as a
+    # group of four with one absent head (the last kv head's absent head
+    # would be past the query tensor), 5..7 as groups of eight, 12 and 24 as
+    # eight-head groups plus a partial one; every row is read once per group
+    (1, 3, 1, 128, 16, 4, "i8", "i8", 16 * 200 + 9, "bf16"),
+    (1, 10, 2, 128, 8, 2, "i8", "i8", 8 * 120 + 3, "bf16"),    # G = 5
+    (2, 12, 2, 64, 16, 4, "i8", "bf16", 16 * 40 + 5, "bf16"),  # G = 6
+    (1, 14, 2, 128, 8, 3, "f32", "f32", 8 * 40 + 7, "f32"),    # G = 7, VALU paths
+    (1, 12, 1, 128, 8, 2, "i8", "i8", 8 * 300 + 1, "bf16"),    # G = 12: 8 + 4
+    (1, 24, 1, 64, 8, 2, "bf16", "i8", 8 * 50 + 2, "bf16"),    # G = 24: 8 + 8 + 8
 ]
 
 
