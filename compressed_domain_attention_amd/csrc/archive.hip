@@ -282,9 +282,13 @@ int launch_view(const ViewArgs &a, hipStream_t stream) {
 int launch_gather(const GatherArgs &g, int64_t n_units, hipStream_t stream) {
   if (n_units == 0) return 0;
   const int64_t work = g.row_bytes / 16 > g.tail_bytes / 16 ? g.row_bytes / 16 : g.tail_bytes / 16;
+  // about one word per thread: a grid-stride loop copies word by word (each
+  // store waits for its load), so the grid, not the loop, carries the
+  // parallelism (a cap of 64 workgroups per unit left 16 round trips per
+  // thread with one batch row)
   int64_t gx = (work + 255) / 256;
   if (gx < 1) gx = 1;
-  if (gx > 64) gx = 64;
+  if (gx > 1024) gx = 1024;
   const bool w16 = (g.slab_bytes | g.dst_slab_bytes | g.row_bytes | g.tail_bytes) % 16 == 0;
   if (w16)
     hipLaunchKernelGGL(gather_kernel<uint4>, dim3((unsigned)gx, (unsigned)n_units), dim3(256), 0, stream, g);
