@@ -125,10 +125,13 @@ DecodePlan make_plan(const codec_stream *k, const codec_stream *v, int64_t Hq, i
     p.chunk = 0;
   } else {
     // enough splits to fill the device once; every wave of a split gets a
-    // tile or more
+    // tile or more.  A split only pays when one split would leave some wave
+    // more than two tiles: the combine costs about what a wave spends on a
+    // tile or two (a C1-sized decode: 10.8 us with one split, 11.7 with two).
     const int64_t tiles = (n + NB - 1) / NB;
     int64_t ns = (p.target + p.pairs - 1) / p.pairs;
-    const int64_t ns_max = (tiles + kDecodeWaves - 1) / kDecodeWaves;
+    int64_t ns_max = (tiles + kDecodeWaves - 1) / kDecodeWaves;
+    if (tiles <= 2 * kDecodeWaves) ns_max = 1;
     if (ns > ns_max) ns = ns_max;
     if (ns < 1) ns = 1;
     if (ns > kMaxSplits) ns = kMaxSplits;

@@ -8,8 +8,9 @@
 // writes (max, sum, acc) and a combine merges them (flash-decoding).
 //
 // MI355X design.  One workgroup = one (b, kv head, query group, split) with
-// all GS query heads of the group, so each coefficient byte is read from HBM
-// once.  kDecodeWaves waves per workgroup, one workgroup per CU.
+// all GS query heads of the group (G rounded up to 1, 2, 4 or 8, eight at a
+// time beyond that), so each coefficient byte is read from HBM once per
+// group.  kDecodeWaves waves per workgroup, one workgroup per CU.
 //  * Tiles of TR coefficient rows (about 8 KB of K+V) stream through
 //    registers with 16-byte buffer loads; a wave requests its next tile's K
 //    rows as soon as its K phase is done and the V rows after the V phase.
@@ -24,13 +25,16 @@
 //  * int8 V rows: the tile goes to LDS (16-byte chunks XOR-swizzled by row),
 //    ds_read_b64_tr_b8 hands out the B operand of v_mfma_i32_16x16x32_i8,
 //    and the weights w * vscale per head and 32-row chunk become three
-//    signed-byte digits of a 22-bit fixed-point value (A operand).  bf16 /
-//    fp32 V rows: fp32 FMAs on the VALU.
-//  * The raw tail (fewer than R tokens) runs on the VALU paths in one wave.
+//    signed-byte digits of a 22-bit fixed-point value (A operand).  bf16 V
+//    rows: ds_read_b64_tr_b16 and v_mfma_f32_16x16x32_bf16, each weight as
+//    three bf16 terms (products exact in fp32).  fp32 V rows: fp32 FMAs on
+//    the VALU.
+//  * The raw tail (fewer than R tokens, plus a fused new token) runs on the
+//    VALU paths in one wave of the last split, before that wave's tiles.
 //  * Waves merge in LDS in a fixed order; the workgroup publishes its
 //    partial with device-scope stores, waits for them, and bumps a per-(b,
 //    h, group) counter; the last workgroup to arrive combines all splits
-//    with one round of device-scope loads and writes the output (no second
+//    with one round of system-scope loads and writes the output (no second
 //    launch, and no L2 write-back or invalidate per workgroup).  A split
 //    that is alone writes the output directly.
 #pragma once

@@ -25,7 +25,8 @@ def _case(B, Hq, H, D, R, S, kfmt, vfmt, T, seed):
     # many splits (one pair per kv head of a single row), then a smaller input
     ((1, 32, 8, 128, 16, 4, "i8", "i8", 16 * 3000 + 5, 1), (1, 8, 2, 128, 16, 4, "i8", "i8", 16 * 500 + 3, 2)),
     # one split per pair (256 pairs), then a smaller many-split input
-    ((32, 32, 8, 128, 8, 2, "i8", "i8", 8 * 400, 3), (1, 4, 2, 64, 8, 2, "i8", "bf16", 8 * 300 + 7, 4)),
+    # (58 tiles per pair: 8 splits)
+    ((32, 32, 8, 128, 8, 2, "i8", "i8", 8 * 400, 3), (1, 4, 2, 64, 8, 2, "i8", "bf16", 8 * 1200 + 7, 4)),
 ])
 def test_noalloc_equals_workspace_call(first, second):
     for case in (first, second):
