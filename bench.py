@@ -354,6 +354,67 @@ def layer_launch_bound(w, L, dev):
             "bytes_per_layer": decode_bytes(w, layers[0][0].n_blocks, layers[0][0].n_tail)}
 
 
+PHASES = ["start", "query converted", "raw tail done", "tile loop done", "waves merged", "partial published",
+          "arrival counted", "output written"]
+
+
+def timeline(w, L, dev, reps=6):
+    """Per-wave phase times of one cold decode launch, from the measurement
+    build (CDATTN_LIBRARY=compressed_domain_attention_amd/timeline/libcdattn.so):
+    the other L - 1 layers are decoded first, so layer 0's archive comes from
+    HBM, then one launch of layer 0 writes its stamps.  Times are microseconds
+    after the first wave's start; min / median / max over the waves that
+    reached each phase, then the median of those over the repetitions."""
+    k, v = syn.workload_kv_device(w, T=w.T, device=dev)
+    q = syn.workload_query(w, 0).to(dev)
+    layers = []
+    for _ in range(L):
+        ks = cda.CodecStream(w.B, w.Hkv, w.D, w.R, w.S, fmt=w.kfmt, device=dev)
+        vs = cda.CodecStream(w.B, w.Hkv, w.D, w.R, w.S, fmt=w.vfmt, device=dev)
+        ks.encode(k[:, :, :w.T])
+        vs.encode(v[:, :, :w.T])
+        layers.append((ks, vs))
+    del k, v
+    out = torch.empty((w.B, w.Hq, 1, w.D), dtype=torch.float32, device=dev)
+    ws = torch.zeros(cda.decode_workspace_bytes(*layers[0], w.Hq), dtype=torch.uint8, device=dev)
+    buf = torch.zeros(4096 * 8 * 8, dtype=torch.int64, device=dev)
+    per_rep = []
+    for _ in range(reps):
+        cda.timeline_set(None)
+        for ks, vs in layers[1:]:
+            cda.decode_attention(q, ks, vs, out=out, workspace=ws)
+        buf.zero_()
+        torch.cuda.synchronize()
+        cda.timeline_set(buf)
+        cda.decode_attention(q, *layers[0], out=out, workspace=ws)
+        torch.cuda.synchronize()
+        cda.timeline_set(None)
+        t = buf.view(4096, 8, 8).cpu().numpy()
+        live = t[:, :, 0] > 0
+        nwg = int(live.any(axis=1).sum())
+        t = t[:nwg].astype(np.float64)
+        t0 = t[:, :, 0][t[:, :, 0] > 0].min()
+        rel = np.where(t > 0, (t - t0) * 0.01, np.nan)      # 100 MHz ticks -> us
+        stats = {}
+        for i, name in enumerate(PHASES):
+            col = rel[:, :, i]
+            col = col[~np.isnan(col)]
+            if col.size:
+                stats[name] = [float(col.min()), float(np.median(col)), float(col.max())]
+        loop = rel[:, :, 3]
+        by_mod8 = [float(np.nanmax(loop[g::8])) for g in range(min(8, nwg))]
+        halves = [float(np.nanmean(loop[:, :4])), float(np.nanmean(loop[:, 4:]))]
+        per_rep.append((stats, by_mod8, halves, nwg))
+    names = [n for n in PHASES if all(n in r[0] for r in per_rep)]
+    phase = {n: [round(float(np.median([r[0][n][j] for r in per_rep])), 2) for j in range(3)] for n in names}
+    return {"workload": w.name, "layers_rotated": L, "launches": reps, "workgroups": per_rep[0][3],
+            "phase_us_min_median_max": phase,
+            "tile_loop_end_max_by_workgroup_index_mod_8_us":
+                [round(float(np.median([r[1][g] for r in per_rep])), 2) for g in range(len(per_rep[0][1]))],
+            "tile_loop_end_mean_waves_0_3_vs_4_7_us":
+                [round(float(np.median([r[2][j] for r in per_rep])), 2) for j in range(2)]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -365,6 +426,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", type=int, default=0, metavar="N",
                     help="launch sequence for rocprofv3 counter passes: N decodes and N calibration copies")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-wave phase times of one cold decode launch (needs the measurement build)")
     ap.add_argument("--layer-launch-bound", action="store_true",
                     help="time L per-layer decode launches against one launch over the same bytes, and print that")
     ap.add_argument("--traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
@@ -387,6 +450,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.layer_launch_bound:
         print(json.dumps(layer_launch_bound(w, args.layers, dev)), flush=True)
+        return
+    if args.timeline:
+        print(json.dumps(timeline(w, args.layers, dev)), flush=True)
         return
     L, K, W = args.layers, args.steps, args.warmup
     extra = K + W

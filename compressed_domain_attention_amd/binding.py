@@ -24,7 +24,9 @@ _LIB = None
 
 
 def library_path():
-    return os.path.join(_HERE, "libcdattn.so")
+    """libcdattn.so beside this file, or the library CDATTN_LIBRARY names
+    (the measurement build, compressed_domain_attention_amd/timeline/)."""
+    return os.environ.get("CDATTN_LIBRARY") or os.path.join(_HERE, "libcdattn.so")
 
 
 class CodecError(RuntimeError):
@@ -88,6 +90,20 @@ def _lib():
 def library():
     """The loaded ctypes library (loads it on first use)."""
     return _lib()
+
+
+def timeline_set(buf):
+    """Measurement builds only: decode launches write per-wave phase stamps
+    (uint64, 100 MHz clock) into `buf`, a device tensor; None stops them."""
+    lib = _lib()
+    if not hasattr(lib, "codec_timeline_set"):
+        raise RuntimeError(f"{library_path()} is not a timeline build (python -m "
+                           "compressed_domain_attention_amd.build --timeline)")
+    lib.codec_timeline_set.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.codec_timeline_set.restype = ctypes.c_int
+    if buf is None:
+        return lib.codec_timeline_set(None, 0)
+    return lib.codec_timeline_set(buf.data_ptr(), buf.numel() * buf.element_size())
 
 
 def _check(status, what):

@@ -19,6 +19,12 @@ using namespace cdattn;
 
 namespace {
 
+#ifdef CDATTN_TIMELINE
+// Measurement builds only: where decode launches write their phase stamps.
+unsigned long long *g_timeline = nullptr;
+int64_t g_timeline_words = 0;
+#endif
+
 // The codec's basis table (see basis.h), host copy.
 const float kBasisHost[kBasisEntries] = {
 #include "cdattn_basis_table.inc"
@@ -386,6 +392,10 @@ int launch_decode_call(const void *q, const int64_t q_stride[2], int64_t Hq, con
   a.counters = reinterpret_cast<uint32_t *>(ws);
   a.part_ml = reinterpret_cast<float *>(ws + p.off_ml);
   a.part_acc = reinterpret_cast<float *>(ws + p.off_acc);
+#ifdef CDATTN_TIMELINE
+  a.timeline = g_timeline;
+  a.timeline_words = g_timeline_words;
+#endif
   (void)hipGetLastError();
   const int DP = pad_dim(k->head_dim);
   const int lr = launch_decode(DP, p.GS, p.SP, row_fmt(k->fmt), row_fmt(v->fmt), DP == k->head_dim, a, p.n_wg, stream);
@@ -671,3 +681,11 @@ int codec_select_batch(const codec_stream *src, codec_stream *dst, const int64_t
 }
 
 }  // extern "C"
+
+#ifdef CDATTN_TIMELINE
+extern "C" int codec_timeline_set(void *buf, size_t bytes) {
+  g_timeline = static_cast<unsigned long long *>(buf);
+  g_timeline_words = buf ? (int64_t)(bytes / 8) : 0;
+  return CODEC_OK;
+}
+#endif

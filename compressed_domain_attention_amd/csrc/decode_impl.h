@@ -217,6 +217,12 @@ struct TileRef {
   int dm;
 };
 
+#ifdef CDATTN_TIMELINE
+constexpr bool kTimeline = true;    // measurement builds: per-wave phase stamps
+#else
+constexpr bool kTimeline = false;
+#endif
+
 constexpr uint32_t kOutOfRange = 0x40000000u;   // a buffer offset past every range: the load reads zeros
 
 template <int D, int GS, int KF, int VF>
@@ -1390,9 +1396,27 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
   __shared__ float tail_m[8];   // the tail wave's running max per head right after the tail (MFMA value path)
   float *lds = reinterpret_cast<float *>(lds_raw);
 
+  // Measurement builds only: the 100 MHz clock at the end of each phase,
+  // 0 start, 1 query converted, 2 raw tail done, 3 tile loop done, 4 waves
+  // merged, 5 partial published, 6 arrival counted, 7 output written.
+  unsigned long long tl[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  auto stamp = [&](int i) {
+    if constexpr (kTimeline) tl[i] = __builtin_amdgcn_s_memrealtime();
+  };
+  stamp(0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile addresses live in SGPRs
+  auto tl_store = [&]() {
+#ifdef CDATTN_TIMELINE
+    const int64_t wg = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+    const int64_t w0 = (wg * W + wave) * 8;
+    if (lane == 0 && a.timeline != nullptr && w0 + 8 <= a.timeline_words) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a.timeline[w0 + i] = tl[i];
+    }
+#endif
+  };
   // grid: x = split, y = query group, z = batch row * kv heads + kv head
   const int split = blockIdx.x;
   const int qg = blockIdx.y;
@@ -1502,6 +1526,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
     qr.convert(a, lane, Q.qB, Q.cqq);
   else
     qr.convert(a, lane, Q.qh, Q.cq);
+  stamp(1);
   // ---- the raw tail: one wave of the last split (the one with the fewest
   // tiles; with the shifted ranges the split has a tile fewer), on the VALU
   // paths, before that wave's tiles (its first tiles are already requested):
@@ -1564,6 +1589,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
     }
   }
 
+  stamp(2);
   for (int t0 = wave; t0 < ntiles; t0 += C::NBUF * W) {
 #pragma unroll
     for (int i = 0; i < C::NBUF; ++i) {
@@ -1581,6 +1607,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
     }
   }
 
+  stamp(3);
   // ---- wave totals: l over the lanes of a head, acc over the rows of a step
   float l_u[GS];
   {
@@ -1641,6 +1668,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
     }
   }
   __syncthreads();
+  stamp(4);
   // workgroup (max, sum, acc) of head g at column d
   auto wg_partial = [&](int g, int d, float &m, float &l, float &sacc) {
     m = -INFINITY;
@@ -1677,6 +1705,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
       wg_partial(idx / D, idx % D, m, l, sacc);
       store_out(idx / D, idx % D, sacc / l);
     }
+    stamp(7);
+    tl_store();
     return;
   }
 
@@ -1697,13 +1727,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
   // drains; only after every thread's have drained is the arrival counted.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  stamp(5);
   if (tid == 0) {
     const uint32_t old =
         __hip_atomic_fetch_add(a.counters + pairq * kCounterStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (old == (uint32_t)(a.ns - 1)) ? 1 : 0;
   }
   __syncthreads();
-  if (!last_flag) return;
+  stamp(6);
+  if (!last_flag) {
+    tl_store();
+    return;
+  }
 
   // ---- last arrival: fold the ns partials of every (head, column).  Wave
   // g < GS turns head g's (max, sum) pairs into split weights exp2(m - M)
@@ -1789,6 +1824,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
     store_out(g, d0 + 2, t.z / Lg);
     store_out(g, d0 + 3, t.w / Lg);
   }
+  stamp(7);
+  tl_store();
   if (tid == 0) __hip_atomic_store(a.counters + pairq * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

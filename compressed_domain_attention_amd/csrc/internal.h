@@ -138,6 +138,12 @@ struct DecodeArgs {
   uint32_t *counters;     // one per (b, h, query group), kCounterStride apart
   float *part_ml;         // [pairs][ns][GS][2]
   float *part_acc;        // [pairs][ns][GS][D]
+#ifdef CDATTN_TIMELINE
+  // Measurement builds only: per-wave phase stamps of each decode launch
+  // (s_memrealtime) at word ((workgroup * waves + wave) * 8 + phase).
+  unsigned long long *timeline;
+  int64_t timeline_words;
+#endif
 };
 static_assert(offsetof(DecodeArgs, H) == 64 && offsetof(DecodeArgs, q_sh) == 112, "kernel argument lines");
 

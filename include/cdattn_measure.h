@@ -30,6 +30,20 @@ extern "C" {
  */
 int codec_measure_read(const void *src, size_t bytes, uint32_t *sink, int32_t workgroups, hipStream_t stream);
 
+/*
+ * codec_timeline_set -- exported only by the measurement build (compiled with
+ * CDATTN_TIMELINE: python -m compressed_domain_attention_amd.build --timeline,
+ * into compressed_domain_attention_amd/timeline/).  Every later decode launch
+ * writes, for each wave, eight uint64 stamps of the 100 MHz clock
+ * (s_memrealtime) to buf[((workgroup * 8 + wave) * 8 + phase)], workgroup =
+ * the linear workgroup index, phase 0 start, 1 query converted, 2 raw tail
+ * done, 3 tile loop done, 4 waves merged, 5 partial published, 6 arrival
+ * counted, 7 output written (0: phase not reached).  Waves past `bytes` write
+ * nothing.  buf is a device pointer owned by the caller; NULL stops the
+ * stamps.  Returns 0.
+ */
+int codec_timeline_set(void *buf, size_t bytes);
+
 #ifdef __cplusplus
 }
 #endif

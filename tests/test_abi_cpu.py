@@ -47,8 +47,10 @@ def test_header_symbols_exported(lib):
 def test_measure_header_symbols_and_checks(lib):
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "cdattn_measure.h")).read(), flags=re.S)
     names = re.findall(r"^int\s+(codec_\w+)\s*\(", text, flags=re.M)
-    assert names == ["codec_measure_read"]
+    assert names == ["codec_measure_read", "codec_timeline_set"]
     assert hasattr(lib, "codec_measure_read")
+    # the phase-stamp hook exists only in the measurement build
+    assert not hasattr(lib, "codec_timeline_set")
     assert lib.codec_measure_read(None, 16, FAKE, 4, None) == NULL
     assert lib.codec_measure_read(FAKE, 16, None, 4, None) == NULL
     assert lib.codec_measure_read(FAKE + 8, 16, FAKE, 4, None) == SHAPE
