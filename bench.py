@@ -319,8 +319,8 @@ def graph_time_us(fn, stream, rounds=4, reps=5):
 def layer_launch_bound(w, L, dev):
     """What one launch per step across L layers could save at most: L decode
     launches (one per layer's archive, as a model runs them) against one
-    launch over the same bytes (the L layers' archives as L times the batch
-    rows, which a model cannot do: each layer's query needs the previous
+    launch over the same bytes (the L layers in one CodecLayerStack, which a
+    model cannot use for a step: each layer's query needs the previous
     layer's output), and the fixed cost of one launch: the intercept of the
     launch time against the context length (full, half and quarter length
     keep the same split count), i.e. launch, prologue, tail, merge and
@@ -337,12 +337,14 @@ def layer_launch_bound(w, L, dev):
         return ks, vs
 
     layers = [make(k, v, w.B, w.T) for _ in range(L)]
-    merged = make(k.repeat(L, 1, 1, 1), v.repeat(L, 1, 1, 1), w.B * L, w.T)
+    stack = cda.CodecLayerStack(L, w.B, w.Hkv, w.D, w.R, w.S, k_fmt=w.kfmt, v_fmt=w.vfmt, device=dev)
+    stack.encode(torch.stack([k] * L), torch.stack([v] * L))
+    merged = (stack.k, stack.v)
     lengths = [w.T, w.T // 2, w.T // 4]
     shorter = {T: [make(k, v, w.B, T) for _ in range(L)] for T in lengths[1:]}
-    qm = q.repeat(L, 1, 1, 1)
+    qm = torch.stack([q] * L)
     outs = [torch.empty((w.B, w.Hq, 1, w.D), dtype=torch.float32, device=dev) for _ in range(L)]
-    om = torch.empty((w.B * L, w.Hq, 1, w.D), dtype=torch.float32, device=dev)
+    om = torch.empty((L, w.B, w.Hq, 1, w.D), dtype=torch.float32, device=dev)
     need = max(cda.decode_workspace_bytes(*layers[0], w.Hq), cda.decode_workspace_bytes(*merged, w.Hq))
     ws = torch.zeros(need + 4096, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
@@ -354,7 +356,7 @@ def layer_launch_bound(w, L, dev):
         return fn
 
     t_layers = graph_time_us(per_layer(layers), cs)
-    t_merged = graph_time_us(lambda: cda.decode_attention(qm, *merged, out=om, workspace=ws), cs)
+    t_merged = graph_time_us(lambda: stack.decode(qm, out=om, workspace=ws), cs)
     per_len = [t_layers / L] + [graph_time_us(per_layer(shorter[T]), cs) / L for T in lengths[1:]]
     slope, intercept = np.polyfit(np.array(lengths, dtype=np.float64), np.array(per_len), 1)
     return {"workload": w.name, "layers": L, "per_layer_launches_us": round(t_layers, 2),
@@ -364,6 +366,32 @@ def layer_launch_bound(w, L, dev):
             "fixed_cost_per_launch_us": round(float(intercept), 3),
             "us_per_million_tokens": round(float(slope) * 1e6, 3),
             "bytes_per_layer": decode_bytes(w, layers[0][0].n_blocks, layers[0][0].n_tail)}
+
+
+def layer_stack_timing(w, kd, vd, L, q, dev, stream, per_layer_us):
+    """One step's decode of all L layers as one launch (CodecLayerStack: the
+    L layers' archives in one allocation, layers folded into the batch axis),
+    graph-timed, beside L per-layer launches of the same archives.  The one
+    launch needs every layer's query at once."""
+    st = cda.CodecLayerStack(L, w.B, w.Hkv, w.D, w.R, w.S, k_fmt=w.kfmt, v_fmt=w.vfmt, device=dev,
+                             capacity=w.T // w.R + 1)
+    for l in range(L):
+        kl, vl = st.layer(l)
+        kl.encode(kd[:, :, :w.T])
+        vl.encode(vd[:, :, :w.T])
+    qs = torch.stack([q] * L)
+    out = torch.empty((L, w.B, w.Hq, 1, w.D), dtype=torch.float32, device=dev)
+    st.decode(qs, out=out)   # sizes and caches the workspace before the capture
+    torch.cuda.synchronize()
+    t = graph_time_us(lambda: st.decode(qs, out=out), stream)
+    per_layer_bytes = decode_bytes(w, st.layer(0)[0].n_blocks, st.layer(0)[0].n_tail)
+    res = {"layers": L, "one_launch_us": round(t, 2), "per_layer_launches_us": round(per_layer_us * L, 2),
+           "GBps": round(L * per_layer_bytes / (t * 1e-6) / 1e9, 2),
+           "frac": round(L * per_layer_bytes / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "what": "CodecLayerStack.decode: every layer's decode in one launch (all queries given at once)"}
+    del st
+    torch.cuda.empty_cache()
+    return res
 
 
 PHASES = ["start", "query converted", "raw tail done", "tile loop done", "waves merged", "partial published",
@@ -555,6 +583,8 @@ def main():
     per_launch = decode_bytes(w, streams[0][0].n_blocks, streams[0][0].n_tail)
     achieved = per_launch / avg_s / 1e9
     traffic = load_traffic(w.name)
+    print("# timing one decode launch over the layer stack", file=sys.stderr, flush=True)
+    stack = layer_stack_timing(w, kd, vd, L, qd, dev, cap_stream, avg_s * 1e6)
     ops = archive_ops(w, streams, dev)
     print("# timing the streaming-read ceiling", file=sys.stderr, flush=True)
     ceiling = read_ceiling(per_launch, L, dev, cap_stream)
@@ -578,6 +608,7 @@ def main():
         "encode": {"avg_ms": round(float(np.mean(enc_ms[1:] or enc_ms)), 4),
                    "bytes": enc_bytes,
                    "GBps": round(enc_bytes / (float(np.mean(enc_ms[1:] or enc_ms)) * 1e-3) / 1e9, 2)},
+        "layer_stack": stack,
         **ops,
     }
     if not args.no_cpu_baseline:

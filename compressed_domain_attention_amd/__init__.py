@@ -7,7 +7,7 @@ and raises if it is missing.
 """
 
 from .binding import (  # noqa: F401
-    CodecError, CodecStream, basis, decode_attention, decode_attention_append, decode_attention_noalloc,
+    CodecError, CodecStream, CodecLayerStack, basis, decode_attention, decode_attention_append, decode_attention_noalloc,
     decode_workspace_bytes, measure_read, timeline_set,
     encode_blocks, append_step, materialise, crop, select_batch, library, library_path,
     FMT_F32, FMT_BF16, FMT_I8, FMT_PNG,

@@ -232,6 +232,187 @@ class CodecStream:
         select_batch(self, idx, stream)
 
 
+
+class _LayerView(CodecStream):
+    """Layer l of a CodecLayerStack's key or value archive: batch rows
+    [l B, (l + 1) B) of the stack's stream, with this layer's own counters.
+    Rows, scales and tail are slices of the stack's tensors, looked up at each
+    use (the stack reallocates them when it grows), so every per-stream call
+    (encode, append, decode, view, crop) works on one layer alone."""
+
+    def __init__(self, parent, stack, layer):
+        self._parent, self._stack, self._layer = parent, stack, layer
+        self.H, self.D, self.R, self.S = parent.H, parent.D, parent.R, parent.S
+        self.fmt, self.raw_dtype, self.device = parent.fmt, parent.raw_dtype, parent.device
+        self.n_blocks, self.n_tail = 0, 0
+        self.discard_view()
+
+    @property
+    def B(self):
+        return self._stack.B
+
+    def _slice(self, t):
+        return None if t is None else t[self._layer * self.B:(self._layer + 1) * self.B]
+
+    @property
+    def rows(self):
+        return self._slice(self._parent.rows)
+
+    @property
+    def scales(self):
+        return self._slice(self._parent.scales)
+
+    @property
+    def tail(self):
+        return self._slice(self._parent.tail)
+
+    @property
+    def capacity(self):
+        return self._parent.capacity
+
+    def _grow(self, need):
+        self._stack._grow(need)
+
+    def select_batch(self, idx, stream=None):
+        raise ValueError("a layer's batch rows are reordered for every layer at once (CodecLayerStack.select_batch)")
+
+
+class CodecLayerStack:
+    """The key and value archives of L layers in one allocation: one stream
+    per side whose batch axis is (layer, batch row), i.e. rows
+    (L * B, H, capacity, S, D), scales (L * B, H, capacity, S) and tails
+    (L * B, H, R, D), all layers at one capacity.
+
+    ``layer(l)`` gives layer l's key and value streams (slices with their own
+    counters) for models that run layer by layer.  When every layer is at the
+    same length, the stack-wide calls do one step for all layers in one
+    launch: ``decode`` (split-K decode with the combine in the same launch,
+    for all L x B x Hkv pairs), ``decode_append`` (the step's tokens of all
+    layers appended, then the decode, in one launch unless the token completes
+    a block), ``append``, ``encode`` (prefill), ``crop`` and
+    ``select_batch`` (the same beam reorder in every layer).  Queries, tokens
+    and outputs of the stack-wide calls are (L, B, heads, 1 or T, D).
+    flashcodec-kv README, end-to-end decode paragraph: the remaining gap is
+    the per-layer launch pair, which one launch per step across layers
+    removes.
+    """
+
+    def __init__(self, L, B, H, D, R, S, k_fmt="i8", v_fmt=None, raw_dtype="bf16", device="cuda", capacity=0):
+        if int(L) < 1 or int(B) < 1:
+            raise ValueError("a layer stack needs L >= 1 layers of B >= 1 batch rows")
+        self.L, self.B = int(L), int(B)
+        self.k = CodecStream(self.L * self.B, H, D, R, S, fmt=k_fmt, raw_dtype=raw_dtype, device=device,
+                             capacity=capacity)
+        self.v = CodecStream(self.L * self.B, H, D, R, S, fmt=v_fmt if v_fmt is not None else k_fmt,
+                             raw_dtype=raw_dtype, device=device, capacity=capacity)
+        self._layers = [(_LayerView(self.k, self, l), _LayerView(self.v, self, l)) for l in range(self.L)]
+
+    def layer(self, l):
+        """Layer l's (key stream, value stream)."""
+        return self._layers[l]
+
+    @property
+    def capacity(self):
+        return self.k.capacity
+
+    @property
+    def seq_len(self):
+        return self._common()[0] * self.k.R + self._common()[1]
+
+    def _grow(self, need):
+        # capacity doubling for all layers at once; every layer's archived
+        # blocks are copied over (the stack copies the longest layer's count)
+        for p, side in ((self.k, 0), (self.v, 1)):
+            p.n_blocks = max(lay[side].n_blocks for lay in self._layers)
+            p._grow(need)
+
+    def _common(self):
+        counts = {(s.n_blocks, s.n_tail) for lay in self._layers for s in lay}
+        if len(counts) != 1:
+            raise ValueError(f"stack-wide calls need every layer at the same length; layers hold {sorted(counts)}")
+        return counts.pop()
+
+    def _enter(self):
+        nb, nt = self._common()
+        for p in (self.k, self.v):
+            p.n_blocks, p.n_tail = nb, nt
+
+    def _leave(self):
+        for lay in self._layers:
+            for s, p in zip(lay, (self.k, self.v)):
+                s.n_blocks, s.n_tail = p.n_blocks, p.n_tail
+                s._rec_blocks = min(s._rec_blocks, s.n_blocks)
+
+    def _flat(self, t, what):
+        if t.dim() != 5 or t.shape[0] != self.L or t.shape[1] != self.B:
+            raise ValueError(f"{what} must be (L, B, heads, tokens, D) = ({self.L}, {self.B}, ...)")
+        try:
+            return t.view(self.L * self.B, *t.shape[2:])
+        except RuntimeError:
+            raise ValueError(f"{what}: the (layer, batch) axes must fold into one (a view, no copy)") from None
+
+    def encode(self, k, v, stream=None):
+        """Prefill every layer: k, v (L, B, H, T, D); every tail must be empty."""
+        self._enter()
+        encode_blocks(self.k, self._flat(k, "k"), stream)
+        encode_blocks(self.v, self._flat(v, "v"), stream)
+        self._leave()
+
+    def append(self, k_new, v_new, stream=None):
+        """One token per layer: k_new, v_new (L, B, H, 1, D)."""
+        self._enter()
+        append_step(self.k, self.v, self._flat(k_new, "k_new"), self._flat(v_new, "v_new"), stream)
+        self._leave()
+
+    def decode(self, q, scale=None, out=None, out_dtype=torch.float32, workspace=None, stream=None):
+        """Decode attention of every layer in one launch: q (L, B, Hq, 1, D)
+        bf16; returns out (L, B, Hq, 1, D)."""
+        self._enter()
+        qf = self._flat(q, "q")
+        of = None if out is None else self._flat(out, "out")
+        of = decode_attention(qf, self.k, self.v, scale, of, out_dtype, workspace, stream)
+        return of.view(self.L, self.B, *of.shape[1:])
+
+    def decode_append(self, q, k_new, v_new, scale=None, out=None, out_dtype=torch.float32, workspace=None,
+                      stream=None):
+        """``append`` then ``decode`` for all layers (codec_decode_attention_append
+        on the stack: one launch unless the token completes a block)."""
+        self._enter()
+        qf = self._flat(q, "q")
+        of = None if out is None else self._flat(out, "out")
+        try:
+            of = decode_attention_append(qf, self.k, self.v, self._flat(k_new, "k_new"),
+                                         self._flat(v_new, "v_new"), scale, of, out_dtype, workspace, stream)
+        finally:
+            self._leave()
+        return of.view(self.L, self.B, *of.shape[1:])
+
+    def crop(self, new_len, stream=None):
+        """Keep the first new_len tokens of every layer (codec_crop on the stack)."""
+        self._enter()
+        try:
+            crop(self.k, new_len, stream)
+            crop(self.v, new_len, stream)
+        finally:
+            self._leave()
+
+    def select_batch(self, idx, stream=None):
+        """Batch row i of every layer becomes its old row idx[i] (beam
+        reorder; new buffers, one gather launch per side for all layers)."""
+        idx = [int(i) for i in (idx.tolist() if hasattr(idx, "tolist") else idx)]
+        if any(i < 0 or i >= self.B for i in idx):
+            raise ValueError(f"batch index out of range [0, {self.B})")
+        self._enter()
+        flat = [l * self.B + i for l in range(self.L) for i in idx]
+        select_batch(self.k, flat, stream)
+        select_batch(self.v, flat, stream)
+        self.B = len(idx)
+        self._leave()
+        for lay in self._layers:
+            for s in lay:
+                s.discard_view()
+
+
 def encode_blocks(s, x, stream=None):
     if x.dtype != _TORCH_DTYPE[s.raw_dtype] or x.dim() != 4 or x.stride(3) != 1:
         raise ValueError("x must be (B, H, T, D) of the stream's raw dtype with unit d stride")
@@ -288,6 +469,8 @@ def crop(s, new_len, stream=None):
 def select_batch(s, idx, stream=None):
     """Batch row i of s becomes its old row idx[i]; new buffers are allocated
     (rows keep their capacity), the memoised view is dropped."""
+    if isinstance(s, _LayerView):
+        raise ValueError("a layer's batch rows are reordered for every layer at once (CodecLayerStack.select_batch)")
     idx = [int(i) for i in (idx.tolist() if hasattr(idx, "tolist") else idx)]
     n = len(idx)
     rows = torch.empty((n, s.H, s.capacity, s.S, s.D), dtype=_TORCH_DTYPE[s.fmt], device=s.device)
