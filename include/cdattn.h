@@ -96,6 +96,17 @@ enum {
  * n_blocks / n_tail itself on success of encode and append calls; the caller
  * grows `capacity` (and re-points `rows` / `scales`) when a call returns
  * CODEC_ERR_CAPACITY.
+ *
+ * Layer stacks: the batch axis may hold (layer, batch row) pairs, layer-major
+ * (batch = L * B, row l * B + b is batch row b of layer l), when the L layers
+ * share R, S, D, formats, capacity and length.  Every call then does one
+ * step for all L layers in one launch (the decode with its combine, the
+ * fused append, the prefill, crop and gather); queries, tokens and outputs
+ * use the same folded batch axis.  A stream whose `rows`, `scales` and `tail`
+ * point at layer l's B rows of such a stack (batch = B) is that layer alone,
+ * with its own counters.  flashcodec-kv README, end-to-end decode paragraph:
+ * the remaining gap there is the per-layer launch pair; one launch per step
+ * across layers needs every layer's query at once.
  */
 typedef struct codec_stream {
   int32_t block;      /* R, 1 .. CODEC_MAX_BLOCK                          */
