@@ -419,6 +419,7 @@ def timeline(w, L, dev, reps=6):
     ws = torch.zeros(cda.decode_workspace_bytes(*layers[0], w.Hq), dtype=torch.uint8, device=dev)
     buf = torch.zeros(4096 * 8 * 8, dtype=torch.int64, device=dev)
     per_rep = []
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
     for _ in range(reps):
         cda.timeline_set(None)
         for ks, vs in layers[1:]:
@@ -444,7 +445,19 @@ def timeline(w, L, dev, reps=6):
         loop = rel[:, :, 3]
         by_mod8 = [float(np.nanmax(loop[g::8])) for g in range(min(8, nwg))]
         halves = [float(np.nanmean(loop[:, :4])), float(np.nanmean(loop[:, 4:]))]
-        per_rep.append((stats, by_mod8, halves, nwg))
+        # dispatch rounds: workgroups in start order, one CU's worth each
+        order = np.argsort(np.nanmin(rel[:, :, 0], axis=1))
+        per_wg = {"workgroup start": np.nanmin(rel[:, :, 0], axis=1),
+                  "query converted (median of its waves)": np.nanmedian(rel[:, :, 1], axis=1),
+                  "last tile loop of the workgroup": np.nanmax(rel[:, :, 3], axis=1),
+                  "output written (or partial published)": np.nanmax(rel[:, :, 5:8], axis=(1, 2))}
+        rounds = []
+        for r0 in range(0, nwg, n_cu):
+            idx = order[r0:r0 + n_cu]
+            rounds.append({k: [float(np.nanmin(x[idx])), float(np.nanmedian(x[idx])), float(np.nanmax(x[idx]))]
+                           for k, x in per_wg.items()})
+        loop_time = [float(np.nanmean(loop[:, :4] - rel[:, :4, 1])), float(np.nanmean(loop[:, 4:] - rel[:, 4:, 1]))]
+        per_rep.append((stats, by_mod8, halves, nwg, rounds, loop_time))
     names = [n for n in PHASES if all(n in r[0] for r in per_rep)]
     phase = {n: [round(float(np.median([r[0][n][j] for r in per_rep])), 2) for j in range(3)] for n in names}
     return {"workload": w.name, "layers_rotated": L, "launches": reps, "workgroups": per_rep[0][3],
@@ -452,7 +465,12 @@ def timeline(w, L, dev, reps=6):
             "tile_loop_end_max_by_workgroup_index_mod_8_us":
                 [round(float(np.median([r[1][g] for r in per_rep])), 2) for g in range(len(per_rep[0][1]))],
             "tile_loop_end_mean_waves_0_3_vs_4_7_us":
-                [round(float(np.median([r[2][j] for r in per_rep])), 2) for j in range(2)]}
+                [round(float(np.median([r[2][j] for r in per_rep])), 2) for j in range(2)],
+            "tile_loop_time_mean_waves_0_3_vs_4_7_us":
+                [round(float(np.median([r[5][j] for r in per_rep])), 2) for j in range(2)],
+            "rounds_of_one_workgroup_per_cu": [
+                {k: [round(float(np.median([r[4][i][k][j] for r in per_rep])), 2) for j in range(3)]
+                 for k in per_rep[0][4][i]} for i in range(len(per_rep[0][4]))]}
 
 
 def main():
