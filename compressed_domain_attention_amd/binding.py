@@ -353,16 +353,22 @@ class CodecLayerStack:
 
     def encode(self, k, v, stream=None):
         """Prefill every layer: k, v (L, B, H, T, D); every tail must be empty."""
+        kf, vf = self._flat(k, "k"), self._flat(v, "v")
         self._enter()
-        encode_blocks(self.k, self._flat(k, "k"), stream)
-        encode_blocks(self.v, self._flat(v, "v"), stream)
-        self._leave()
+        try:
+            encode_blocks(self.k, kf, stream)
+            encode_blocks(self.v, vf, stream)
+        finally:
+            self._leave()   # a failed value encode leaves K ahead of V: stack-wide calls then refuse
 
     def append(self, k_new, v_new, stream=None):
         """One token per layer: k_new, v_new (L, B, H, 1, D)."""
+        kf, vf = self._flat(k_new, "k_new"), self._flat(v_new, "v_new")
         self._enter()
-        append_step(self.k, self.v, self._flat(k_new, "k_new"), self._flat(v_new, "v_new"), stream)
-        self._leave()
+        try:
+            append_step(self.k, self.v, kf, vf, stream)
+        finally:
+            self._leave()
 
     def decode(self, q, scale=None, out=None, out_dtype=torch.float32, workspace=None, stream=None):
         """Decode attention of every layer in one launch: q (L, B, Hq, 1, D)
