@@ -1541,7 +1541,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
   for (int g = 0; g < (C::VM ? GS : 1); ++g)
 #pragma unroll
     for (int e = 0; e < ET; ++e) acct[g][e] = 0.0f;
-  if (tail_wave) {
+  auto run_tail = [&]() {
     // MFMA key path: the VALU-layout query is loaded here and converted once
     // the tail's own loads are in flight
     QRegValu<D, GS, FULL> qv;
@@ -1587,9 +1587,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
     } else {
       run(acc.v);
     }
+  };
+  // Eight-head groups hold more registers than the tail pass can find
+  // beside a requested tile: there the tail runs after the wave's tiles
+  // (the tail wave has the fewest), elsewhere before them.
+  constexpr bool kTailAfter = GS >= 8;
+  if constexpr (!kTailAfter) {
+    if (tail_wave) run_tail();
+    stamp(2);
   }
-
-  stamp(2);
   for (int t0 = wave; t0 < ntiles; t0 += C::NBUF * W) {
 #pragma unroll
     for (int i = 0; i < C::NBUF; ++i) {
@@ -1608,6 +1614,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
   }
 
   stamp(3);
+  if constexpr (kTailAfter) {
+    if (tail_wave) run_tail();
+    stamp(2);
+  }
   // ---- wave totals: l over the lanes of a head, acc over the rows of a step
   float l_u[GS];
   {
