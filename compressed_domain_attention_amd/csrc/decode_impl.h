@@ -1588,10 +1588,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const char *k
       run(acc.v);
     }
   };
-  // Eight-head groups hold more registers than the tail pass can find
-  // beside a requested tile: there the tail runs after the wave's tiles
-  // (the tail wave has the fewest), elsewhere before them.
-  constexpr bool kTailAfter = GS >= 8;
+  // Eight-head groups, head_dim 256 and 32 kept rows hold more registers
+  // than the tail pass can find beside a requested tile (it would spill, and
+  // each reload is a round trip while the other waves stream): there the
+  // tail runs after the wave's tiles (the tail wave has the fewest),
+  // elsewhere before them.
+  constexpr bool kTailAfter = GS >= 8 || D >= 256 || SP >= 32;
   if constexpr (!kTailAfter) {
     if (tail_wave) run_tail();
     stamp(2);
