@@ -50,3 +50,33 @@ def test_fused_equals_two_calls(fmt, raw, R, S, B, Hq, H, D, T0):
             assert_archive_equal(gpu_archive(vb), gpu_archive(va))
             ref = O.decode_attention(syn.bf16_to_numpy(q.cpu()), gpu_archive(kb), gpu_archive(vb))
             assert rel_err(ob[:, :, 0].float().cpu().numpy(), ref) <= TOL
+
+
+@pytest.mark.parametrize("kfmt,vfmt,R,S,B,Hq,H,D,T0", [
+    # the large-batch GQA-8 constants (eight-head groups, int8 keys, bf16
+    # values, R = 8, S = 3; the raw tail runs after the tail wave's tiles),
+    # one split per pair and several
+    ("i8", "bf16", 8, 3, 2, 16, 2, 128, 8 * 150 + 2),     # one split per pair
+    ("i8", "bf16", 8, 3, 1, 16, 2, 128, 8 * 600 + 1),
+    # head_dim 256 and 32 kept rows (also tail after the tiles)
+    ("i8", "i8", 16, 4, 1, 8, 2, 256, 16 * 70 + 3),
+    ("i8", "i8", 32, 32, 1, 8, 2, 64, 32 * 9 + 5),
+])
+def test_fused_tail_after_tiles(kfmt, vfmt, R, S, B, Hq, H, D, T0):
+    note("fused append, tail after tiles", kfmt, vfmt, R, S, B, Hq, H, D, T0)
+    steps = R + 3
+    k, v, _ = syn.small_case(B, Hq, H, D, T0 + steps, seed=R * 7 + S + D)
+    ka, va = make_streams(k[:, :, :T0], v[:, :, :T0], R, S, kfmt, vfmt)
+    kb, vb = make_streams(k[:, :, :T0], v[:, :, :T0], R, S, kfmt, vfmt)
+    for s in range(steps):
+        t = T0 + s
+        q = syn.gaussian((B, Hq, 1, D), 700 + s).to(DEV)
+        kn, vn = k[:, :, t:t + 1].to(DEV).contiguous(), v[:, :, t:t + 1].to(DEV).contiguous()
+        bd.append_step(ka, va, kn, vn)
+        oa = bd.decode_attention(q, ka, va)
+        ob = bd.decode_attention_append(q, kb, vb, kn, vn)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), (s, (oa - ob).abs().max().item())
+        if s in (0, R - T0 % R - 1, steps - 1):
+            ref = O.decode_attention(syn.bf16_to_numpy(q.cpu()), gpu_archive(kb), gpu_archive(vb))
+            assert rel_err(ob[:, :, 0].float().cpu().numpy(), ref) <= TOL
