@@ -406,6 +406,8 @@ class CodecLayerStack:
         """Batch row i of every layer becomes its old row idx[i] (beam
         reorder; new buffers, one gather launch per side for all layers)."""
         idx = [int(i) for i in (idx.tolist() if hasattr(idx, "tolist") else idx)]
+        if not idx:
+            raise ValueError("a beam reorder keeps at least one batch row")
         if any(i < 0 or i >= self.B for i in idx):
             raise ValueError(f"batch index out of range [0, {self.B})")
         self._enter()

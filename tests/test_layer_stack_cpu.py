@@ -74,3 +74,5 @@ def test_layer_views_refuse_their_own_beam_reorder():
         bd.select_batch(st.layer(0)[1], [1, 0])
     with pytest.raises(ValueError):
         st.select_batch([0, 2])                               # row 2 out of range for B = 2
+    with pytest.raises(ValueError):
+        st.select_batch([])
