@@ -161,13 +161,15 @@ constexpr int kMaxTargetWorkgroups = 1024;
 // MFMA value paths (int8 / bf16 rows) work in 32-row chunks, so a tile below
 // 32 rows is raised to 32 when that stays within 12 KB (int8 keys with bf16
 // values at head_dim 128: 21 -> 32 rows, measured 10 % faster).  Int8 keys
-// and values at head_dim 64 take 32 rows (4 KB) instead of 64: a 64-row tile
-// holds up to 256 (block, head) logits at once and spilled registers inside
-// the tile loop (B 8, GQA 4, 4K context: 14.3 -> 11.5 us per decode).
+// with int8 or bf16 values at head_dim 64 take one 32-row chunk per tile
+// instead of 64 or 42 rows: a larger tile holds up to 256 (block, head)
+// logits at once and spilled registers inside the tile loop, and 42 rows left
+// a second value chunk with 10 live rows (B 8, GQA 4, 4K context: int8 values
+// 14.3 -> 11.5 us per decode, bf16 values 13.8 -> 12.2 us).
 constexpr int decode_elem_bytes(int f) { return f == I8 ? 1 : (f == BF16 ? 2 : 4); }
 constexpr int decode_tile_rows(int D, int kf, int vf) {
   const int rb = D * (decode_elem_bytes(kf) + decode_elem_bytes(vf));
-  const int rows = D == 64 && kf == I8 && vf == I8 ? 32 : 8192 / rb;
+  const int rows = D == 64 && kf == I8 && (vf == I8 || vf == BF16) ? 32 : 8192 / rb;
   return (vf == I8 || vf == BF16) && rows < 32 && 32 * rb <= 12288 ? 32 : rows;
 }
 
