@@ -316,6 +316,47 @@ def graph_time_us(fn, stream, rounds=4, reps=5):
     return a.elapsed_time(b) * 1e3 / (reps * rounds)
 
 
+def shape_timing(spec, dev):
+    """Graph-timed decode launch for a shape outside the named workloads:
+    spec = "B,Hq,Hkv,D,T,R,S,kfmt,vfmt" (AR(1) rho 0.95 keys and values drawn
+    on the device, N(0,1) query), layers rotated for at least 512 MiB of
+    archives (at least 2, at most 64)."""
+    f = spec.split(",")
+    B, Hq, H, D, T, R, S = (int(x) for x in f[:7])
+    kf, vf = f[7], f[8]
+    k = syn.ar1_sequence_device(B, H, T, D, 0.95, 11, device=dev)
+    v = syn.ar1_sequence_device(B, H, T, D, 0.95, 12, device=dev)
+    q = syn.gaussian((B, Hq, 1, D), 13).to(dev)
+    ks = cda.CodecStream(B, H, D, R, S, fmt=kf, device=dev)
+    vs = cda.CodecStream(B, H, D, R, S, fmt=vf, device=dev)
+    ks.encode(k)
+    vs.encode(v)
+    layers = [(ks, vs)]
+    eb = {"i8": 1, "bf16": 2, "f32": 4}
+    n, t = ks.n_blocks, ks.n_tail
+    per = B * H * n * S * (D * (eb[kf] + eb[vf]) + 4 * ((kf == "i8") + (vf == "i8"))) \
+        + 2 * B * H * t * D * 2 + B * Hq * D * (2 + 4)
+    L = min(64, max(2, -(-(512 << 20) // per)))
+    for _ in range(L - 1):
+        a = cda.CodecStream(B, H, D, R, S, fmt=kf, device=dev)
+        b = cda.CodecStream(B, H, D, R, S, fmt=vf, device=dev)
+        a.encode(k)
+        b.encode(v)
+        layers.append((a, b))
+    del k, v
+    out = torch.empty((B, Hq, 1, D), dtype=torch.float32, device=dev)
+    ws = torch.zeros(cda.decode_workspace_bytes(*layers[0], Hq) + 4096, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def fn():
+        for a, b in layers:
+            cda.decode_attention(q, a, b, out=out, workspace=ws)
+    us = graph_time_us(fn, torch.cuda.Stream()) / L
+    return {"shape": {"B": B, "Hq": Hq, "Hkv": H, "D": D, "T": T, "R": R, "S": S, "k_rows": kf, "v_rows": vf},
+            "layers_rotated": L, "avg_launch_us": round(us, 2), "algorithmic_bytes_per_launch": per,
+            "GBps": round(per / us / 1e3, 1), "hbm_peak_fraction": round(per / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
 def layer_launch_bound(w, L, dev):
     """What one launch per step across L layers could save at most: L decode
     launches (one per layer's archive, as a model runs them) against one
@@ -488,6 +529,8 @@ def main():
                     help="per-wave phase times of one cold decode launch (needs the measurement build)")
     ap.add_argument("--layer-launch-bound", action="store_true",
                     help="time L per-layer decode launches against one launch over the same bytes, and print that")
+    ap.add_argument("--shape", metavar="B,Hq,Hkv,D,T,R,S,KFMT,VFMT",
+                    help="graph-time the decode launch of one shape outside the named workloads, and print that")
     ap.add_argument("--traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="summarise two rocprofv3 --pmc runs into profiles/decode_<workload>_traffic.json")
     args = ap.parse_args()
@@ -506,6 +549,9 @@ def main():
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.shape:
+        print(json.dumps(shape_timing(args.shape, dev)), flush=True)
+        return
     if args.layer_launch_bound:
         print(json.dumps(layer_launch_bound(w, args.layers, dev)), flush=True)
         return
