@@ -1167,7 +1167,9 @@ __device__ __forceinline__ void process_lv(const TileBuf<D, GS, KF, VF> &B, int 
   constexpr int kSmin = SP == 2 ? 2 : SP / 2 + 1;
   constexpr int NG = cmax(1, cdiv((C::TR / kSmin) * GS, 16));
   bool done = false;
-  if constexpr (SP == 2 && GS <= 4)   // (eight-head groups keep the registers for the plain path)
+  // eight-head groups pack only with int8 keys and values: other row formats
+  // leave no registers for it (their tile loops would reach scratch)
+  if constexpr (SP == 2 && (GS <= 4 || (KF == I8 && VF == I8)))
     done = logits_packed<GS, C::SWR, cdiv(NG, 2)>(bas, L.sw, nrows / S, R, S, lane, m_u, m_lane, l_lane, alpha);
   if (!done) logits<GS, SP, C::SWR, NG>(bas, L.sw, nrows / S, R, S, lane, m_u, m_lane, l_lane, alpha);
   if constexpr (C::VM)
