@@ -114,8 +114,12 @@ DECODE_CASES = [
     # plain path when R > 8
     (1, 8, 2, 128, 6, 2, "i8", "i8", 6 * 201 + 5, "bf16"),
     (3, 8, 2, 128, 16, 2, "i8", "i8", 16 * 64 + 3, "bf16"),
-    # eight-head groups with S = 2 (plain logit path), bf16 values at D = 256 and D = 64
+    # eight-head groups with S = 2 (int8 rows: two items per logit column;
+    # bf16 values: plain logit path), at D = 128, 64 and 256
     (1, 16, 2, 128, 8, 2, "i8", "i8", 8 * 150 + 3, "bf16"),
+    (2, 16, 2, 64, 8, 2, "i8", "i8", 8 * 400 + 5, "bf16"),    # 32-row tiles, thirteen splits
+    (1, 16, 2, 256, 8, 2, "i8", "i8", 8 * 200 + 3, "bf16"),
+    (1, 8, 2, 64, 16, 4, "i8", "i8", 16 * 300 + 7, "bf16"),   # D = 64, GQA 4, S = 4, several splits
     (1, 8, 2, 256, 8, 3, "i8", "bf16", 8 * 60 + 5, "bf16"),
     (2, 16, 2, 64, 8, 2, "i8", "bf16", 8 * 70 + 1, "bf16"),
     # query groups that do not divide the kv head's G heads: G = 3 runs as a
